@@ -1,0 +1,192 @@
+/*
+ * dspark.h -- C ABI of the DSpark draft/verify round on AMD MI355X (gfx950).
+ *
+ * One round of DSpark speculative decoding over a serving batch of B requests:
+ *   dspark_draft_round  semi-autoregressive drafting of a gamma-token block
+ *   dspark_schedule     confidence-driven verify budgets (prefix scheduler)
+ *   dspark_verify       lossless rejection sampling against the target
+ *
+ * Sources (the pages):
+ *   [P1] "DSpark, la bozza che sa quando fermarsi" (paithon.it), section
+ *        "Un po' di autoregressione basta": eq. p_k (backbone logits U_k plus a
+ *        prefix-dependent bias B_k), the Markov head B = W1 W2 of rank 256.
+ *   [P2] same page, section "Verificare meglio, non di più": eq. a_j = prod c_i,
+ *        eq. Theta = tau * SPS(B), greedy admission with an early stop.
+ *   [P3] "Les mathématiques derrière l'accélération ..." (seventnews.com),
+ *        section "La garantie de l'échantillonnage par rejet": accept with
+ *        probability min(1, p/q), stop at the first rejection, resample it from
+ *        the residual distribution.
+ *   [P4] "DeepSeek发布DSpark" (learnblockchain.cn), section "DSpark 是什么？":
+ *        a bonus token after a fully accepted block.
+ *
+ * Conventions for every call:
+ *   - Tensor arguments are DEVICE pointers owned by the caller; the library
+ *     never allocates, frees or keeps them.  Layouts are dense row-major.
+ *   - `workspace` is a device buffer of at least dspark_workspace_bytes(B,
+ *     gamma, V, r) bytes, 256-byte aligned, owned by the caller.  Calls that
+ *     share a workspace must be ordered on one stream.
+ *   - `stream` is a hipStream_t passed as void* (NULL = default stream).  Every
+ *     call only enqueues work on it and returns; nothing synchronises the host
+ *     except dspark_status().
+ *   - Return value: DSPARK_OK, or a negative error code.  Host-checkable
+ *     argument errors return DSPARK_EINVAL before anything is enqueued; a failed
+ *     launch returns DSPARK_EHIP.  Data errors found on the device (a token id
+ *     outside [0, V), a budget outside [0, gamma], a negative or NaN
+ *     temperature, a confidence outside (0, 1)) set a bit in the workspace's
+ *     status word; the offending value is clamped so that every kernel stays in
+ *     bounds, and dspark_status() reports DSPARK_EDATA.
+ *   - Sizes: B >= 1, 1 <= gamma <= 16, V >= 1, r >= 1.
+ *   - Randomness: Philox4x32-10 (Salmon et al., SC'11) keyed by `seed`, with
+ *     counter (draw index / 4, block position + pos_offset[b], request b,
+ *     stream); the same (seed, pos_offset) reproduces a round bit for bit.
+ */
+#ifndef DSPARK_H
+#define DSPARK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSPARK_ABI_VERSION 1
+
+enum dspark_status_code {
+  DSPARK_OK = 0,
+  DSPARK_EINVAL = -1, /* bad argument (checked on the host) */
+  DSPARK_EHIP = -2,   /* a HIP runtime call or kernel launch failed */
+  DSPARK_EDATA = -3   /* bad input data found on the device (see dspark_status) */
+};
+
+enum dspark_dtype {
+  DSPARK_BF16 = 0, /* bfloat16 */
+  DSPARK_F32 = 1   /* IEEE float32 */
+};
+
+/* Version of this ABI (DSPARK_ABI_VERSION of the built library). */
+int dspark_abi_version(void);
+
+/* Static text for a return code. */
+const char* dspark_error_string(int code);
+
+/* Bytes of device workspace the three calls need for these sizes (0 if a size
+ * is out of range).  One workspace serves draft, schedule and verify. */
+size_t dspark_workspace_bytes(int B, int gamma, int V, int r);
+
+/*
+ * dspark_draft_round -- [P1] eq. p_k with the Markov head.
+ *
+ * For k = 1..gamma, for every request b:
+ *   d_k(v) = base_logits[b, k-1, v] + sum_rho U[x_{k-1}, rho] * W[v, rho]
+ *   q_k    = softmax(d_k / T_b)   (T_b = temperature[b]; T_b = 0 means argmax)
+ *   x_k   ~ q_k                    (x_0 = prev0[b])
+ * The Markov bias is computed on the fly and never written to memory.
+ *
+ *   base_logits  [B, gamma, V]  logits_dtype   backbone logits U_k of [P1]
+ *   U            [V, r]         factor_dtype   first factor W1 of [P1]
+ *   W            [V, r]         factor_dtype   second factor W2 of [P1] stored
+ *                                              vocabulary-major: row v holds
+ *                                              column v of W2 (W2 = W^T)
+ *   prev0        [B] int32      last committed token of each request
+ *   temperature  [B] float32    >= 0; 0 = greedy
+ *   seed                        Philox key
+ *   pos_offset   [B] int32 or NULL (= 0): absolute position of the block, so
+ *                                that successive rounds draw fresh numbers
+ * Outputs:
+ *   draft_tokens [B, gamma] int32   x_1..x_gamma
+ *   draft_logq   [B, gamma] float32 ln q_k(x_k) (0 for greedy requests)
+ *   draft_lse    [B, gamma] float64 ln sum_v exp(d_k(v) / T_b) (for greedy
+ *                                   requests: max_v d_k(v)); kept in fp64 so
+ *                                   that dspark_verify can rebuild q_k exactly
+ */
+int dspark_draft_round(const void* base_logits, int logits_dtype,
+                       const void* U, const void* W, int factor_dtype,
+                       const int32_t* prev0, const float* temperature,
+                       uint64_t seed, const int32_t* pos_offset,
+                       int B, int gamma, int V, int r,
+                       int32_t* draft_tokens, float* draft_logq, double* draft_lse,
+                       void* workspace, void* stream);
+
+/*
+ * dspark_schedule -- [P2] hardware-aware prefix scheduler.
+ *
+ *   a[b, j] = fl32(a[b, j-1] * conf[b, j]), a[b, -1] = 1      (eq. a_j)
+ *   Q[b, j] = floor(a[b, j] * 2^32)
+ * Candidates (b, j) are taken in decreasing Q (ties: lower b, then lower j).
+ * With tau_0 = B * 2^32, N_0 = B (verify batch in tokens, one per request) and
+ * t(N) = 1 / SPS(N) linear between the table points (first value below the
+ * first point, last segment extended beyond the last one), candidate m is
+ * admitted iff (tau_m + Q_m) * t(N_m) > tau_m * t(N_m + 1) in float64, i.e.
+ * iff Theta = tau * SPS(N) strictly grows (eq. Theta); the first failure ends
+ * the scan.  budget[b] = number of admitted candidates of request b.
+ *
+ *   conf     [B, gamma] float32  confidence scores, each in (0, 1)
+ *   sps_B    [n_points] float64  batch sizes in tokens, strictly increasing
+ *   sps_val  [n_points] float64  steps per second at those sizes, > 0
+ *   budget   [B] int32 out       verify budgets in [0, gamma]
+ * Limits: n_points in [2, 1024], B * gamma <= 8192.
+ */
+int dspark_schedule(const float* conf, const double* sps_B, const double* sps_val,
+                    int n_points, int B, int gamma, int32_t* budget,
+                    void* workspace, void* stream);
+
+/*
+ * dspark_verify -- [P3] lossless verification with the [P4] bonus token.
+ *
+ * For request b with budget L = budget[b] (NULL: L = gamma), target row j of
+ * target_logits predicts block position j+1.  For k = 1..L:
+ *   p_k = softmax(target_logits[b, k-1] / T_b)
+ *   accept x_k iff u < min(1, p_k(x_k) / q_k(x_k)), u = uniform draw;
+ * the first rejection at position n+1 draws its replacement from
+ *   max(0, p_{n+1} - q_{n+1}) normalised (p_{n+1} if that has no mass),
+ * with q_{n+1} rebuilt from base_logits, U, W and draft_lse; if all L are
+ * accepted a bonus token is drawn from p_{L+1}.  Greedy requests (T_b = 0)
+ * accept x_k iff it is the target argmax (lowest index on ties) and emit the
+ * target argmax.
+ *
+ *   target_logits [B, gamma+1, V] logits_dtype
+ *   base_logits, U, W, prev0, temperature, seed, pos_offset: as given to
+ *                 dspark_draft_round for the same round
+ *   draft_tokens, draft_logq, draft_lse: its outputs
+ *   budget       [B] int32 or NULL
+ * Outputs:
+ *   out_tokens   [B, gamma+1] int32: x_1..x_n, final token, then -1
+ *   num_accepted [B] int32 n;  num_emitted [B] int32 n + 1
+ *   debug_logp_logq [B, gamma, 2] float32 or NULL: (ln p_k(x_k), ln q_k(x_k))
+ *                 at verified positions of sampled requests (untouched
+ *                 elsewhere)
+ *   debug_residual  [B, V] float32 or NULL: the normalised residual row of
+ *                 requests that rejected (untouched elsewhere)
+ */
+int dspark_verify(const void* target_logits, const void* base_logits, int logits_dtype,
+                  const void* U, const void* W, int factor_dtype,
+                  const int32_t* prev0, const int32_t* draft_tokens,
+                  const float* draft_logq, const double* draft_lse,
+                  const int32_t* budget, const float* temperature,
+                  uint64_t seed, const int32_t* pos_offset,
+                  int B, int gamma, int V, int r,
+                  int32_t* out_tokens, int32_t* num_accepted, int32_t* num_emitted,
+                  float* debug_logp_logq, float* debug_residual,
+                  void* workspace, void* stream);
+
+/* Synchronises `stream`, returns DSPARK_EDATA if any call on this workspace
+ * found bad data since the last dspark_status() (and clears the word), else
+ * DSPARK_OK; DSPARK_EHIP if the stream reports an error. */
+int dspark_status(void* workspace, void* stream);
+
+/* Timing of individual kernels (measurement support).  While enabled, every
+ * launch of the kernel class `kernel_class` is bracketed by HIP events on the
+ * caller's stream.  dspark_profile_read() synchronises the stream and returns
+ * the number of bracketed launches and their summed duration in ms, then
+ * clears the record.  Classes: 0 draft GEMM + softmax statistics, 1 draft
+ * sample, 2 target row statistics, 3 accept / bonus, 4 residual statistics,
+ * 5 residual sample, 6 scheduler. */
+int dspark_profile_enable(int kernel_class, int enabled);
+int dspark_profile_read(int kernel_class, int* launches, double* total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSPARK_H */

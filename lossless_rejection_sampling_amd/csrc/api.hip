@@ -1,0 +1,274 @@
+// C ABI of the DSpark round (declared in include/dspark.h): argument checks,
+// workspace layout, launch order and the per-kernel event timing.
+#include <stdint.h>
+#include <string.h>
+
+#include <mutex>
+#include <vector>
+
+#include "dspark.h"
+#include "kernels.hpp"
+
+namespace dspark {
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Workspace: [header | tile stats | block stats | request state | slot list | residual tile mass]
+struct Layout {
+  size_t header, tstat, bstat, req, slots, rsum, total;
+  int n_tiles, n_blk;
+};
+
+bool sizes_ok(int B, int gamma, int V, int r) {
+  return B >= 1 && gamma >= 1 && gamma <= 16 && V >= 1 && r >= 1 &&
+         (long long)B * (gamma + 1) <= (1ll << 31) / 4;
+}
+
+Layout layout(int B, int gamma, int V, int r) {
+  (void)r;
+  Layout L{};
+  L.n_tiles = (V + kTile - 1) / kTile;
+  L.n_blk = (V + kBlock - 1) / kBlock;
+  size_t off = 0;
+  L.header = off;
+  off = align_up(off + 256);
+  L.tstat = off;
+  off = align_up(off + (size_t)B * L.n_tiles * sizeof(TileStat));
+  L.bstat = off;
+  off = align_up(off + (size_t)B * (gamma + 1) * L.n_blk * sizeof(BlockStat));
+  L.req = off;
+  off = align_up(off + (size_t)B * sizeof(ReqState));
+  L.slots = off;
+  off = align_up(off + (size_t)B * sizeof(int32_t));
+  L.rsum = off;
+  off = align_up(off + (size_t)B * L.n_tiles * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+template <typename T> T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+bool dtype_ok(int d) { return d == DSPARK_BF16 || d == DSPARK_F32; }
+
+// ---------------------------------------------------------------------------
+// Kernel timing with HIP events (off unless enabled per class).
+// ---------------------------------------------------------------------------
+struct ProfState {
+  std::mutex mu;
+  bool on[kNumClasses] = {};
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> ev[kNumClasses];
+};
+ProfState& prof() {
+  static ProfState p;
+  return p;
+}
+
+}  // namespace
+
+ProfileScope::ProfileScope(int c, hipStream_t s) : cls(c), stream(s), ev0(nullptr), ev1(nullptr), on(false) {
+  ProfState& p = prof();
+  std::lock_guard<std::mutex> g(p.mu);
+  if (!p.on[cls]) return;
+  if (hipEventCreate(&ev0) != hipSuccess || hipEventCreate(&ev1) != hipSuccess) return;
+  on = hipEventRecord(ev0, stream) == hipSuccess;
+}
+
+ProfileScope::~ProfileScope() {
+  if (!on) return;
+  if (hipEventRecord(ev1, stream) != hipSuccess) return;
+  ProfState& p = prof();
+  std::lock_guard<std::mutex> g(p.mu);
+  p.ev[cls].emplace_back(ev0, ev1);
+}
+
+}  // namespace dspark
+
+using namespace dspark;
+
+#define DSPARK_TRY(expr)                  \
+  do {                                    \
+    if ((expr) != hipSuccess) return DSPARK_EHIP; \
+  } while (0)
+
+extern "C" {
+
+int dspark_abi_version(void) { return DSPARK_ABI_VERSION; }
+
+const char* dspark_error_string(int code) {
+  switch (code) {
+    case DSPARK_OK: return "ok";
+    case DSPARK_EINVAL: return "invalid argument";
+    case DSPARK_EHIP: return "HIP runtime error";
+    case DSPARK_EDATA: return "invalid input data found on the device";
+    default: return "unknown error";
+  }
+}
+
+size_t dspark_workspace_bytes(int B, int gamma, int V, int r) {
+  if (!sizes_ok(B, gamma, V, r)) return 0;
+  return layout(B, gamma, V, r).total;
+}
+
+int dspark_draft_round(const void* base_logits, int logits_dtype, const void* U, const void* W,
+                       int factor_dtype, const int32_t* prev0, const float* temperature,
+                       uint64_t seed, const int32_t* pos_offset, int B, int gamma, int V, int r,
+                       int32_t* draft_tokens, float* draft_logq, double* draft_lse, void* workspace,
+                       void* stream) {
+  if (!sizes_ok(B, gamma, V, r) || !dtype_ok(logits_dtype) || !dtype_ok(factor_dtype)) return DSPARK_EINVAL;
+  if (!base_logits || !U || !W || !prev0 || !temperature || !draft_tokens || !draft_logq || !draft_lse ||
+      !workspace)
+    return DSPARK_EINVAL;
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return DSPARK_EINVAL;
+  const Layout L = layout(B, gamma, V, r);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t* status = at<uint32_t>(workspace, L.header);
+
+  GemmArgs g{};
+  g.base = base_logits, g.U = U, g.Wt = W, g.prev0 = prev0, g.draft = draft_tokens;
+  g.temperature = temperature;
+  g.B = B, g.gamma = gamma, g.V = V, g.r = r, g.n_tiles = L.n_tiles;
+  g.tstat = at<TileStat>(workspace, L.tstat);
+  g.status = status;
+
+  DraftSelectArgs d{};
+  d.base = base_logits, d.U = U, d.Wt = W, d.prev0 = prev0, d.temperature = temperature;
+  d.pos_offset = pos_offset, d.tstat = g.tstat, d.seed = seed;
+  d.B = B, d.gamma = gamma, d.V = V, d.r = r, d.n_tiles = L.n_tiles;
+  d.draft = draft_tokens, d.logq = draft_logq, d.lse = draft_lse, d.status = status;
+
+  for (int pos = 0; pos < gamma; ++pos) {
+    g.pos = pos;
+    d.pos = pos;
+    {
+      ProfileScope ps(kClsDraftGemm, s);
+      DSPARK_TRY(launch_gemm_stats(g, logits_dtype, factor_dtype, false, s));
+    }
+    {
+      ProfileScope ps(kClsDraftSelect, s);
+      DSPARK_TRY(launch_draft_select(d, logits_dtype, factor_dtype, s));
+    }
+  }
+  return DSPARK_OK;
+}
+
+int dspark_schedule(const float* conf, const double* sps_B, const double* sps_val, int n_points,
+                    int B, int gamma, int32_t* budget, void* workspace, void* stream) {
+  if (B < 1 || gamma < 1 || gamma > 16 || (long long)B * gamma > 8192) return DSPARK_EINVAL;
+  if (n_points < 2 || n_points > 1024) return DSPARK_EINVAL;
+  if (!conf || !sps_B || !sps_val || !budget || !workspace) return DSPARK_EINVAL;
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return DSPARK_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  ScheduleArgs a{};
+  a.conf = conf, a.sps_B = sps_B, a.sps_val = sps_val, a.n_points = n_points;
+  a.B = B, a.gamma = gamma, a.budget = budget;
+  a.status = at<uint32_t>(workspace, 0);
+  ProfileScope ps(kClsSchedule, s);
+  DSPARK_TRY(launch_schedule(a, s));
+  return DSPARK_OK;
+}
+
+int dspark_verify(const void* target_logits, const void* base_logits, int logits_dtype, const void* U,
+                  const void* W, int factor_dtype, const int32_t* prev0, const int32_t* draft_tokens,
+                  const float* draft_logq, const double* draft_lse, const int32_t* budget,
+                  const float* temperature, uint64_t seed, const int32_t* pos_offset, int B, int gamma,
+                  int V, int r, int32_t* out_tokens, int32_t* num_accepted, int32_t* num_emitted,
+                  float* debug_logp_logq, float* debug_residual, void* workspace, void* stream) {
+  if (!sizes_ok(B, gamma, V, r) || !dtype_ok(logits_dtype) || !dtype_ok(factor_dtype)) return DSPARK_EINVAL;
+  if (!target_logits || !base_logits || !U || !W || !prev0 || !draft_tokens || !draft_logq || !draft_lse ||
+      !temperature || !out_tokens || !num_accepted || !num_emitted || !workspace)
+    return DSPARK_EINVAL;
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return DSPARK_EINVAL;
+  const Layout L = layout(B, gamma, V, r);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  VerifyArgs a{};
+  a.target = target_logits, a.base = base_logits, a.U = U, a.Wt = W, a.prev0 = prev0;
+  a.draft = draft_tokens, a.draft_logq = draft_logq, a.draft_lse = draft_lse, a.budget = budget;
+  a.temperature = temperature, a.pos_offset = pos_offset, a.seed = seed;
+  a.B = B, a.gamma = gamma, a.V = V, a.r = r, a.n_blk = L.n_blk, a.n_tiles = L.n_tiles;
+  a.bstat = at<BlockStat>(workspace, L.bstat);
+  a.req = at<ReqState>(workspace, L.req);
+  a.slot_req = at<int32_t>(workspace, L.slots);
+  a.slot_count = at<uint32_t>(workspace, L.header) + 1;
+  a.rsum = at<float>(workspace, L.rsum);
+  a.out_tokens = out_tokens, a.num_accepted = num_accepted, a.num_emitted = num_emitted;
+  a.debug_logp_logq = debug_logp_logq, a.debug_residual = debug_residual;
+  a.status = at<uint32_t>(workspace, L.header);
+
+  DSPARK_TRY(launch_verify_prep(a, s));
+  {
+    ProfileScope ps(kClsRowStats, s);
+    DSPARK_TRY(launch_row_stats(a, logits_dtype, s));
+  }
+  {
+    ProfileScope ps(kClsAccept, s);
+    DSPARK_TRY(launch_accept(a, logits_dtype, s));
+  }
+  {
+    GemmArgs g{};
+    g.base = base_logits, g.target = target_logits, g.U = U, g.Wt = W, g.prev0 = prev0;
+    g.draft = draft_tokens, g.temperature = temperature, g.draft_lse = draft_lse, g.req = a.req;
+    g.slot_req = a.slot_req, g.slot_count = a.slot_count;
+    g.B = B, g.gamma = gamma, g.V = V, g.r = r, g.n_tiles = L.n_tiles;
+    g.rsum = a.rsum, g.status = a.status;
+    ProfileScope ps(kClsResidualGemm, s);
+    DSPARK_TRY(launch_gemm_stats(g, logits_dtype, factor_dtype, true, s));
+  }
+  {
+    ProfileScope ps(kClsResidualSelect, s);
+    DSPARK_TRY(launch_residual_select(a, logits_dtype, factor_dtype, s));
+  }
+  if (debug_residual) DSPARK_TRY(launch_residual_debug(a, logits_dtype, factor_dtype, s));
+  return DSPARK_OK;
+}
+
+int dspark_status(void* workspace, void* stream) {
+  if (!workspace) return DSPARK_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t word = 0;
+  DSPARK_TRY(hipMemcpyAsync(&word, workspace, sizeof(word), hipMemcpyDeviceToHost, s));
+  DSPARK_TRY(hipStreamSynchronize(s));
+  if (word) {
+    DSPARK_TRY(hipMemsetAsync(workspace, 0, sizeof(word), s));
+    DSPARK_TRY(hipStreamSynchronize(s));
+    return DSPARK_EDATA;
+  }
+  return DSPARK_OK;
+}
+
+int dspark_profile_enable(int kernel_class, int enabled) {
+  if (kernel_class < 0 || kernel_class >= kNumClasses) return DSPARK_EINVAL;
+  ProfState& p = prof();
+  std::lock_guard<std::mutex> g(p.mu);
+  p.on[kernel_class] = enabled != 0;
+  return DSPARK_OK;
+}
+
+int dspark_profile_read(int kernel_class, int* launches, double* total_ms) {
+  if (kernel_class < 0 || kernel_class >= kNumClasses || !launches || !total_ms) return DSPARK_EINVAL;
+  ProfState& p = prof();
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> evs;
+  {
+    std::lock_guard<std::mutex> g(p.mu);
+    evs.swap(p.ev[kernel_class]);
+  }
+  double tot = 0.0;
+  int rc = DSPARK_OK;
+  for (auto& e : evs) {
+    float ms = 0.0f;
+    if (hipEventSynchronize(e.second) != hipSuccess || hipEventElapsedTime(&ms, e.first, e.second) != hipSuccess)
+      rc = DSPARK_EHIP;
+    tot += ms;
+    (void)hipEventDestroy(e.first);
+    (void)hipEventDestroy(e.second);
+  }
+  *launches = (int)evs.size();
+  *total_ms = tot;
+  return rc;
+}
+
+}  // extern "C"

@@ -1,0 +1,164 @@
+// Device-side building blocks of the DSpark round for gfx950: the counter-based
+// generator, bf16 handling, 64-lane wavefront reductions and the record types
+// kernels exchange through the workspace.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dspark {
+
+// Sampler partition: 64 elements per tile, 64 tiles per block.
+constexpr int kTile = 64;
+constexpr int kTilesPerBlock = 64;
+constexpr int kBlock = kTile * kTilesPerBlock;
+
+// Philox streams: which decision of the round a draw feeds.
+enum : uint32_t {
+  kDraftTop = 0, kDraftMid = 1, kDraftLeaf = 2,
+  kAccept = 3,
+  kFinalTop = 4, kFinalMid = 5, kFinalLeaf = 6,
+};
+
+// Bits of the workspace status word.
+enum : uint32_t {
+  kBadPrev = 1u, kBadDraft = 2u, kBadBudget = 4u, kBadTemp = 8u, kBadConf = 16u,
+};
+
+// Softmax statistics of one 64-column tile of one draft row:
+//   d(v) = ref + t(v) with ref an exact input value (the tile's largest backbone
+//   logit), mx = max_v t(v), sum = sum_v exp((t(v) - mx) / T).
+struct TileStat {
+  float ref, mx, sum, pad;
+};
+
+// Statistics of one 4096-column block of one target row:
+//   mx = max z (an input value), sum = sum exp((z - mx) / T), arg = lowest index
+//   of mx (greedy requests only).
+struct BlockStat {
+  float mx, sum;
+  int arg;
+  float pad;
+};
+
+// Per-request state handed from the accept pass to the residual pass.
+struct ReqState {
+  double row_max;    // max of target row n (an input value)
+  double row_logsum; // ln sum exp((z - row_max) / T) over target row n
+  double res_mass;   // total residual mass of the row (set by the residual draw)
+  int n;             // accepted count
+  int pending;       // 1 while the final token still has to be drawn from the residual
+};
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+template <typename TL> __device__ __forceinline__ float load_logit(const TL* p);
+template <> __device__ __forceinline__ float load_logit<uint16_t>(const uint16_t* p) {
+  return bf16_bits_to_f32(*p);
+}
+template <> __device__ __forceinline__ float load_logit<float>(const float* p) { return *p; }
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10 (J. K. Salmon et al., "Parallel Random Numbers: As Easy as 1,
+// 2, 3", SC'11): per round, words 0 and 2 are multiplied by two odd constants;
+// the high halves are xored with words 1 and 3 and the round key, the low
+// halves become the new words 1 and 3.  The key advances by two Weyl
+// increments between rounds.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int i = 0; i < 10; ++i) {
+    if (i) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint32_t lo0 = 0xD2511F53u * c.x, hi0 = __umulhi(0xD2511F53u, c.x);
+    const uint32_t lo1 = 0xCD9E8D57u * c.z, hi1 = __umulhi(0xCD9E8D57u, c.z);
+    c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
+  }
+  return c;
+}
+
+// Draw n of (stream, request, position): word n % 4 of the block n / 4.
+__device__ __forceinline__ uint32_t rng_word(uint64_t seed, uint32_t stream, uint32_t req,
+                                             uint32_t pos, uint32_t n) {
+  const uint4 o = philox4x32_10(make_uint4(n >> 2, pos, req, stream), (uint32_t)seed,
+                                (uint32_t)(seed >> 32));
+  const uint32_t j = n & 3u;
+  return j == 0 ? o.x : j == 1 ? o.y : j == 2 ? o.z : o.w;
+}
+
+// Uniform in (0, 1): the odd multiples of 2^-24, from the top 23 bits.
+__device__ __forceinline__ double uniform_from_word(uint32_t w) {
+  return ((double)(w >> 9) + 0.5) * 0x1p-23;
+}
+
+__device__ __forceinline__ double gumbel_from_word(uint32_t w) {
+  return -log(-log(uniform_from_word(w)));
+}
+
+__device__ __forceinline__ double gumbel(uint64_t seed, uint32_t stream, uint32_t req, uint32_t pos,
+                                         uint32_t n) {
+  return gumbel_from_word(rng_word(seed, stream, req, pos, n));
+}
+
+// ---------------------------------------------------------------------------
+// 64-lane reductions (every lane receives the result).
+// ---------------------------------------------------------------------------
+template <typename T> __device__ __forceinline__ T wave_max(T v) {
+#pragma unroll
+  for (int o = 32; o; o >>= 1) v = fmax(v, __shfl_xor(v, o));
+  return v;
+}
+template <typename T> __device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+  for (int o = 32; o; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ int wave_min_int(int v) {
+#pragma unroll
+  for (int o = 32; o; o >>= 1) v = min(v, __shfl_xor(v, o));
+  return v;
+}
+// Largest value; among equal values the lowest index.
+__device__ __forceinline__ void wave_argmax(double& v, int& i) {
+#pragma unroll
+  for (int o = 32; o; o >>= 1) {
+    const double ov = __shfl_xor(v, o);
+    const int oi = __shfl_xor(i, o);
+    if (ov > v || (ov == v && oi < i)) {
+      v = ov;
+      i = oi;
+    }
+  }
+}
+
+__device__ __forceinline__ void flag_status(uint32_t* status, uint32_t bit) {
+  atomicOr(status, bit);
+}
+
+// Token id checked against [0, V): out-of-range ids are reported and clamped.
+__device__ __forceinline__ int checked_token(int x, int V, uint32_t* status, uint32_t bit) {
+  if (x < 0 || x >= V) {
+    flag_status(status, bit);
+    return x < 0 ? 0 : V - 1;
+  }
+  return x;
+}
+
+// Temperatures below 2^-64 count as 0 (greedy), and so do NaN and negative
+// values, which checked_temp() also reports.
+__device__ __forceinline__ float effective_temp(float T) { return T >= 0x1p-64f ? T : 0.0f; }
+
+__device__ __forceinline__ float checked_temp(float T, uint32_t* status) {
+  if (!(T >= 0.0f)) flag_status(status, kBadTemp);
+  return effective_temp(T);
+}
+
+// An index produced by a reduction that found no candidate (only possible with
+// non-finite inputs) is replaced by `fallback` so that no access leaves its buffer.
+__device__ __forceinline__ int index_or(int i, int limit, int fallback) {
+  return (i >= 0 && i < limit) ? i : fallback;
+}
+
+}  // namespace dspark

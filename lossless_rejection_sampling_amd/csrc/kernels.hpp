@@ -1,0 +1,116 @@
+// Host-side launchers of the DSpark kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device.hpp"
+
+namespace dspark {
+
+enum KernelClass : int {
+  kClsDraftGemm = 0, kClsDraftSelect = 1, kClsRowStats = 2, kClsAccept = 3,
+  kClsResidualGemm = 4, kClsResidualSelect = 5, kClsSchedule = 6, kNumClasses = 7,
+};
+
+// Event bracketing of kernel launches (measurement support).
+struct ProfileScope {
+  ProfileScope(int cls, hipStream_t s);
+  ~ProfileScope();
+  int cls;
+  hipStream_t stream;
+  hipEvent_t ev0, ev1;
+  bool on;
+};
+
+// Arguments of the fused Markov-bias GEMM with its softmax-statistics epilogue.
+// Draft mode: one slot per request, base row `pos`; writes TileStat [B][n_tiles].
+// Residual mode: slots are the requests listed in slot_req[0..*slot_count), each
+// at its own row req[b].n; writes the residual mass of every tile [B][n_tiles].
+struct GemmArgs {
+  const void* base;          // [B, gamma, V]
+  const void* target;        // [B, gamma+1, V]        (residual mode)
+  const void* U;             // [V, r]
+  const void* Wt;            // [V, r]
+  const int32_t* prev0;      // [B]
+  const int32_t* draft;      // [B, gamma]
+  const float* temperature;  // [B]
+  const double* draft_lse;   // [B, gamma]             (residual mode)
+  const ReqState* req;       // [B]                    (residual mode)
+  const int32_t* slot_req;   // [B]                    (residual mode)
+  const uint32_t* slot_count;//                        (residual mode)
+  int B, gamma, V, r, n_tiles, pos;
+  TileStat* tstat;           // draft mode output
+  float* rsum;               // residual mode output
+  uint32_t* status;
+};
+
+hipError_t launch_gemm_stats(const GemmArgs& a, int logits_dtype, int factor_dtype, bool residual,
+                             hipStream_t s);
+
+struct DraftSelectArgs {
+  const void* base;
+  const void* U;
+  const void* Wt;
+  const int32_t* prev0;
+  const float* temperature;
+  const int32_t* pos_offset;
+  const TileStat* tstat;
+  uint64_t seed;
+  int B, gamma, V, r, n_tiles, pos;
+  int32_t* draft;
+  float* logq;
+  double* lse;
+  uint32_t* status;
+};
+
+hipError_t launch_draft_select(const DraftSelectArgs& a, int logits_dtype, int factor_dtype,
+                               hipStream_t s);
+
+struct VerifyArgs {
+  const void* target;
+  const void* base;
+  const void* U;
+  const void* Wt;
+  const int32_t* prev0;
+  const int32_t* draft;
+  const float* draft_logq;
+  const double* draft_lse;
+  const int32_t* budget;
+  const float* temperature;
+  const int32_t* pos_offset;
+  uint64_t seed;
+  int B, gamma, V, r, n_blk, n_tiles;
+  BlockStat* bstat;          // [B, gamma+1, n_blk]
+  ReqState* req;             // [B]
+  int32_t* slot_req;         // [B]
+  uint32_t* slot_count;
+  float* rsum;               // [B, n_tiles]
+  int32_t* out_tokens;
+  int32_t* num_accepted;
+  int32_t* num_emitted;
+  float* debug_logp_logq;
+  float* debug_residual;
+  uint32_t* status;
+};
+
+hipError_t launch_verify_prep(const VerifyArgs& a, hipStream_t s);
+hipError_t launch_row_stats(const VerifyArgs& a, int logits_dtype, hipStream_t s);
+hipError_t launch_accept(const VerifyArgs& a, int logits_dtype, hipStream_t s);
+hipError_t launch_residual_select(const VerifyArgs& a, int logits_dtype, int factor_dtype,
+                                  hipStream_t s);
+hipError_t launch_residual_debug(const VerifyArgs& a, int logits_dtype, int factor_dtype,
+                                 hipStream_t s);
+
+struct ScheduleArgs {
+  const float* conf;
+  const double* sps_B;
+  const double* sps_val;
+  int n_points, B, gamma;
+  int32_t* budget;
+  uint32_t* status;
+};
+
+hipError_t launch_schedule(const ScheduleArgs& a, hipStream_t s);
+
+}  // namespace dspark

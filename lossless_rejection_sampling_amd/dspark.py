@@ -1,0 +1,181 @@
+"""Python binding of libdspark.so: the C entry points under the same names.
+
+Argument marshalling only.  Each function checks that the tensors it is given
+are contiguous, of the expected dtype and on the GPU, turns them into device
+pointers and calls the library on the caller's current HIP stream.  Every step
+of the round runs in the library's kernels; when the library is missing or
+fails to load the calls raise instead of doing anything else.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "_lib", "libdspark.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "dspark.h")
+
+DSPARK_BF16, DSPARK_F32 = 0, 1
+DSPARK_OK, DSPARK_EINVAL, DSPARK_EHIP, DSPARK_EDATA = 0, -1, -2, -3
+KERNEL_CLASSES = {"draft_gemm": 0, "draft_select": 1, "row_stats": 2, "accept": 3,
+                  "residual_gemm": 4, "residual_select": 5, "schedule": 6}
+
+
+class DsparkError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        super().__init__(f"{fn} failed: {code} ({error_string(code)})")
+        self.code = code
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_SIG = {
+    "dspark_abi_version": (_I, []),
+    "dspark_error_string": (ctypes.c_char_p, [_I]),
+    "dspark_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
+    "dspark_draft_round": (_I, [_P, _I, _P, _P, _I, _P, _P, ctypes.c_uint64, _P,
+                                _I, _I, _I, _I, _P, _P, _P, _P, _P]),
+    "dspark_schedule": (_I, [_P, _P, _P, _I, _I, _I, _P, _P, _P]),
+    "dspark_verify": (_I, [_P, _P, _I, _P, _P, _I, _P, _P, _P, _P, _P, _P, ctypes.c_uint64, _P,
+                           _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]),
+    "dspark_status": (_I, [_P, _P]),
+    "dspark_profile_enable": (_I, [_I, _I]),
+    "dspark_profile_read": (_I, [_I, ctypes.POINTER(_I), ctypes.POINTER(ctypes.c_double)]),
+}
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run __graft_entry__.build() first")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIG.items():
+            fn = getattr(handle, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = handle
+    return _lib
+
+
+def declared_functions(header: str = HEADER):
+    """Names of the functions include/dspark.h declares."""
+    text = open(header).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dspark_[a-z_]+)\s*\(", text)))
+
+
+def error_string(code: int) -> str:
+    try:
+        return lib().dspark_error_string(code).decode()
+    except Exception:
+        return "unknown"
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DSPARK_BF16
+    if t.dtype == torch.float32:
+        return DSPARK_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(t: Optional[torch.Tensor], name: str, dtype=None, optional=False):
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(fn: str, rc: int):
+    if rc != DSPARK_OK:
+        raise DsparkError(fn, rc)
+
+
+def dspark_abi_version() -> int:
+    return lib().dspark_abi_version()
+
+
+def dspark_workspace_bytes(B: int, gamma: int, V: int, r: int) -> int:
+    return int(lib().dspark_workspace_bytes(B, gamma, V, r))
+
+
+def dspark_draft_round(base_logits, U, W, prev0, temperature, seed, pos_offset,
+                       draft_tokens, draft_logq, draft_lse, workspace, stream=None):
+    """base_logits [B, gamma, V]; U, W [V, r] (W = second factor, vocabulary-major)."""
+    B, gamma, V = base_logits.shape
+    r = U.shape[1]
+    if tuple(U.shape) != (V, r) or tuple(W.shape) != (V, r) or U.dtype != W.dtype:
+        raise ValueError("U and W must both be [V, r] of one dtype")
+    rc = lib().dspark_draft_round(
+        _dev(base_logits, "base_logits"), _dtype_code(base_logits), _dev(U, "U"), _dev(W, "W"),
+        _dtype_code(U), _dev(prev0, "prev0", torch.int32), _dev(temperature, "temperature", torch.float32),
+        int(seed) & (2 ** 64 - 1), _dev(pos_offset, "pos_offset", torch.int32, optional=True),
+        B, gamma, V, r, _dev(draft_tokens, "draft_tokens", torch.int32),
+        _dev(draft_logq, "draft_logq", torch.float32), _dev(draft_lse, "draft_lse", torch.float64),
+        _dev(workspace, "workspace", torch.uint8), _stream(stream))
+    _check("dspark_draft_round", rc)
+
+
+def dspark_schedule(conf, sps_B, sps_val, budget, workspace, stream=None):
+    B, gamma = conf.shape
+    rc = lib().dspark_schedule(
+        _dev(conf, "conf", torch.float32), _dev(sps_B, "sps_B", torch.float64),
+        _dev(sps_val, "sps_val", torch.float64), int(sps_B.numel()), B, gamma,
+        _dev(budget, "budget", torch.int32), _dev(workspace, "workspace", torch.uint8), _stream(stream))
+    _check("dspark_schedule", rc)
+
+
+def dspark_verify(target_logits, base_logits, U, W, prev0, draft_tokens, draft_logq, draft_lse,
+                  budget, temperature, seed, pos_offset, out_tokens, num_accepted, num_emitted,
+                  workspace, debug_logp_logq=None, debug_residual=None, stream=None):
+    B, gamma, V = base_logits.shape
+    r = U.shape[1]
+    if tuple(target_logits.shape) != (B, gamma + 1, V) or target_logits.dtype != base_logits.dtype:
+        raise ValueError("target_logits must be [B, gamma+1, V] with the dtype of base_logits")
+    rc = lib().dspark_verify(
+        _dev(target_logits, "target_logits"), _dev(base_logits, "base_logits"), _dtype_code(base_logits),
+        _dev(U, "U"), _dev(W, "W"), _dtype_code(U), _dev(prev0, "prev0", torch.int32),
+        _dev(draft_tokens, "draft_tokens", torch.int32), _dev(draft_logq, "draft_logq", torch.float32),
+        _dev(draft_lse, "draft_lse", torch.float64), _dev(budget, "budget", torch.int32, optional=True),
+        _dev(temperature, "temperature", torch.float32), int(seed) & (2 ** 64 - 1),
+        _dev(pos_offset, "pos_offset", torch.int32, optional=True), B, gamma, V, r,
+        _dev(out_tokens, "out_tokens", torch.int32), _dev(num_accepted, "num_accepted", torch.int32),
+        _dev(num_emitted, "num_emitted", torch.int32),
+        _dev(debug_logp_logq, "debug_logp_logq", torch.float32, optional=True),
+        _dev(debug_residual, "debug_residual", torch.float32, optional=True),
+        _dev(workspace, "workspace", torch.uint8), _stream(stream))
+    _check("dspark_verify", rc)
+
+
+def dspark_status(workspace, stream=None) -> int:
+    return int(lib().dspark_status(_dev(workspace, "workspace", torch.uint8), _stream(stream)))
+
+
+def dspark_profile_enable(kernel_class: int, enabled: bool = True):
+    _check("dspark_profile_enable", lib().dspark_profile_enable(int(kernel_class), int(bool(enabled))))
+
+
+def dspark_profile_read(kernel_class: int):
+    n = ctypes.c_int(0)
+    ms = ctypes.c_double(0.0)
+    _check("dspark_profile_read", lib().dspark_profile_read(int(kernel_class), ctypes.byref(n), ctypes.byref(ms)))
+    return n.value, ms.value

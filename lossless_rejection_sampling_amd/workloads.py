@@ -34,8 +34,8 @@ class Round:
     name: str
     target: torch.Tensor          # [B, gamma+1, V] bf16 or fp32 target logits
     base: torch.Tensor            # [B, gamma, V]   backbone draft logits, same dtype
-    U: torch.Tensor               # [V, r] first low-rank factor of the Markov head
-    W: torch.Tensor               # [r, V] second low-rank factor
+    U: torch.Tensor               # [V, r] first low-rank factor W1 of the Markov head
+    Wt: torch.Tensor              # [V, r] second factor W2 stored vocabulary-major (W2 = Wt^T)
     prev0: torch.Tensor           # [B] int32 last committed token of each request
     temperature: torch.Tensor     # [B] fp32, 0 = greedy
     seed: int                     # Philox key for this round
@@ -44,6 +44,11 @@ class Round:
     sps_B: Optional[np.ndarray] = None          # [n] float64 batch sizes (tokens), host
     sps_val: Optional[np.ndarray] = None        # [n] float64 steps per second, host
     budget: Optional[torch.Tensor] = None       # [B] int32 fixed verify budget, None = gamma
+
+    @property
+    def W(self) -> torch.Tensor:
+        """The second factor W2 as an [r, V] view."""
+        return self.Wt.t()
 
     @property
     def B(self) -> int:
@@ -66,9 +71,9 @@ class Round:
         return self.conf is not None
 
     def subset(self, idx) -> "Round":
-        """The same round restricted to the requests in ``idx`` (keeps request ids
-        meaning by returning ``pos``-independent copies; callers that need the
-        original request index for the RNG pass it separately)."""
+        """The same round restricted to the requests in ``idx``.  The Philox
+        counter of a request uses its index in the full batch, so a caller that
+        compares a subset passes ``idx`` on as the request ids."""
         idx_t = torch.as_tensor(idx, dtype=torch.long, device=self.base.device)
         pick = lambda t: None if t is None else t.index_select(0, idx_t)
         return dataclasses.replace(
@@ -115,10 +120,10 @@ def tiny(device="cpu") -> Round:
     target = _randn((B, gamma + 1, V), g, device, std=2.0)
     base = target[:, :gamma] + _randn((B, gamma, V), g, device, std=0.5)
     U = _randn((V, r), g, device, std=0.25)
-    W = _randn((r, V), g, device, std=0.25)
+    Wt = _randn((V, r), g, device, std=0.25)
     prev0 = torch.randint(0, V, (B,), generator=g, device=device, dtype=torch.int64).to(torch.int32)
     T = torch.ones(B, device=device, dtype=torch.float32)
-    return Round("tiny", target.contiguous(), base.contiguous(), U, W, prev0, T, seed=0)
+    return Round("tiny", target.contiguous(), base.contiguous(), U, Wt, prev0, T, seed=0)
 
 
 def _boosted_target(B, gamma, V, g, device, std=3.0, boost=6.0, frac=0.05):
@@ -140,10 +145,10 @@ def dspark5(B=64, V=151936, gamma=5, r=256, device="cpu", seed_base=1234 + 2, T=
     target = _boosted_target(B, gamma, V, g, device)
     base = (target[:, :gamma].float() + _randn((B, gamma, V), g, device)).to(torch.bfloat16)
     U = _randn((V, r), g, device, std=1.0 / 16.0, dtype=torch.bfloat16)
-    W = _randn((r, V), g, device, std=1.0 / 16.0, dtype=torch.bfloat16)
+    Wt = _randn((V, r), g, device, std=1.0 / 16.0, dtype=torch.bfloat16)
     prev0 = torch.randint(0, V, (B,), generator=g, device=device, dtype=torch.int64).to(torch.int32)
     Tt = torch.full((B,), T, device=device, dtype=torch.float32)
-    rnd = Round(name or f"dspark5_B{B}", target.contiguous(), base.contiguous(), U, W, prev0, Tt,
+    rnd = Round(name or f"dspark5_B{B}", target.contiguous(), base.contiguous(), U, Wt, prev0, Tt,
                 seed=20260706)
     if scheduled:
         rnd.conf = confidence_scores(B, gamma, g, device)
@@ -175,10 +180,10 @@ def block_length(gamma: int, B=256, V=151936, r=256, device="cpu") -> Round:
     noise = torch.randn((B, gamma, V), generator=g, device=device, dtype=torch.float32) * sig[None, :, None]
     base = (target[:, :gamma].float() + noise).to(torch.bfloat16)
     U = _randn((V, r), g, device, std=1.0 / 16.0, dtype=torch.bfloat16)
-    W = _randn((r, V), g, device, std=1.0 / 16.0, dtype=torch.bfloat16)
+    Wt = _randn((V, r), g, device, std=1.0 / 16.0, dtype=torch.bfloat16)
     prev0 = torch.randint(0, V, (B,), generator=g, device=device, dtype=torch.int64).to(torch.int32)
     Tt = torch.full((B,), 0.8, device=device, dtype=torch.float32)
-    return Round(f"block_length_g{gamma}", target.contiguous(), base.contiguous(), U, W, prev0, Tt,
+    return Round(f"block_length_g{gamma}", target.contiguous(), base.contiguous(), U, Wt, prev0, Tt,
                  seed=7000 + gamma)
 
 
@@ -204,10 +209,10 @@ def stress(B=1024, V=262144, gamma=8, r=256, device="cpu") -> Round:
     rows[tie_rows, tie_cols] = mx
     base = target[:, :gamma] + _randn((B, gamma, V), g, device, std=1.5)
     U = _randn((V, r), g, device, std=1.0 / 16.0, dtype=torch.bfloat16)
-    W = _randn((r, V), g, device, std=1.0 / 16.0, dtype=torch.bfloat16)
+    Wt = _randn((V, r), g, device, std=1.0 / 16.0, dtype=torch.bfloat16)
     prev0 = torch.randint(0, V, (B,), generator=g, device=device, dtype=torch.int64).to(torch.int32)
     Tt = torch.where(torch.arange(B, device=device) % 2 == 0, 0.0, 1.3).to(torch.float32)
-    rnd = Round(f"stress_B{B}", target.contiguous(), base.contiguous(), U, W, prev0, Tt, seed=99)
+    rnd = Round(f"stress_B{B}", target.contiguous(), base.contiguous(), U, Wt, prev0, Tt, seed=99)
     rnd.conf = confidence_scores(B, gamma, g, device)
     rnd.sps_B, rnd.sps_val = sps_table_linear()
     return rnd
@@ -222,12 +227,12 @@ def small_random(B, gamma, V, r, device="cpu", seed=0, dtype=torch.float32, fact
     fs = rank_std if rank_std is not None else 1.0 / math.sqrt(max(r, 1))
     fdt = factor_dtype or dtype
     U = _randn((V, r), g, device, std=math.sqrt(fs), dtype=fdt)
-    W = _randn((r, V), g, device, std=math.sqrt(fs), dtype=fdt)
+    Wt = _randn((V, r), g, device, std=math.sqrt(fs), dtype=fdt)
     prev0 = torch.randint(0, V, (B,), generator=g, device=device, dtype=torch.int64).to(torch.int32)
     tv = torch.tensor(temps, dtype=torch.float32, device=device)
     Tt = tv[torch.arange(B, device=device) % len(temps)]
     return Round(f"small_{B}x{gamma}x{V}", target.to(dtype).contiguous(), base.to(dtype).contiguous(),
-                 U, W, prev0, Tt, seed=seed)
+                 U, Wt, prev0, Tt, seed=seed)
 
 
 def to_host(t: Optional[torch.Tensor]) -> Optional[np.ndarray]:

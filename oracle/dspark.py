@@ -43,6 +43,13 @@ def _f64(a):
     return np.asarray(a, dtype=np.float64)
 
 
+def effective_temperature(T) -> float:
+    """Greedy decoding is the T -> 0 limit; temperatures below 2^-64 are taken
+    as that limit (T = 0)."""
+    T = float(T)
+    return T if T >= 2.0 ** -64 else 0.0
+
+
 def softmax(s):
     s = _f64(s)
     return np.exp(s - logsumexp(s))
@@ -85,7 +92,7 @@ def draft_round(base, U, W, prev0, temperature, seed: int, pos_offset=None, req_
         d_all = base[:, k - 1, :] + U[prev] @ W
         for b in range(B):
             d = d_all[b]
-            T = float(temperature[b])
+            T = effective_temperature(temperature[b])
             if T == 0.0:
                 x = argmax_first(d)
                 _, m = pick(d - d[x])
@@ -149,7 +156,7 @@ def verify(target, base, U, W, prev0, draft_tokens, temperature, seed: int, budg
         L = int(L_all[b])
         if not 0 <= L <= gamma:
             raise ValueError(f"budget {L} outside [0, {gamma}]")
-        T = float(temperature[b])
+        T = effective_temperature(temperature[b])
         rq, pos0 = int(req_ids[b]), int(off[b])
         xs = [int(prev0[b])] + [int(t) for t in draft_tokens[b]]
         n = 0

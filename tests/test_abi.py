@@ -1,0 +1,68 @@
+"""The C-ABI library loads, exports every function include/dspark.h declares,
+and rejects bad arguments on the host (no GPU work is launched by these calls)."""
+
+import ctypes
+import os
+
+import pytest
+
+from lossless_rejection_sampling_amd import dspark as ds
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ds.LIB_PATH):
+        from lossless_rejection_sampling_amd import build
+        build.build()
+    return ds.lib()
+
+
+def test_exports_every_declared_function(lib):
+    names = ds.declared_functions()
+    assert {"dspark_draft_round", "dspark_verify", "dspark_schedule"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_error_strings(lib):
+    assert ds.dspark_abi_version() == 1
+    assert ds.error_string(0) == "ok"
+    assert "argument" in ds.error_string(-1)
+    assert "device" in ds.error_string(-3)
+
+
+def test_workspace_size_rules(lib):
+    assert ds.dspark_workspace_bytes(256, 5, 151936, 256) > 0
+    assert ds.dspark_workspace_bytes(0, 5, 100, 8) == 0
+    assert ds.dspark_workspace_bytes(4, 0, 100, 8) == 0
+    assert ds.dspark_workspace_bytes(4, 17, 100, 8) == 0
+    assert ds.dspark_workspace_bytes(4, 5, 0, 8) == 0
+    small = ds.dspark_workspace_bytes(4, 4, 1024, 16)
+    assert small % 256 == 0 and small < ds.dspark_workspace_bytes(8, 4, 1024, 16)
+
+
+def test_host_argument_checks_return_einval(lib):
+    P = ctypes.c_void_p
+    nul = P(None)
+    fake = P(256)  # never dereferenced: the checks fail before any launch
+    # B = 0
+    rc = lib.dspark_draft_round(fake, 0, fake, fake, 0, fake, fake, 1, nul, 0, 5, 100, 16,
+                                fake, fake, fake, fake, nul)
+    assert rc == ds.DSPARK_EINVAL
+    # unknown dtype
+    rc = lib.dspark_draft_round(fake, 7, fake, fake, 0, fake, fake, 1, nul, 4, 5, 100, 16,
+                                fake, fake, fake, fake, nul)
+    assert rc == ds.DSPARK_EINVAL
+    # missing workspace
+    rc = lib.dspark_verify(fake, fake, 0, fake, fake, 0, fake, fake, fake, fake, nul, fake, 1, nul,
+                           4, 5, 100, 16, fake, fake, fake, nul, nul, nul, nul)
+    assert rc == ds.DSPARK_EINVAL
+    # misaligned workspace
+    rc = lib.dspark_verify(fake, fake, 0, fake, fake, 0, fake, fake, fake, fake, nul, fake, 1, nul,
+                           4, 5, 100, 16, fake, fake, fake, nul, nul, P(257), nul)
+    assert rc == ds.DSPARK_EINVAL
+    # scheduler limits: too many candidates, too few table points
+    assert lib.dspark_schedule(fake, fake, fake, 16, 1025, 8, fake, fake, nul) == ds.DSPARK_EINVAL
+    assert lib.dspark_schedule(fake, fake, fake, 1, 4, 4, fake, fake, nul) == ds.DSPARK_EINVAL
+    assert lib.dspark_status(nul, nul) == ds.DSPARK_EINVAL
+    assert lib.dspark_profile_enable(99, 1) == ds.DSPARK_EINVAL

@@ -1,0 +1,166 @@
+"""GPU round (through the C ABI) against the CPU oracle on the same seeded inputs.
+
+Small rounds are compared request by request in full; the full-size workloads
+(DSpark-5 at B=64 and B=256, block lengths 4/8/16 at B=256, the scheduled round
+at B=512 and the stress round at B=1024, V=262144) run the whole batch on the
+GPU in the configuration the benchmark times, and the oracle checks a sample of
+requests one by one plus the budgets of the whole batch.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from lossless_rejection_sampling_amd import dspark as ds
+from lossless_rejection_sampling_amd import round as rd
+from lossless_rejection_sampling_amd import workloads as wl
+from oracle import dspark as od
+
+from parity import check, compare, run_gpu, run_oracle, say
+
+pytestmark = [
+    pytest.mark.gpu,
+    pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU"),
+]
+
+DEV = "cuda"
+
+
+def _full(rnd, name, debug=True):
+    say(f"[{name}] B={rnd.B} gamma={rnd.gamma} V={rnd.V} r={rnd.r} dtype={rnd.base.dtype}")
+    buf = run_gpu(rnd, debug=debug)
+    assert ds.dspark_status(buf.workspace) == ds.DSPARK_OK
+    idx = np.arange(rnd.B)
+    rep = compare(rnd, buf, run_oracle(rnd, idx), idx)
+    check(rep, name)
+    return buf
+
+
+def test_tiny_round():
+    _full(wl.tiny(DEV), "tiny")
+
+
+@pytest.mark.parametrize("case", [
+    dict(B=24, gamma=5, V=1000, r=32, dtype=torch.float32, fdt=torch.bfloat16, temps=(1.0, 0.7, 1.5, 0.0)),
+    dict(B=24, gamma=5, V=1000, r=32, dtype=torch.bfloat16, fdt=torch.bfloat16, temps=(1.0, 0.0)),
+    dict(B=16, gamma=4, V=9000, r=16, dtype=torch.float32, fdt=torch.float32, temps=(1.0, 0.8)),
+    dict(B=16, gamma=3, V=4097, r=48, dtype=torch.bfloat16, fdt=torch.bfloat16, temps=(1.3,)),
+    dict(B=8, gamma=2, V=8, r=16, dtype=torch.float32, fdt=torch.bfloat16, temps=(1.0, 0.0)),
+    dict(B=8, gamma=6, V=65, r=20, dtype=torch.float32, fdt=torch.bfloat16, temps=(0.9,)),
+    dict(B=1, gamma=16, V=2048, r=64, dtype=torch.bfloat16, fdt=torch.bfloat16, temps=(1.0,)),
+    dict(B=300, gamma=2, V=700, r=16, dtype=torch.float32, fdt=torch.bfloat16, temps=(1.0, 0.0, 2.0)),
+])
+def test_small_rounds(case):
+    rnd = wl.small_random(case["B"], case["gamma"], case["V"], case["r"], device=DEV, seed=case["B"] + case["V"],
+                          dtype=case["dtype"], factor_dtype=case["fdt"], temps=case["temps"])
+    g = torch.Generator(device="cpu").manual_seed(5)
+    rnd.budget = torch.randint(0, rnd.gamma + 1, (rnd.B,), generator=g, dtype=torch.int32).to(DEV)
+    rnd.pos_offset = torch.randint(0, 1 << 20, (rnd.B,), generator=g, dtype=torch.int32).to(DEV)
+    _full(rnd, f"small_{case['B']}x{case['gamma']}x{case['V']}_r{case['r']}")
+
+
+def test_identical_draft_always_accepts():
+    rnd = wl.small_random(32, 4, 3000, 16, device=DEV, seed=3, temps=(1.0, 0.6))
+    rnd.base = rnd.target[:, :4].contiguous()
+    rnd.Wt = torch.zeros_like(rnd.Wt)
+    buf = _full(rnd, "identical_draft")
+    assert torch.all(buf.num_accepted == 4)
+
+
+def test_zero_budget_is_plain_decode():
+    rnd = wl.small_random(16, 4, 5000, 32, device=DEV, seed=4, factor_dtype=torch.bfloat16,
+                          temps=(1.0, 0.0))
+    rnd.budget = torch.zeros(16, dtype=torch.int32, device=DEV)
+    buf = _full(rnd, "zero_budget")
+    assert torch.all(buf.num_accepted == 0) and torch.all(buf.num_emitted == 1)
+
+
+def test_deterministic_and_position_offsets():
+    rnd = wl.small_random(16, 5, 5000, 32, device=DEV, seed=9, factor_dtype=torch.bfloat16)
+    a = run_gpu(rnd)
+    b = run_gpu(rnd)
+    assert torch.equal(a.out_tokens, b.out_tokens) and torch.equal(a.draft_tokens, b.draft_tokens)
+    rnd.pos_offset = torch.full((16,), 1000, dtype=torch.int32, device=DEV)
+    c = run_gpu(rnd)
+    assert not torch.equal(a.draft_tokens, c.draft_tokens)
+
+
+def test_bad_data_is_reported_not_faulted():
+    rnd = wl.small_random(8, 3, 500, 16, device=DEV, seed=1)
+    rnd.prev0 = rnd.prev0.clone()
+    rnd.prev0[3] = 10 ** 6          # out of range: clamped on the device, reported
+    rnd.budget = torch.tensor([3, 3, 9, 3, -1, 3, 3, 3], dtype=torch.int32, device=DEV)
+    buf = run_gpu(rnd)
+    assert ds.dspark_status(buf.workspace) == ds.DSPARK_EDATA
+    assert ds.dspark_status(buf.workspace) == ds.DSPARK_OK   # cleared
+    n = buf.num_accepted.cpu().numpy()
+    assert n.min() >= 0 and n.max() <= 3
+
+
+def test_scheduler_bit_exact():
+    Bs, sps = wl.sps_table_linear()
+    for B, gamma, seed in [(7, 3, 0), (256, 5, 1), (512, 5, 2), (1024, 8, 3), (64, 16, 4)]:
+        say(f"[schedule] B={B} gamma={gamma}")
+        g = torch.Generator(device=DEV).manual_seed(seed)
+        conf = wl.confidence_scores(B, gamma, g, DEV)
+        budget = torch.empty(B, dtype=torch.int32, device=DEV)
+        ws = torch.zeros(4096, dtype=torch.uint8, device=DEV)
+        ds.dspark_schedule(conf, torch.tensor(Bs, device=DEV), torch.tensor(sps, device=DEV), budget, ws)
+        ref = od.schedule(conf.cpu().numpy(), Bs, sps)
+        assert ref.min_gap > od.SCHED_FLAG
+        assert np.array_equal(budget.cpu().numpy(), ref.budget)
+    # special tables: constant rate admits every candidate with Q > 0; t ~ N admits none
+    conf = torch.full((64, 4), 0.5, device=DEV)
+    budget = torch.empty(64, dtype=torch.int32, device=DEV)
+    ws = torch.zeros(4096, dtype=torch.uint8, device=DEV)
+    ds.dspark_schedule(conf, torch.tensor([1.0, 1024.0], device=DEV, dtype=torch.float64),
+                       torch.tensor([50.0, 50.0], device=DEV, dtype=torch.float64), budget, ws)
+    assert torch.all(budget == 4)
+    pts = torch.tensor([1.0, 8.0, 64.0, 1024.0], device=DEV, dtype=torch.float64)
+    ds.dspark_schedule(conf, pts, 1.0 / pts, budget, ws)
+    assert torch.all(budget == 0)
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads: the whole batch on the GPU, a sample through the oracle.
+# ---------------------------------------------------------------------------
+
+def _sampled(rnd, name, n_sample, seed=0):
+    say(f"[{name}] B={rnd.B} gamma={rnd.gamma} V={rnd.V} r={rnd.r} dtype={rnd.base.dtype}")
+    buf = run_gpu(rnd, debug=True)
+    assert ds.dspark_status(buf.workspace) == ds.DSPARK_OK
+    n = buf.num_accepted.cpu().numpy()
+    L = buf.budget.cpu().numpy() if buf.budget is not None else np.full(rnd.B, rnd.gamma)
+    assert np.all((0 <= n) & (n <= L)) and np.all(L <= rnd.gamma)
+    out = buf.out_tokens.cpu().numpy()
+    assert np.all(out[np.arange(rnd.B), n] >= 0) and np.all(out < rnd.V)
+    rng = np.random.default_rng(seed)
+    idx = np.sort(rng.choice(rnd.B, size=min(n_sample, rnd.B), replace=False))
+    ref = run_oracle(rnd, idx)
+    if ref.sched is not None:
+        assert np.array_equal(buf.budget.cpu().numpy(), ref.sched.budget)
+    check(compare(rnd, buf, ref, idx), name)
+    return buf
+
+
+def test_dspark5_b64():
+    _sampled(wl.dspark5(device=DEV), "dspark5_B64", 16)
+
+
+def test_headline_b256():
+    _sampled(wl.headline(device=DEV), "headline_B256", 12)
+
+
+@pytest.mark.parametrize("gamma", [4, 8, 16])
+def test_block_length(gamma):
+    _sampled(wl.block_length(gamma, device=DEV), f"block_length_g{gamma}", 6)
+
+
+def test_scheduled_b512():
+    _sampled(wl.scheduled(device=DEV), "scheduled_B512", 8)
+
+
+def test_stress_b1024():
+    rnd = wl.stress(device=DEV)
+    _sampled(rnd, "stress_B1024", 8)
+    torch.cuda.empty_cache()
