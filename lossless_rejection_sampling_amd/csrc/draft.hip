@@ -190,6 +190,244 @@ __global__ __launch_bounds__(256) void gemm_stats_mfma(GemmArgs a) {
   }
 }
 
+constexpr int kSlotsPerGroup = 256;
+
+// ---------------------------------------------------------------------------
+// Pipelined MFMA path (bf16 factors, R in {64, 128, 256}): the main kernel.
+//
+// Workgroup = 8 wavefronts (two per SIMD), wave w owning slots sg0 + 32w .. +31
+// of a 256-slot group (grid.y); grid.x is a persistent index over 64-column
+// tiles, all wavefronts of a workgroup working on the same tile.
+//   * B operands: the gathered rows h_s = U[prev_s] of the wave's 32 slots stay
+//     in registers for the whole kernel.
+//   * A operands: the tile's W2 rows are streamed into a two-slot LDS ring by
+//     direct global->LDS loads, laid out as operand blocks (column block vb,
+//     k-step ks) of 64 lanes x 16 B, so each MFMA operand is one conflict-free
+//     1 KB ds_read_b128.
+//   * The backbone logits the epilogue needs are loaded one tile ahead into
+//     registers (the residual pass loads its target logits at the start of
+//     the epilogue).  Only the last tile can be ragged; it takes a
+//     separate, masked load path so the loop has no per-lane branches around
+//     its loads.
+//   * Iteration i issues the W2 load of tile i+2, the logits of tile i+1 and the
+//     MFMAs of tile i+1, then runs the softmax epilogue of tile i; the barrier
+//     at its end waits only for the W2 load, the oldest outstanding one.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+constexpr int kLdsWaves = 8;
+
+// Logits of one tile for one 32-slot block: 2 column blocks x 16 accumulator
+// rows, as loaded (bf16 pairs per 32-bit register, or fp32); missing columns
+// read as -inf.
+template <typename TL> struct TileBuf;
+template <> struct TileBuf<uint16_t> {
+  uint32_t w[2][8];
+  __device__ __forceinline__ float get(int vb, int e) const {
+    const uint32_t u = w[vb][e >> 1];
+    return (e & 1) ? __uint_as_float(u & 0xffff0000u) : __uint_as_float(u << 16);
+  }
+};
+template <> struct TileBuf<float> {
+  float f[2][16];
+  __device__ __forceinline__ float get(int vb, int e) const { return f[vb][e]; }
+};
+
+// Loads of one tile: `full` (uniform) selects unmasked vector loads.
+template <typename TL>
+__device__ __forceinline__ void load_tile(const TL* row, int v0, int half, int V, bool full, TileBuf<TL>& x) {
+  if (full) {
+#pragma unroll
+    for (int vb = 0; vb < 2; ++vb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const TL* p = row + v0 + vb * 32 + g * 8 + half * 4;
+        if constexpr (sizeof(TL) == 2) {
+          const uint2 u = *reinterpret_cast<const uint2*>(p);
+          x.w[vb][2 * g] = u.x, x.w[vb][2 * g + 1] = u.y;
+        } else {
+          const float4 f = *reinterpret_cast<const float4*>(p);
+          x.f[vb][4 * g] = f.x, x.f[vb][4 * g + 1] = f.y, x.f[vb][4 * g + 2] = f.z, x.f[vb][4 * g + 3] = f.w;
+        }
+      }
+  } else {
+#pragma unroll
+    for (int vb = 0; vb < 2; ++vb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int v = v0 + vb * 32 + g * 8 + half * 4;
+        if constexpr (sizeof(TL) == 2) {
+          uint32_t h[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) h[e] = (v + e < V) ? (uint32_t)row[v + e] : 0xff80u;
+          x.w[vb][2 * g] = h[0] | (h[1] << 16), x.w[vb][2 * g + 1] = h[2] | (h[3] << 16);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x.f[vb][4 * g + e] = (v + e < V) ? row[v + e] : -INFINITY;
+        }
+      }
+  }
+}
+
+template <typename TL, bool RESIDUAL>
+__device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const f32x16 (&acc)[2], const TileBuf<TL>& x,
+                                              const TL* trow, int rq, int pos, bool valid, float T, int tile,
+                                              int half, bool full) {
+  float ref = -INFINITY;
+#pragma unroll
+  for (int vb = 0; vb < 2; ++vb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) ref = fmaxf(ref, x.get(vb, e));
+  ref = fmaxf(ref, __shfl_xor(ref, 32));
+  float t[2][16];
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int vb = 0; vb < 2; ++vb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      t[vb][e] = (x.get(vb, e) - ref) + acc[vb][e];
+      tmax = fmaxf(tmax, t[vb][e]);
+    }
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+  if constexpr (!RESIDUAL) {
+    const float c = T > 0.0f ? kLog2e / T : 0.0f;
+    const float mc = tmax * c;
+    float s = 0.0f;
+#pragma unroll
+    for (int vb = 0; vb < 2; ++vb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s += __builtin_amdgcn_exp2f(fmaf(t[vb][e], c, -mc));
+    s += __shfl_xor(s, 32);
+    if (half == 0 && valid) {
+      TileStat st;
+      st.ref = ref, st.mx = tmax, st.sum = s, st.pad = 0.0f;
+      a.tstat[(size_t)rq * a.n_tiles + tile] = st;
+    }
+  } else {
+    TileBuf<TL> z;
+    load_tile<TL>(trow, tile * kTile, half, a.V, full, z);
+    float rs = 0.0f;
+    if (valid) {
+      const ReqState st = a.req[rq];
+      const float c = kLog2e / T;
+      const float kp = (float)(((double)st.row_max / (double)T + st.row_logsum) * 1.4426950408889634);
+      const double lse_q = a.draft_lse[(size_t)rq * a.gamma + pos];
+      const float kq = (float)((lse_q - (double)ref / (double)T) * 1.4426950408889634);
+#pragma unroll
+      for (int vb = 0; vb < 2; ++vb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(z.get(vb, e), c, -kp));
+          const float q = __builtin_amdgcn_exp2f(fmaf(t[vb][e], c, -kq));
+          rs += fmaxf(p - q, 0.0f);
+        }
+    }
+    rs += __shfl_xor(rs, 32);
+    if (half == 0 && valid) a.rsum[(size_t)rq * a.n_tiles + tile] = rs;
+  }
+}
+
+template <typename TL, bool RESIDUAL, int R>
+__global__ __launch_bounds__(512, 1) void gemm_stats_lds(GemmArgs a) {
+  constexpr int KS = R / 16, NBLK = 2 * KS, TILE_BYTES = NBLK * 1024;
+  constexpr bool PF = true;  // backbone logits prefetched a tile ahead (the residual pass
+                             // loads its target logits at the start of the epilogue)
+  extern __shared__ __attribute__((aligned(1024))) char lds[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nwaves = blockDim.x >> 6;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int nslots = RESIDUAL ? (int)*a.slot_count : a.B;
+  const int sg0 = blockIdx.y * kSlotsPerGroup;
+  const int nt = a.n_tiles, G = gridDim.x;
+  if (sg0 >= nslots || (int)blockIdx.x >= nt) return;  // uniform across the workgroup
+  const int V = a.V;
+  const uint16_t* Wt = static_cast<const uint16_t*>(a.Wt);
+
+  // this wave's 32 slots: request, row, temperature and gathered U row
+  const bool active = sg0 + wave * 32 < nslots;
+  int rq, pos, prev;
+  bool valid;
+  slot_info<RESIDUAL>(a, sg0 + wave * 32 + l32, nslots, rq, pos, prev, valid);
+  const TL* brow = static_cast<const TL*>(a.base) + ((size_t)rq * a.gamma + pos) * V;
+  const TL* trow = RESIDUAL ? static_cast<const TL*>(a.target) + ((size_t)rq * (a.gamma + 1) + pos) * V : brow;
+  const float T = valid ? effective_temp(a.temperature[rq]) : 1.0f;
+  bf16x8 H[KS];
+  {
+    const uint16_t* h = static_cast<const uint16_t*>(a.U) + (size_t)prev * R + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 zero = {};
+      H[ks] = valid ? *reinterpret_cast<const bf16x8*>(h + ks * 16) : zero;
+    }
+  }
+
+  auto fill = [&](int tile, int buf) {  // this wave's share of the tile's operand blocks
+    for (int j = wave; j < NBLK; j += nwaves) {
+      const int vb = j / KS, ks = j - vb * KS;
+      int v = tile * kTile + vb * 32 + l32;
+      v = v < V ? v : V - 1;  // columns beyond V are masked in the epilogue
+      __builtin_amdgcn_global_load_lds(Wt + (size_t)v * R + ks * 16 + half * 8,
+                                       (lds_ptr_t)(lds + buf * TILE_BYTES + j * 1024), 16, 0, 0);
+    }
+  };
+  auto mma = [&](int buf, f32x16 (&acc)[2]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][e] = 0.0f;
+    const char* base = lds + buf * TILE_BYTES + lane * 16;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8 A[2];
+#pragma unroll
+      for (int vb = 0; vb < 2; ++vb) A[vb] = *reinterpret_cast<const bf16x8*>(base + (vb * KS + ks) * 1024);
+#pragma unroll
+      for (int vb = 0; vb < 2; ++vb) acc[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[vb], H[ks], acc[vb], 0, 0, 0);
+    }
+  };
+  auto full_tile = [&](int tile) { return (tile + 1) * kTile <= V; };
+  // Wait until at most `newer` vector-memory loads issued after the W2 fill are
+  // still in flight (loads complete in order), then synchronise the workgroup.
+  auto sync_fill = [&](bool wait_all) {
+    if (wait_all) __builtin_amdgcn_s_waitcnt(0xF70);        // vmcnt(0)
+    else __builtin_amdgcn_s_waitcnt(0xF70 | 8);             // vmcnt(8): the 8 logit loads may stay in flight
+    __syncthreads();
+  };
+
+  f32x16 acc0[2], acc1[2];
+  TileBuf<TL> x0, x1;
+  int t = blockIdx.x;
+  fill(t, 0);
+  if (PF && active) load_tile<TL>(brow, t * kTile, half, V, full_tile(t), x0);
+  sync_fill(true);
+  if (t + G < nt) fill(t + G, 1);
+  if (active) mma(0, acc0);
+  sync_fill(true);
+
+  for (;;) {
+    // tile t: acc0, x0, W2 buffer 0; tile t+G ready in buffer 1
+    if (t + 2 * G < nt) fill(t + 2 * G, 0);
+    const bool more = t + G < nt;
+    if (more && active) {
+      if (PF) load_tile<TL>(brow, (t + G) * kTile, half, V, full_tile(t + G), x1);
+      mma(1, acc1);
+    }
+    if (active) epilogue_tile<TL, RESIDUAL>(a, acc0, x0, trow, rq, pos, valid, T, t, half, full_tile(t));
+    sync_fill(!(PF && more && active && full_tile(t + G)));
+    t += G;
+    if (t >= nt) break;
+    // tile t: acc1, x1, buffer 1; tile t+G ready in buffer 0
+    if (t + 2 * G < nt) fill(t + 2 * G, 1);
+    const bool more2 = t + G < nt;
+    if (more2 && active) {
+      if (PF) load_tile<TL>(brow, (t + G) * kTile, half, V, full_tile(t + G), x0);
+      mma(0, acc0);
+    }
+    if (active) epilogue_tile<TL, RESIDUAL>(a, acc1, x1, trow, rq, pos, valid, T, t, half, full_tile(t));
+    sync_fill(!(PF && more2 && active && full_tile(t + G)));
+    t += G;
+    if (t >= nt) break;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // VALU path (any factor type and rank): one wavefront per (slot, tile), one
 // column per lane.
@@ -241,14 +479,40 @@ __global__ __launch_bounds__(64) void gemm_stats_valu(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// One draw per request at block position pos+1: three-level Gumbel-max over
-// blocks of 64 tiles, tiles of 64 columns, and columns, from the tile
-// statistics; the chosen tile is recomputed in fp64.  Greedy requests take the
-// tile with the largest logit and its argmax (lowest index on ties).
+// One draw per request at block position pos+1 (a workgroup of 4 wavefronts
+// per request): three-level Gumbel-max over blocks of 64 tiles, tiles of 64
+// columns, and columns.  Block and tile levels use the tile statistics (one
+// coalesced 1 KB read per block); the chosen tile is recomputed in fp64 with
+// the rank split over the four wavefronts.  Greedy requests take the tile with
+// the largest logit and its argmax (lowest index on ties).
 // ---------------------------------------------------------------------------
+template <typename TF>
+__device__ __forceinline__ double dot_part(const TF* h, const TF* w, int k0, int k1) {
+  double acc = 0.0;
+  if constexpr (sizeof(TF) == 2) {
+    if (((k1 - k0) & 7) == 0 && (k0 & 7) == 0) {
+      for (int k = k0; k < k1; k += 8) {
+        const uint4 hv = *reinterpret_cast<const uint4*>(h + k);
+        const uint4 wv = *reinterpret_cast<const uint4*>(w + k);
+        const uint32_t hh[4] = {hv.x, hv.y, hv.z, hv.w}, ww[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc += (double)__uint_as_float(hh[q] << 16) * (double)__uint_as_float(ww[q] << 16);
+          acc += (double)__uint_as_float(hh[q] & 0xffff0000u) * (double)__uint_as_float(ww[q] & 0xffff0000u);
+        }
+      }
+      return acc;
+    }
+  }
+  for (int k = k0; k < k1; ++k) acc += (double)load_logit(h + k) * (double)load_logit(w + k);
+  return acc;
+}
+
 template <typename TL, typename TF>
-__global__ __launch_bounds__(64) void draft_select_kernel(DraftSelectArgs a) {
-  const int b = blockIdx.x, lane = threadIdx.x;
+__global__ __launch_bounds__(256) void draft_select_kernel(DraftSelectArgs a) {
+  __shared__ double s_val[4], s_m[4], s_s[4], s_part[4][64];
+  __shared__ int s_idx[4];
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int V = a.V, r = a.r, gamma = a.gamma, nt = a.n_tiles, pos = a.pos;
   const uint32_t rpos = (uint32_t)(pos + 1 + (a.pos_offset ? a.pos_offset[b] : 0));
   const float Tf = checked_temp(a.temperature[b], a.status);
@@ -258,47 +522,49 @@ __global__ __launch_bounds__(64) void draft_select_kernel(DraftSelectArgs a) {
   const TL* brow = static_cast<const TL*>(a.base) + ((size_t)b * gamma + pos) * V;
   const TF* h = static_cast<const TF*>(a.U) + (size_t)prev * r;
   const TF* Wt = static_cast<const TF*>(a.Wt);
+  const int nblk = (nt + kTilesPerBlock - 1) / kTilesPerBlock;
 
-  auto recompute = [&](int v) -> double {  // d(v) in fp64
-    const TF* w = Wt + (size_t)v * r;
-    double acc = 0.0;
-    for (int k = 0; k < r; ++k) acc += (double)load_logit(h + k) * (double)load_logit(w + k);
-    return (double)load_logit(brow + v) + acc;
-  };
-
-  int x;
-  double logq, lse;
+  int tile;  // chosen tile
+  double invT = 0.0, lse = 0.0;
   if (Tf > 0.0f) {
-    const double invT = 1.0 / (double)Tf;
+    invT = 1.0 / (double)Tf;
     const double mref = (double)ts[0].ref + (double)ts[0].mx;
-    const int nblk = (nt + kTilesPerBlock - 1) / kTilesPerBlock;
-    double row_m = -INFINITY, row_s = 0.0, best = -INFINITY;
+    double best = -INFINITY, row_m = -INFINITY, row_s = 0.0;
     int best_blk = 0x7fffffff;
-    for (int g = 0; g < nblk; g += 64) {
-      const int blk = g + lane;
-      if (blk < nblk) {
-        const int t0 = blk * kTilesPerBlock, t1 = min(t0 + kTilesPerBlock, nt);
-        double dmax = -INFINITY;
-        for (int t = t0; t < t1; ++t) dmax = fmax(dmax, (double)ts[t].ref + (double)ts[t].mx);
-        float s = 0.0f;
-        for (int t = t0; t < t1; ++t)
-          s += ts[t].sum * expf((float)(((double)ts[t].ref + (double)ts[t].mx - dmax) * invT));
-        const double val = (dmax - mref) * invT + log((double)s) + gumbel(a.seed, kDraftTop, b, rpos, blk);
-        if (val > best) best = val, best_blk = blk;
-        if (dmax > row_m) {
-          row_s = row_s * exp((row_m - dmax) * invT) + s;
-          row_m = dmax;
-        } else {
-          row_s += s * exp((dmax - row_m) * invT);
-        }
+    for (int blk = wave; blk < nblk; blk += 4) {
+      const int t = blk * kTilesPerBlock + lane;
+      double d = -INFINITY;
+      float sum = 0.0f;
+      if (t < nt) {
+        const TileStat st = ts[t];
+        d = (double)st.ref + (double)st.mx;
+        sum = st.sum;
+      }
+      const double dmax = wave_max(d);
+      const float e = t < nt ? sum * expf((float)((d - dmax) * invT)) : 0.0f;
+      const double sblk = (double)wave_sum(e);
+      const double val = (dmax - mref) * invT + log(sblk) + gumbel(a.seed, kDraftTop, b, rpos, blk);
+      if (val > best) best = val, best_blk = blk;
+      if (dmax > row_m) {
+        row_s = row_s * exp((row_m - dmax) * invT) + sblk;
+        row_m = dmax;
+      } else {
+        row_s += sblk * exp((dmax - row_m) * invT);
       }
     }
-    wave_argmax(best, best_blk);
-    best_blk = index_or(best_blk, nblk, 0);
-    const double M = wave_max(row_m);
-    const double S = wave_sum(row_s > 0.0 ? row_s * exp((row_m - M) * invT) : 0.0);
+    if (lane == 0) s_val[wave] = best, s_idx[wave] = best_blk, s_m[wave] = row_m, s_s[wave] = row_s;
+    __syncthreads();
+    double M = -INFINITY;
+    for (int w = 0; w < 4; ++w) M = fmax(M, s_m[w]);
+    double S = 0.0;
+    for (int w = 0; w < 4; ++w)
+      if (s_s[w] > 0.0) S += s_s[w] * exp((s_m[w] - M) * invT);
     lse = M * invT + log(S);
-
+    best = -INFINITY, best_blk = 0x7fffffff;
+    for (int w = 0; w < 4; ++w)
+      if (s_val[w] > best || (s_val[w] == best && s_idx[w] < best_blk)) best = s_val[w], best_blk = s_idx[w];
+    best_blk = index_or(best_blk, nblk, 0);
+    // tile inside the chosen block (every wavefront computes the same choice)
     const int t0 = best_blk * kTilesPerBlock, t1 = min(t0 + kTilesPerBlock, nt);
     double val = -INFINITY;
     int ti = 0x7fffffff;
@@ -309,47 +575,82 @@ __global__ __launch_bounds__(64) void draft_select_kernel(DraftSelectArgs a) {
       ti = t0 + lane;
     }
     wave_argmax(val, ti);
-    ti = index_or(ti, nt, t0);
-
-    const int v = ti * kTile + lane;
-    double sv = -INFINITY, lv = -INFINITY;
-    int vi = 0x7fffffff;
-    if (v < V) {
-      sv = recompute(v) / (double)Tf;
-      lv = sv + gumbel(a.seed, kDraftLeaf, b, rpos, lane);
-      vi = v;
-    }
-    wave_argmax(lv, vi);
-    x = index_or(vi, min(V, (ti + 1) * kTile), ti * kTile);
-    const double sx = __shfl(sv, x - ti * kTile);
-    logq = sx - lse;
+    tile = index_or(ti, t1, t0);
   } else {
     double best = -INFINITY;
     int bt = 0x7fffffff;
-    for (int t = lane; t < nt; t += 64) {
+    for (int t = tid; t < nt; t += 256) {
       const double d = (double)ts[t].ref + (double)ts[t].mx;
       if (d > best) best = d, bt = t;
     }
     wave_argmax(best, bt);
-    bt = index_or(bt, nt, 0);
-    const int v = bt * kTile + lane;
-    double d = -INFINITY;
+    if (lane == 0) s_val[wave] = best, s_idx[wave] = bt;
+    __syncthreads();
+    best = -INFINITY, bt = 0x7fffffff;
+    for (int w = 0; w < 4; ++w)
+      if (s_val[w] > best || (s_val[w] == best && s_idx[w] < bt)) best = s_val[w], bt = s_idx[w];
+    tile = index_or(bt, nt, 0);
+  }
+
+  // recompute the chosen tile in fp64: the rank is split over the wavefronts
+  const int v = tile * kTile + lane;
+  const int kq = (r + 3) / 4, k0 = min(wave * kq, r), k1 = min(k0 + kq, r);
+  s_part[wave][lane] = v < V ? dot_part<TF>(h, Wt + (size_t)v * r, k0, k1) : 0.0;
+  __syncthreads();
+  if (wave == 0) {
+    double lv = -INFINITY, sv = -INFINITY;
     int vi = 0x7fffffff;
-    if (v < V) d = recompute(v), vi = v;
-    wave_argmax(d, vi);
-    x = index_or(vi, min(V, (bt + 1) * kTile), bt * kTile);
-    logq = 0.0;
-    lse = d;
+    if (v < V) {
+      const double d = (double)load_logit(brow + v) + ((s_part[0][lane] + s_part[1][lane]) +
+                                                       (s_part[2][lane] + s_part[3][lane]));
+      if (Tf > 0.0f) {
+        sv = d / (double)Tf;
+        lv = sv + gumbel(a.seed, kDraftLeaf, b, rpos, lane);
+      } else {
+        sv = d;
+        lv = d;
+      }
+      vi = v;
+    }
+    wave_argmax(lv, vi);
+    const int x = index_or(vi, min(V, (tile + 1) * kTile), tile * kTile);
+    const double sx = __shfl(sv, x - tile * kTile);
+    if (lane == 0) {
+      a.draft[(size_t)b * gamma + pos] = x;
+      a.logq[(size_t)b * gamma + pos] = Tf > 0.0f ? (float)(sx - lse) : 0.0f;
+      a.lse[(size_t)b * gamma + pos] = Tf > 0.0f ? lse : sx;
+    }
   }
-  if (lane == 0) {
-    a.draft[(size_t)b * gamma + pos] = x;
-    a.logq[(size_t)b * gamma + pos] = (float)logq;
-    a.lse[(size_t)b * gamma + pos] = lse;
+}
+
+template <typename TL, bool RESIDUAL, int R>
+hipError_t launch_pipelined(const GemmArgs& a, hipStream_t s) {
+  static int max_wg = 0;
+  const size_t lds = (size_t)2 * (2 * (R / 16) * 1024);
+  const void* fn = reinterpret_cast<const void*>(&gemm_stats_lds<TL, RESIDUAL, R>);
+  if (!max_wg) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return hipErrorUnknown;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64 * kLdsWaves, lds) != hipSuccess || per_cu < 1)
+      per_cu = 1;
+    max_wg = cus * per_cu;
   }
+  const int groups = (a.B + kSlotsPerGroup - 1) / kSlotsPerGroup;
+  const int threads = 64 * min(kLdsWaves, (a.B + 31) / 32);
+  const int wg_x = max(1, min(a.n_tiles, max_wg / groups));
+  gemm_stats_lds<TL, RESIDUAL, R><<<dim3(wg_x, groups), threads, lds, s>>>(a);
+  return hipGetLastError();
 }
 
 template <typename TL, bool RESIDUAL>
 hipError_t gemm_dispatch(const GemmArgs& a, int factor_dtype, bool vec, hipStream_t s) {
+  if (factor_dtype == DSPARK_BF16 && vec && (a.r == 64 || a.r == 128 || a.r == 256)) {
+    if (a.r == 256) return launch_pipelined<TL, RESIDUAL, 256>(a, s);
+    if (a.r == 128) return launch_pipelined<TL, RESIDUAL, 128>(a, s);
+    return launch_pipelined<TL, RESIDUAL, 64>(a, s);
+  }
   if (factor_dtype == DSPARK_BF16 && a.r % 16 == 0) {
     const dim3 grid(a.n_tiles, (a.B + 255) / 256);
     if (vec) gemm_stats_mfma<TL, RESIDUAL, true><<<grid, 256, 0, s>>>(a);
@@ -378,11 +679,11 @@ hipError_t launch_draft_select(const DraftSelectArgs& a, int logits_dtype, int f
                                hipStream_t s) {
   const dim3 grid(a.B);
   if (logits_dtype == DSPARK_BF16) {
-    if (factor_dtype == DSPARK_BF16) draft_select_kernel<uint16_t, uint16_t><<<grid, 64, 0, s>>>(a);
-    else draft_select_kernel<uint16_t, float><<<grid, 64, 0, s>>>(a);
+    if (factor_dtype == DSPARK_BF16) draft_select_kernel<uint16_t, uint16_t><<<grid, 256, 0, s>>>(a);
+    else draft_select_kernel<uint16_t, float><<<grid, 256, 0, s>>>(a);
   } else {
-    if (factor_dtype == DSPARK_BF16) draft_select_kernel<float, uint16_t><<<grid, 64, 0, s>>>(a);
-    else draft_select_kernel<float, float><<<grid, 64, 0, s>>>(a);
+    if (factor_dtype == DSPARK_BF16) draft_select_kernel<float, uint16_t><<<grid, 256, 0, s>>>(a);
+    else draft_select_kernel<float, float><<<grid, 256, 0, s>>>(a);
   }
   return hipGetLastError();
 }

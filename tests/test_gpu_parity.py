@@ -49,6 +49,10 @@ def test_tiny_round():
     dict(B=8, gamma=6, V=65, r=20, dtype=torch.float32, fdt=torch.bfloat16, temps=(0.9,)),
     dict(B=1, gamma=16, V=2048, r=64, dtype=torch.bfloat16, fdt=torch.bfloat16, temps=(1.0,)),
     dict(B=300, gamma=2, V=700, r=16, dtype=torch.float32, fdt=torch.bfloat16, temps=(1.0, 0.0, 2.0)),
+    dict(B=300, gamma=3, V=5000, r=64, dtype=torch.bfloat16, fdt=torch.bfloat16, temps=(1.0, 0.0, 0.7)),
+    dict(B=40, gamma=4, V=12345, r=128, dtype=torch.float32, fdt=torch.bfloat16, temps=(1.0, 1.2)),
+    dict(B=70, gamma=3, V=9000, r=256, dtype=torch.bfloat16, fdt=torch.bfloat16, temps=(1.0, 0.0)),
+    dict(B=520, gamma=2, V=3001, r=256, dtype=torch.float32, fdt=torch.bfloat16, temps=(0.9,)),
 ])
 def test_small_rounds(case):
     rnd = wl.small_random(case["B"], case["gamma"], case["V"], case["r"], device=DEV, seed=case["B"] + case["V"],
