@@ -232,51 +232,53 @@ template <> struct TileBuf<float> {
   __device__ __forceinline__ float get(int vb, int e) const { return f[vb][e]; }
 };
 
-// Loads of one tile: `full` (uniform) selects unmasked vector loads.
+// Loads of one tile, branch-free: every lane issues its 8 vector loads, with
+// column addresses clamped into the row (V is a multiple of 4 on this path);
+// columns at or beyond V are masked by the epilogue of the (single) ragged tile.
 template <typename TL>
-__device__ __forceinline__ void load_tile(const TL* row, int v0, int half, int V, bool full, TileBuf<TL>& x) {
-  if (full) {
+__device__ __forceinline__ void load_tile(const TL* row, int v0, int half, int V, TileBuf<TL>& x) {
 #pragma unroll
-    for (int vb = 0; vb < 2; ++vb)
+  for (int vb = 0; vb < 2; ++vb)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const TL* p = row + v0 + vb * 32 + g * 8 + half * 4;
-        if constexpr (sizeof(TL) == 2) {
-          const uint2 u = *reinterpret_cast<const uint2*>(p);
-          x.w[vb][2 * g] = u.x, x.w[vb][2 * g + 1] = u.y;
-        } else {
-          const float4 f = *reinterpret_cast<const float4*>(p);
-          x.f[vb][4 * g] = f.x, x.f[vb][4 * g + 1] = f.y, x.f[vb][4 * g + 2] = f.z, x.f[vb][4 * g + 3] = f.w;
-        }
+    for (int g = 0; g < 4; ++g) {
+      const int v = min(v0 + vb * 32 + g * 8 + half * 4, V - 4);
+      const TL* p = row + v;
+      if constexpr (sizeof(TL) == 2) {
+        const uint2 u = *reinterpret_cast<const uint2*>(p);
+        x.w[vb][2 * g] = u.x, x.w[vb][2 * g + 1] = u.y;
+      } else {
+        const float4 f = *reinterpret_cast<const float4*>(p);
+        x.f[vb][4 * g] = f.x, x.f[vb][4 * g + 1] = f.y, x.f[vb][4 * g + 2] = f.z, x.f[vb][4 * g + 3] = f.w;
       }
-  } else {
-#pragma unroll
-    for (int vb = 0; vb < 2; ++vb)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int v = v0 + vb * 32 + g * 8 + half * 4;
-        if constexpr (sizeof(TL) == 2) {
-          uint32_t h[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) h[e] = (v + e < V) ? (uint32_t)row[v + e] : 0xff80u;
-          x.w[vb][2 * g] = h[0] | (h[1] << 16), x.w[vb][2 * g + 1] = h[2] | (h[3] << 16);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) x.f[vb][4 * g + e] = (v + e < V) ? row[v + e] : -INFINITY;
-        }
-      }
-  }
+    }
+}
+
+// Column of accumulator element e of column block vb (see the MFMA layout).
+__device__ __forceinline__ int acc_col(int v0, int vb, int e, int half) {
+  return v0 + vb * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
 }
 
 template <typename TL, bool RESIDUAL>
 __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const f32x16 (&acc)[2], const TileBuf<TL>& x,
                                               const TL* trow, int rq, int pos, bool valid, float T, int tile,
                                               int half, bool full) {
+  float xv[2][16];
+#pragma unroll
+  for (int vb = 0; vb < 2; ++vb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) xv[vb][e] = x.get(vb, e);
+  if (!full) {  // the ragged last tile: columns >= V do not exist
+#pragma unroll
+    for (int vb = 0; vb < 2; ++vb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (acc_col(tile * kTile, vb, e, half) >= a.V) xv[vb][e] = -INFINITY;
+  }
   float ref = -INFINITY;
 #pragma unroll
   for (int vb = 0; vb < 2; ++vb)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) ref = fmaxf(ref, x.get(vb, e));
+    for (int e = 0; e < 16; ++e) ref = fmaxf(ref, xv[vb][e]);
   ref = fmaxf(ref, __shfl_xor(ref, 32));
   float t[2][16];
   float tmax = -INFINITY;
@@ -284,7 +286,7 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const f32x16 (&
   for (int vb = 0; vb < 2; ++vb)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      t[vb][e] = (x.get(vb, e) - ref) + acc[vb][e];
+      t[vb][e] = (xv[vb][e] - ref) + acc[vb][e];
       tmax = fmaxf(tmax, t[vb][e]);
     }
   tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
@@ -304,7 +306,7 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const f32x16 (&
     }
   } else {
     TileBuf<TL> z;
-    load_tile<TL>(trow, tile * kTile, half, a.V, full, z);
+    load_tile<TL>(trow, tile * kTile, half, a.V, z);
     float rs = 0.0f;
     if (valid) {
       const ReqState st = a.req[rq];
@@ -316,7 +318,8 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const f32x16 (&
       for (int vb = 0; vb < 2; ++vb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(z.get(vb, e), c, -kp));
+          const float zv = (full || acc_col(tile * kTile, vb, e, half) < a.V) ? z.get(vb, e) : -INFINITY;
+          const float p = __builtin_amdgcn_exp2f(fmaf(zv, c, -kp));
           const float q = __builtin_amdgcn_exp2f(fmaf(t[vb][e], c, -kq));
           rs += fmaxf(p - q, 0.0f);
         }
@@ -326,11 +329,29 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const f32x16 (&
   }
 }
 
+// s_waitcnt on the vector-memory counter only: at most n loads of this wave
+// may still be in flight (they complete in issue order).
+__device__ __forceinline__ void wait_vmcnt(int n) {
+#define DSPARK_VMCNT(k) __builtin_amdgcn_s_waitcnt(((k) & 15) | (7 << 4) | (15 << 8) | (((k) >> 4) << 14))
+  switch (n) {
+    case 0: DSPARK_VMCNT(0); break;   case 1: DSPARK_VMCNT(1); break;   case 2: DSPARK_VMCNT(2); break;
+    case 3: DSPARK_VMCNT(3); break;   case 4: DSPARK_VMCNT(4); break;   case 5: DSPARK_VMCNT(5); break;
+    case 6: DSPARK_VMCNT(6); break;   case 7: DSPARK_VMCNT(7); break;   case 8: DSPARK_VMCNT(8); break;
+    case 9: DSPARK_VMCNT(9); break;   case 10: DSPARK_VMCNT(10); break; case 11: DSPARK_VMCNT(11); break;
+    case 12: DSPARK_VMCNT(12); break; case 13: DSPARK_VMCNT(13); break; case 14: DSPARK_VMCNT(14); break;
+    case 15: DSPARK_VMCNT(15); break; case 16: DSPARK_VMCNT(16); break; case 20: DSPARK_VMCNT(20); break;
+    case 24: DSPARK_VMCNT(24); break; case 32: DSPARK_VMCNT(32); break; case 36: DSPARK_VMCNT(36); break;
+    case 40: DSPARK_VMCNT(40); break; case 48: DSPARK_VMCNT(48); break;
+    default: DSPARK_VMCNT(0); break;
+  }
+#undef DSPARK_VMCNT
+}
+
+constexpr int kRing = 4;  // W2 tiles in flight: the fill of tile i+3 overlaps tiles i and i+1
+
 template <typename TL, bool RESIDUAL, int R>
 __global__ __launch_bounds__(512, 1) void gemm_stats_lds(GemmArgs a) {
   constexpr int KS = R / 16, NBLK = 2 * KS, TILE_BYTES = NBLK * 1024;
-  constexpr bool PF = true;  // backbone logits prefetched a tile ahead (the residual pass
-                             // loads its target logits at the start of the epilogue)
   extern __shared__ __attribute__((aligned(1024))) char lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nwaves = blockDim.x >> 6;
   const int half = lane >> 5, l32 = lane & 31;
@@ -358,8 +379,10 @@ __global__ __launch_bounds__(512, 1) void gemm_stats_lds(GemmArgs a) {
       H[ks] = valid ? *reinterpret_cast<const bf16x8*>(h + ks * 16) : zero;
     }
   }
+  // number of W2 operand blocks this wave loads per tile
+  const int my_fills = (NBLK - wave + nwaves - 1) / nwaves;
 
-  auto fill = [&](int tile, int buf) {  // this wave's share of the tile's operand blocks
+  auto fill = [&](int tile, int buf) {
     for (int j = wave; j < NBLK; j += nwaves) {
       const int vb = j / KS, ks = j - vb * KS;
       int v = tile * kTile + vb * 32 + l32;
@@ -374,56 +397,74 @@ __global__ __launch_bounds__(512, 1) void gemm_stats_lds(GemmArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][e] = 0.0f;
     const char* base = lds + buf * TILE_BYTES + lane * 16;
+    // all operand reads of the tile are issued ahead in groups of four k-steps
+    constexpr int GK = KS < 4 ? KS : 4;
+    bf16x8 A[2][2][GK];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      bf16x8 A[2];
+    for (int q = 0; q < GK; ++q)
 #pragma unroll
-      for (int vb = 0; vb < 2; ++vb) A[vb] = *reinterpret_cast<const bf16x8*>(base + (vb * KS + ks) * 1024);
+      for (int vb = 0; vb < 2; ++vb) A[0][vb][q] = *reinterpret_cast<const bf16x8*>(base + (vb * KS + q) * 1024);
 #pragma unroll
-      for (int vb = 0; vb < 2; ++vb) acc[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[vb], H[ks], acc[vb], 0, 0, 0);
+    for (int g = 0; g < KS / GK; ++g) {
+      const int cur = g & 1;
+      if (g + 1 < KS / GK) {
+#pragma unroll
+        for (int q = 0; q < GK; ++q)
+#pragma unroll
+          for (int vb = 0; vb < 2; ++vb)
+            A[cur ^ 1][vb][q] = *reinterpret_cast<const bf16x8*>(base + (vb * KS + (g + 1) * GK + q) * 1024);
+      }
+#pragma unroll
+      for (int q = 0; q < GK; ++q)
+#pragma unroll
+        for (int vb = 0; vb < 2; ++vb)
+          acc[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[cur][vb][q], H[g * GK + q], acc[vb], 0, 0, 0);
     }
   };
   auto full_tile = [&](int tile) { return (tile + 1) * kTile <= V; };
-  // Wait until at most `newer` vector-memory loads issued after the W2 fill are
-  // still in flight (loads complete in order), then synchronise the workgroup.
-  auto sync_fill = [&](bool wait_all) {
-    if (wait_all) __builtin_amdgcn_s_waitcnt(0xF70);        // vmcnt(0)
-    else __builtin_amdgcn_s_waitcnt(0xF70 | 8);             // vmcnt(8): the 8 logit loads may stay in flight
-    __syncthreads();
-  };
+  constexpr int kXLoads = 8;  // vector loads issued by load_tile()
 
   f32x16 acc0[2], acc1[2];
   TileBuf<TL> x0, x1;
   int t = blockIdx.x;
+  // prologue: tiles t0..t2 requested, t0 computed
   fill(t, 0);
-  if (PF && active) load_tile<TL>(brow, t * kTile, half, V, full_tile(t), x0);
-  sync_fill(true);
   if (t + G < nt) fill(t + G, 1);
+  if (t + 2 * G < nt) fill(t + 2 * G, 2);
+  if (active) load_tile<TL>(brow, t * kTile, half, V, x0);
+  wait_vmcnt(0);
+  __syncthreads();
   if (active) mma(0, acc0);
-  sync_fill(true);
 
+  // steady state, two tiles per trip so that accumulators and logit registers
+  // are static; the W2 ring slot of tile t_i is i % kRing
+  int i = 0;
   for (;;) {
-    // tile t: acc0, x0, W2 buffer 0; tile t+G ready in buffer 1
-    if (t + 2 * G < nt) fill(t + 2 * G, 0);
-    const bool more = t + G < nt;
-    if (more && active) {
-      if (PF) load_tile<TL>(brow, (t + G) * kTile, half, V, full_tile(t + G), x1);
-      mma(1, acc1);
+    // tile t = t_i: acc0, x0; t_{i+1} ready in ring slot (i+1) % kRing
+    int pending = 0;  // loads this wave issues in this iteration
+    if (t + 3 * G < nt) fill(t + 3 * G, (i + 3) % kRing), pending += my_fills;
+    if (t + G < nt && active) {
+      load_tile<TL>(brow, (t + G) * kTile, half, V, x1);
+      pending += kXLoads;
+      mma((i + 1) % kRing, acc1);
     }
     if (active) epilogue_tile<TL, RESIDUAL>(a, acc0, x0, trow, rq, pos, valid, T, t, half, full_tile(t));
-    sync_fill(!(PF && more && active && full_tile(t + G)));
-    t += G;
+    wait_vmcnt(pending);  // the fill of t_{i+2} (issued one iteration ago) has landed
+    __syncthreads();
+    t += G, ++i;
     if (t >= nt) break;
-    // tile t: acc1, x1, buffer 1; tile t+G ready in buffer 0
-    if (t + 2 * G < nt) fill(t + 2 * G, 1);
-    const bool more2 = t + G < nt;
-    if (more2 && active) {
-      if (PF) load_tile<TL>(brow, (t + G) * kTile, half, V, full_tile(t + G), x0);
-      mma(0, acc0);
+    // tile t = t_i: acc1, x1; t_{i+1} ready in ring slot (i+1) % kRing
+    pending = 0;
+    if (t + 3 * G < nt) fill(t + 3 * G, (i + 3) % kRing), pending += my_fills;
+    if (t + G < nt && active) {
+      load_tile<TL>(brow, (t + G) * kTile, half, V, x0);
+      pending += kXLoads;
+      mma((i + 1) % kRing, acc0);
     }
     if (active) epilogue_tile<TL, RESIDUAL>(a, acc1, x1, trow, rq, pos, valid, T, t, half, full_tile(t));
-    sync_fill(!(PF && more2 && active && full_tile(t + G)));
-    t += G;
+    wait_vmcnt(pending);
+    __syncthreads();
+    t += G, ++i;
     if (t >= nt) break;
   }
 }
@@ -531,26 +572,44 @@ __global__ __launch_bounds__(256) void draft_select_kernel(DraftSelectArgs a) {
     const double mref = (double)ts[0].ref + (double)ts[0].mx;
     double best = -INFINITY, row_m = -INFINITY, row_s = 0.0;
     int best_blk = 0x7fffffff;
-    for (int blk = wave; blk < nblk; blk += 4) {
-      const int t = blk * kTilesPerBlock + lane;
-      double d = -INFINITY;
-      float sum = 0.0f;
-      if (t < nt) {
-        const TileStat st = ts[t];
-        d = (double)st.ref + (double)st.mx;
-        sum = st.sum;
+    // blocks of this wavefront in chunks of 16: all tile records of a chunk are
+    // requested first, then reduced block by block; lane j keeps block j's
+    // (max, mass), and the 16 Gumbels and logarithms are computed in parallel
+    for (int c0 = wave; c0 < nblk; c0 += 64) {
+      TileStat rec[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int t = (c0 + 4 * j) * kTilesPerBlock + lane;
+        if (c0 + 4 * j < nblk && t < nt) rec[j] = ts[t];
+        else rec[j].ref = -INFINITY, rec[j].mx = 0.0f, rec[j].sum = 0.0f;
       }
-      const double dmax = wave_max(d);
-      const float e = t < nt ? sum * expf((float)((d - dmax) * invT)) : 0.0f;
-      const double sblk = (double)wave_sum(e);
-      const double val = (dmax - mref) * invT + log(sblk) + gumbel(a.seed, kDraftTop, b, rpos, blk);
-      if (val > best) best = val, best_blk = blk;
-      if (dmax > row_m) {
-        row_s = row_s * exp((row_m - dmax) * invT) + sblk;
-        row_m = dmax;
-      } else {
-        row_s += sblk * exp((dmax - row_m) * invT);
+      double my_d = -INFINITY, my_s = 0.0;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        if (c0 + 4 * j >= nblk) break;  // uniform
+        const double d = (double)rec[j].ref + (double)rec[j].mx;
+        const double dmax = wave_max(d);
+        const float e = rec[j].sum > 0.0f ? rec[j].sum * expf((float)((d - dmax) * invT)) : 0.0f;
+        const float sblk = wave_sum(e);
+        if (lane == j) my_d = dmax, my_s = (double)sblk;
       }
+      const int blk = c0 + 4 * lane;
+      if (lane < 16 && blk < nblk) {
+        const double val = (my_d - mref) * invT + log(my_s) + gumbel(a.seed, kDraftTop, b, rpos, blk);
+        if (val > best) best = val, best_blk = blk;
+        if (my_d > row_m) {
+          row_s = row_s * exp((row_m - my_d) * invT) + my_s;
+          row_m = my_d;
+        } else {
+          row_s += my_s * exp((my_d - row_m) * invT);
+        }
+      }
+    }
+    wave_argmax(best, best_blk);
+    {
+      const double m = wave_max(row_m);
+      row_s = wave_sum(row_s > 0.0 ? row_s * exp((row_m - m) * invT) : 0.0);
+      row_m = m;
     }
     if (lane == 0) s_val[wave] = best, s_idx[wave] = best_blk, s_m[wave] = row_m, s_s[wave] = row_s;
     __syncthreads();
@@ -623,15 +682,216 @@ __global__ __launch_bounds__(256) void draft_select_kernel(DraftSelectArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Coalesced variant for bf16 logits (V a multiple of 8), the one the headline
+// round runs.  Both streams of a tile go through LDS by direct loads whose every
+// instruction reads whole rows:
+//   * W2 tile: 64 rows x R bf16.  Instruction f reads 64/NC full rows (NC = R/8
+//     16-byte chunks per row); lane l takes chunk (l % NC) ^ (row % NC) of its
+//     row, so LDS holds the rows with their chunks xor-swizzled by the row and
+//     the MFMA operand reads (32 rows, one chunk each) spread over all banks.
+//   * backbone logits: 256 slots x 64 columns x 2 B; instruction f reads 8 full
+//     128-byte slot rows, chunk (l % 8) ^ (slot % 8) per lane, swizzled alike
+//     for the epilogue's 8-byte reads.
+// Two-slot rings for both (128 KB of LDS at R = 256).
+// ---------------------------------------------------------------------------
+template <bool RESIDUAL, int R>
+__global__ __launch_bounds__(512, 1) void gemm_stats_coalesced(GemmArgs a) {
+  constexpr int NC = R / 8;                       // 16-byte chunks per W2 row
+  constexpr int W_BYTES = kTile * R * 2;          // 32 KB at R = 256
+  constexpr int X_BYTES = kSlotsPerGroup * kTile * 2;  // 32 KB
+  constexpr int W_INSTR = W_BYTES / 1024, X_INSTR = X_BYTES / 1024;
+  extern __shared__ __attribute__((aligned(1024))) char lds[];
+  char* const wring = lds;                        // 2 x W_BYTES
+  char* const xring = lds + 2 * W_BYTES;          // 2 x X_BYTES
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nwaves = blockDim.x >> 6;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int nslots = RESIDUAL ? (int)*a.slot_count : a.B;
+  const int sg0 = blockIdx.y * kSlotsPerGroup;
+  const int nt = a.n_tiles, G = gridDim.x;
+  if (sg0 >= nslots || (int)blockIdx.x >= nt) return;  // uniform across the workgroup
+  const int V = a.V;
+  const uint16_t* Wt = static_cast<const uint16_t*>(a.Wt);
+
+  // this wave's 32 slots (MFMA B operand columns)
+  const bool active = sg0 + wave * 32 < nslots;
+  int rq, pos, prev;
+  bool valid;
+  slot_info<RESIDUAL>(a, sg0 + wave * 32 + l32, nslots, rq, pos, prev, valid);
+  const uint16_t* trow = RESIDUAL
+      ? static_cast<const uint16_t*>(a.target) + ((size_t)rq * (a.gamma + 1) + pos) * V : nullptr;
+  const float T = valid ? effective_temp(a.temperature[rq]) : 1.0f;
+  bf16x8 H[R / 16];
+  {
+    const uint16_t* h = static_cast<const uint16_t*>(a.U) + (size_t)prev * R + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < R / 16; ++ks) {
+      const bf16x8 zero = {};
+      H[ks] = valid ? *reinterpret_cast<const bf16x8*>(h + ks * 16) : zero;
+    }
+  }
+  // rows of the backbone logits this lane loads for the logit stream: slot
+  // f*8 + lane/8 of each of this wave's instructions f = wave, wave+nwaves, ...
+  constexpr int XMAX = X_INSTR;  // at most one instruction per wave per 8 slots
+  const uint16_t* xsrc[4];
+  int nx = 0;
+  for (int f = wave; f < X_INSTR && nx < 4; f += nwaves, ++nx) {
+    const int s = f * 8 + (lane >> 3);
+    int b2, p2, pr2;
+    bool v2;
+    slot_info<RESIDUAL>(a, sg0 + s, nslots, b2, p2, pr2, v2);
+    xsrc[nx] = static_cast<const uint16_t*>(a.base) + ((size_t)b2 * a.gamma + p2) * V;
+  }
+  (void)XMAX;
+
+  auto fill_w = [&](int tile, int buf) {
+    for (int f = wave; f < W_INSTR; f += nwaves) {
+      const int r = f * (64 / NC) + lane / NC, p = lane % NC;
+      int v = tile * kTile + r;
+      v = v < V ? v : V - 1;  // rows beyond V only feed masked columns
+      const int c = p ^ (r % NC);
+      __builtin_amdgcn_global_load_lds(Wt + (size_t)v * R + c * 8,
+                                       (lds_ptr_t)(wring + buf * W_BYTES + f * 1024), 16, 0, 0);
+    }
+  };
+  auto fill_x = [&](int tile, int buf) {
+    int k = 0;
+    for (int f = wave; f < X_INSTR && k < 4; f += nwaves, ++k) {
+      const int s = f * 8 + (lane >> 3), p = lane & 7;
+      const int c = p ^ (s & 7);
+      const int col = min(tile * kTile + c * 8, V - 8);  // the ragged tile is masked later
+      __builtin_amdgcn_global_load_lds(xsrc[k] + col, (lds_ptr_t)(xring + buf * X_BYTES + f * 1024), 16, 0, 0);
+    }
+  };
+  auto mma = [&](int buf, f32x16 (&acc)[2]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][e] = 0.0f;
+    const char* base = wring + buf * W_BYTES;
+    bf16x8 A[2][2][4];
+    auto rd = [&](int ks, int vb) {
+      const int v = vb * 32 + l32, c = 2 * ks + half;
+      return *reinterpret_cast<const bf16x8*>(base + v * (R * 2) + ((c ^ (v % NC)) << 4));
+    };
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int vb = 0; vb < 2; ++vb) A[0][vb][q] = rd(q, vb);
+#pragma unroll
+    for (int g = 0; g < R / 64; ++g) {
+      const int cur = g & 1;
+      if (g + 1 < R / 64) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int vb = 0; vb < 2; ++vb) A[cur ^ 1][vb][q] = rd((g + 1) * 4 + q, vb);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int vb = 0; vb < 2; ++vb)
+          acc[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[cur][vb][q], H[g * 4 + q], acc[vb], 0, 0, 0);
+    }
+  };
+  auto read_x = [&](int buf, TileBuf<uint16_t>& x) {
+    const int s = wave * 32 + l32;
+    const char* rowp = xring + buf * X_BYTES + s * 128 + half * 8;
+#pragma unroll
+    for (int vb = 0; vb < 2; ++vb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = vb * 4 + g;
+        const uint2 u = *reinterpret_cast<const uint2*>(rowp + ((c ^ (s & 7)) << 4));
+        x.w[vb][2 * g] = u.x, x.w[vb][2 * g + 1] = u.y;
+      }
+  };
+  auto full_tile = [&](int tile) { return (tile + 1) * kTile <= V; };
+
+  f32x16 acc0[2], acc1[2];
+  int t = blockIdx.x;
+  // Ring discipline: at the start of iteration i (tile t_i) the W2 slot i%2
+  // (last read by the MFMAs of t_i in iteration i-1) receives W2 of t_{i+2}, and
+  // the logit slot (i+1)%2 (last read by the epilogue of t_{i-1}) receives the
+  // logits of t_{i+1}; both loads have the whole iteration to land.
+  fill_w(t, 0);
+  if (t + G < nt) fill_w(t + G, 1);
+  fill_x(t, 0);
+  wait_vmcnt(0);
+  __syncthreads();
+  if (active) mma(0, acc0);
+  __syncthreads();
+
+  int i = 0;
+  for (;;) {
+    // tile t = t_i with accumulators acc0
+    {
+      const int c0 = i & 1, c1 = c0 ^ 1;
+      if (t + 2 * G < nt) fill_w(t + 2 * G, c0);
+      if (t + G < nt) fill_x(t + G, c1);
+      if (t + G < nt && active) mma(c1, acc1);
+      if (active) {
+        TileBuf<uint16_t> x;
+        read_x(c0, x);
+        epilogue_tile<uint16_t, RESIDUAL>(a, acc0, x, trow, rq, pos, valid, T, t, half, full_tile(t));
+      }
+      wait_vmcnt(0);
+      __syncthreads();
+      t += G, ++i;
+      if (t >= nt) break;
+    }
+    // tile t = t_i with accumulators acc1
+    {
+      const int c0 = i & 1, c1 = c0 ^ 1;
+      if (t + 2 * G < nt) fill_w(t + 2 * G, c0);
+      if (t + G < nt) fill_x(t + G, c1);
+      if (t + G < nt && active) mma(c1, acc0);
+      if (active) {
+        TileBuf<uint16_t> x;
+        read_x(c0, x);
+        epilogue_tile<uint16_t, RESIDUAL>(a, acc1, x, trow, rq, pos, valid, T, t, half, full_tile(t));
+      }
+      wait_vmcnt(0);
+      __syncthreads();
+      t += G, ++i;
+      if (t >= nt) break;
+    }
+  }
+}
+
+template <bool RESIDUAL, int R>
+hipError_t launch_coalesced(const GemmArgs& a, hipStream_t s) {
+  static int max_wg = 0;
+  const size_t lds = (size_t)2 * (kTile * R * 2) + (size_t)2 * (kSlotsPerGroup * kTile * 2);
+  const void* fn = reinterpret_cast<const void*>(&gemm_stats_coalesced<RESIDUAL, R>);
+  if (!max_wg) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return hipErrorUnknown;
+    if (lds > 64 * 1024 && hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+      return hipErrorUnknown;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64 * kLdsWaves, lds) != hipSuccess || per_cu < 1)
+      per_cu = 1;
+    max_wg = cus * per_cu;
+  }
+  const int groups = (a.B + kSlotsPerGroup - 1) / kSlotsPerGroup;
+  const int wg_x = max(1, min(a.n_tiles, max_wg / groups));
+  gemm_stats_coalesced<RESIDUAL, R><<<dim3(wg_x, groups), 64 * kLdsWaves, lds, s>>>(a);
+  return hipGetLastError();
+}
+
 template <typename TL, bool RESIDUAL, int R>
 hipError_t launch_pipelined(const GemmArgs& a, hipStream_t s) {
   static int max_wg = 0;
-  const size_t lds = (size_t)2 * (2 * (R / 16) * 1024);
+  const size_t lds = (size_t)kRing * (2 * (R / 16) * 1024);
   const void* fn = reinterpret_cast<const void*>(&gemm_stats_lds<TL, RESIDUAL, R>);
   if (!max_wg) {
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return hipErrorUnknown;
+    if (lds > 64 * 1024 && hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
       return hipErrorUnknown;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64 * kLdsWaves, lds) != hipSuccess || per_cu < 1)
       per_cu = 1;
@@ -646,6 +906,12 @@ hipError_t launch_pipelined(const GemmArgs& a, hipStream_t s) {
 
 template <typename TL, bool RESIDUAL>
 hipError_t gemm_dispatch(const GemmArgs& a, int factor_dtype, bool vec, hipStream_t s) {
+  if constexpr (sizeof(TL) == 2) {
+    if (factor_dtype == DSPARK_BF16 && a.V % 8 == 0 && a.V >= 64 && (a.r == 128 || a.r == 256)) {
+      if (a.r == 256) return launch_coalesced<RESIDUAL, 256>(a, s);
+      return launch_coalesced<RESIDUAL, 128>(a, s);
+    }
+  }
   if (factor_dtype == DSPARK_BF16 && vec && (a.r == 64 || a.r == 128 || a.r == 256)) {
     if (a.r == 256) return launch_pipelined<TL, RESIDUAL, 256>(a, s);
     if (a.r == 128) return launch_pipelined<TL, RESIDUAL, 128>(a, s);

@@ -23,46 +23,65 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kMaxKeys = 8192;
+constexpr int kMaxPoints = 1024;
 
 #pragma clang fp contract(off)
 
-// 1/SPS at a verify batch of N tokens (see the ABI header for the rule).
-__device__ double step_time(double N, const double* Bs, const double* sv, int np) {
-  if (N <= Bs[0]) return 1.0 / sv[0];
-  int i = 0;
-  while (i + 1 < np - 1 && Bs[i + 1] <= N) ++i;
-  const double t0 = 1.0 / sv[i], t1 = 1.0 / sv[i + 1];
-  const double frac = (N - Bs[i]) / (Bs[i + 1] - Bs[i]);
-  const double dt = t1 - t0;
+// 1/SPS at a verify batch of N tokens (see the ABI header for the rule), from
+// the table held in LDS: batch sizes Bs and step times ts = 1/SPS.  The
+// segment is the last i <= np-2 with Bs[i] <= N (binary search).
+__device__ double step_time(double N, const double* Bs, const double* ts, int np) {
+  if (N <= Bs[0]) return ts[0];
+  int lo = 0, hi = np - 2;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (Bs[mid] <= N) lo = mid;
+    else hi = mid - 1;
+  }
+  const double frac = (N - Bs[lo]) / (Bs[lo + 1] - Bs[lo]);
+  const double dt = ts[lo + 1] - ts[lo];
   const double inc = dt * frac;
-  return t0 + inc;
+  return ts[lo] + inc;
 }
 
 __global__ __launch_bounds__(kThreads) void schedule_kernel(ScheduleArgs a) {
   __shared__ unsigned long long keys[kMaxKeys];
   __shared__ unsigned long long part[kThreads];
+  __shared__ double tB[kMaxPoints], tT[kMaxPoints];
   __shared__ int first_fail;
-  const int tid = threadIdx.x, B = a.B, gamma = a.gamma;
+  const int tid = threadIdx.x, B = a.B, gamma = a.gamma, np = a.n_points;
   const int nk = B * gamma;
   int M = 1;
   while (M < nk) M <<= 1;
 
+  for (int i = tid; i < np; i += kThreads) {
+    tB[i] = a.sps_B[i];
+    tT[i] = 1.0 / a.sps_val[i];
+  }
+  bool bad = false;
   for (int b = tid; b < B; b += kThreads) {
+    float c[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) c[j] = j < gamma ? a.conf[(size_t)b * gamma + j] : 0.5f;
     float acc = 1.0f;
-    for (int j = 0; j < gamma; ++j) {
-      float c = a.conf[(size_t)b * gamma + j];
-      if (!(c > 0.0f && c < 1.0f)) {
-        flag_status(a.status, kBadConf);
-        c = c > 0.0f ? 0x1.fffffep-1f : 0x1p-126f;  // clamp into (0, 1); NaN -> tiny
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (j >= gamma) break;
+      float cj = c[j];
+      if (!(cj > 0.0f && cj < 1.0f)) {
+        bad = true;
+        cj = cj > 0.0f ? 0x1.fffffep-1f : 0x1p-126f;  // clamp into (0, 1); NaN -> tiny
       }
-      acc = acc * c;
+      acc = acc * cj;
       const unsigned long long q = (unsigned long long)floor((double)acc * 4294967296.0);
       keys[b * gamma + j] = ((0xFFFFFFFFull - q) << 32) | ((unsigned long long)b << 4) | (unsigned)j;
     }
   }
+  if (bad) flag_status(a.status, kBadConf);
   for (int i = nk + tid; i < M; i += kThreads) keys[i] = ~0ull;
   if (tid == 0) first_fail = nk;
   for (int b = tid; b < B; b += kThreads) a.budget[b] = 0;
+  __threadfence();
   __syncthreads();
 
   for (int k = 2; k <= M; k <<= 1) {
@@ -96,8 +115,8 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(ScheduleArgs a) {
   for (int i = lo; i < hi; ++i) {
     const unsigned long long q = 0xFFFFFFFFull - (keys[i] >> 32);
     const double N = (double)(B + i);
-    const double lhs = (double)(tau + q) * step_time(N, a.sps_B, a.sps_val, a.n_points);
-    const double rhs = (double)tau * step_time(N + 1.0, a.sps_B, a.sps_val, a.n_points);
+    const double lhs = (double)(tau + q) * step_time(N, tB, tT, np);
+    const double rhs = (double)tau * step_time(N + 1.0, tB, tT, np);
     if (!(lhs > rhs)) {
       atomicMin(&first_fail, i);
       break;

@@ -115,35 +115,42 @@ __global__ __launch_bounds__(64) void row_stats_kernel(VerifyArgs a) {
   }
 }
 
-// ln-sum-exp of one target row from its block statistics: row maximum M and
-// ln sum_v exp((z_v - M) / T).
-__device__ __forceinline__ void row_lse(const BlockStat* bs, int nb, double invT, int lane, double& M,
-                                        double& logsum) {
-  double m = -INFINITY;
-  for (int i = lane; i < nb; i += 64) m = fmax(m, (double)bs[i].mx);
-  M = wave_max(m);
-  double s = 0.0;
-  for (int i = lane; i < nb; i += 64) s += (double)bs[i].sum * exp(((double)bs[i].mx - M) * invT);
-  logsum = log(wave_sum(s));
-}
+// Statistics of target rows 0..nrows-1 of one request from their block
+// statistics, one wavefront per row: maximum M, ln sum_v exp((z_v - M) / T)
+// and, for greedy requests, the lowest index of the maximum.
+struct RowInfo {
+  double M, logS;
+  int arg;
+};
 
-// Lowest index of the row maximum.
-__device__ __forceinline__ int row_argmax(const BlockStat* bs, int nb, int lane) {
-  double best = -INFINITY;
+__device__ __forceinline__ RowInfo row_info(const BlockStat* bs, int nb, bool greedy, double invT, int lane) {
+  RowInfo ri;
+  double m = -INFINITY;
   int arg = 0x7fffffff;
   for (int i = lane; i < nb; i += 64) {
-    const double m = bs[i].mx;
-    if (m > best || (m == best && bs[i].arg < arg)) best = m, arg = bs[i].arg;
+    const double mi = bs[i].mx;
+    if (mi > m || (greedy && mi == m && bs[i].arg < arg)) m = mi, arg = bs[i].arg;
   }
-  wave_argmax(best, arg);
-  return arg;
+  double mm = m;
+  int aa = arg;
+  wave_argmax(mm, aa);
+  ri.M = mm;
+  ri.arg = aa;
+  ri.logS = 0.0;
+  if (!greedy) {
+    double sum = 0.0;
+    for (int i = lane; i < nb; i += 64) sum += (double)bs[i].sum * exp(((double)bs[i].mx - mm) * invT);
+    ri.logS = log(wave_sum(sum));
+  }
+  return ri;
 }
 
-// Three-level Gumbel-max draw from softmax(row / T): block from the block
-// statistics, tile from the chosen block (reread), column from the chosen tile.
+// Three-level Gumbel-max draw from softmax(row / T) by wavefront 0 of the
+// workgroup: block from the block statistics, tile from a re-read of the chosen
+// block (one 64-column tile per lane), column from the chosen tile.
 template <typename TL>
-__device__ int sample_row(const TL* row, const BlockStat* bs, int nb, int V, double invT,
-                          uint64_t seed, uint32_t req, uint32_t rpos, int lane) {
+__device__ int sample_row(const TL* row, const BlockStat* bs, int nb, int V, double invT, uint64_t seed,
+                          uint32_t req, uint32_t rpos, int lane) {
   const double mref = bs[0].mx;
   double best = -INFINITY;
   int bi = 0x7fffffff;
@@ -161,11 +168,39 @@ __device__ int sample_row(const TL* row, const BlockStat* bs, int nb, int V, dou
   if (lane * kTile < len) {
     const TL* tp = row + start + lane * kTile;
     const int tl = min(kTile, len - lane * kTile);
+    float z[kTile];
+    const bool vec = tl == kTile && (reinterpret_cast<uintptr_t>(tp) & 15) == 0;
+    if (vec) {
+      if constexpr (sizeof(TL) == 2) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint4 w = reinterpret_cast<const uint4*>(tp)[i];
+          const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            z[8 * i + 2 * q] = __uint_as_float(ww[q] << 16);
+            z[8 * i + 2 * q + 1] = __uint_as_float(ww[q] & 0xffff0000u);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float4 w = reinterpret_cast<const float4*>(tp)[i];
+          z[4 * i] = w.x, z[4 * i + 1] = w.y, z[4 * i + 2] = w.z, z[4 * i + 3] = w.w;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < kTile; ++e) z[e] = e < tl ? load_logit(tp + e) : -INFINITY;
+    }
     float mt = -INFINITY;
-    for (int e = 0; e < tl; ++e) mt = fmaxf(mt, load_logit(tp + e));
-    double st = 0.0;
-    for (int e = 0; e < tl; ++e) st += exp(((double)load_logit(tp + e) - (double)mt) * invT);
-    val = ((double)mt - mref) * invT + log(st) + gumbel(seed, kFinalMid, req, rpos, lane);
+#pragma unroll
+    for (int e = 0; e < kTile; ++e) mt = fmaxf(mt, z[e]);
+    const float c = (float)invT;
+    float st = 0.0f;
+#pragma unroll
+    for (int e = 0; e < kTile; ++e) st += expf((z[e] - mt) * c);
+    val = ((double)mt - mref) * invT + log((double)st) + gumbel(seed, kFinalMid, req, rpos, lane);
     ti = lane;
   }
   wave_argmax(val, ti);
@@ -182,9 +217,12 @@ __device__ int sample_row(const TL* row, const BlockStat* bs, int nb, int V, dou
   return index_or(vi, min(start + len, tstart + kTile), tstart);
 }
 
+// One workgroup of 4 wavefronts per request.
 template <typename TL>
-__global__ __launch_bounds__(64) void accept_kernel(VerifyArgs a) {
-  const int b = blockIdx.x, lane = threadIdx.x;
+__global__ __launch_bounds__(256) void accept_kernel(VerifyArgs a) {
+  __shared__ double s_M[17], s_logS[17];
+  __shared__ int s_arg[17], s_n;
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int gamma = a.gamma, V = a.V, nb = a.n_blk;
   const int L = budget_of(a, b);
   const float Tf = checked_temp(a.temperature[b], a.status);
@@ -195,82 +233,111 @@ __global__ __launch_bounds__(64) void accept_kernel(VerifyArgs a) {
   const TL* trow0 = static_cast<const TL*>(a.target) + (size_t)b * (gamma + 1) * V;
   const int32_t* xs = a.draft + (size_t)b * gamma;
 
-  int n = 0;
-  for (int k = 1; k <= L; ++k) {
-    const int j = k - 1;
-    const int x = checked_token(xs[j], V, a.status, kBadDraft);
-    bool ok;
-    if (greedy) {
-      ok = x == row_argmax(bs + (size_t)j * nb, nb, lane);
-    } else {
-      double M, lS;
-      row_lse(bs + (size_t)j * nb, nb, invT, lane, M, lS);
-      const double lp = ((double)load_logit(trow0 + (size_t)j * V + x) - M) * invT - lS;
-      const double lq = (double)a.draft_logq[(size_t)b * gamma + j];
-      const double lnu = log(uniform_from_word(rng_word(a.seed, kAccept, b, k + off, 0)));
-      ok = lnu < lp - lq;  // u < min(1, p/q) since ln u < 0
-      if (a.debug_logp_logq && lane == 0) {
-        a.debug_logp_logq[((size_t)b * gamma + j) * 2] = (float)lp;
-        a.debug_logp_logq[((size_t)b * gamma + j) * 2 + 1] = (float)lq;
+  // statistics of rows 0..L, one wavefront per row
+  for (int j = wave; j <= L; j += 4) {
+    const RowInfo ri = row_info(bs + (size_t)j * nb, nb, greedy, invT, lane);
+    if (lane == 0) s_M[j] = ri.M, s_logS[j] = ri.logS, s_arg[j] = ri.arg;
+  }
+  __syncthreads();
+
+  // every accept test at once (lane k-1 tests position k); n = first failure
+  if (wave == 0) {
+    bool fail = false;
+    if (lane < L) {
+      const int k = lane + 1;
+      const int x = checked_token(xs[lane], V, a.status, kBadDraft);
+      if (greedy) {
+        fail = x != s_arg[lane];
+      } else {
+        const double lp = ((double)load_logit(trow0 + (size_t)lane * V + x) - s_M[lane]) * invT - s_logS[lane];
+        const double lq = (double)a.draft_logq[(size_t)b * gamma + lane];
+        const double lnu = log(uniform_from_word(rng_word(a.seed, kAccept, b, k + off, 0)));
+        fail = !(lnu < lp - lq);  // accept iff u < min(1, p/q), since ln u < 0
+        if (a.debug_logp_logq) {
+          a.debug_logp_logq[((size_t)b * gamma + lane) * 2] = (float)lp;
+          a.debug_logp_logq[((size_t)b * gamma + lane) * 2 + 1] = (float)lq;
+        }
       }
     }
-    if (!ok) break;
-    ++n;
+    const unsigned long long m = __ballot(fail);
+    if (lane == 0) s_n = m ? __ffsll((long long)m) - 1 : L;
   }
+  __syncthreads();
+  const int n = s_n;
 
   int y = -1;
-  const BlockStat* bn = bs + (size_t)n * nb;
   if (greedy) {
-    y = row_argmax(bn, nb, lane);
+    y = s_arg[n];
   } else if (n == L) {
-    y = sample_row(trow0 + (size_t)n * V, bn, nb, V, invT, a.seed, b, n + 1 + off, lane);
-  } else {
-    double M, lS;
-    row_lse(bn, nb, invT, lane, M, lS);
-    if (lane == 0) {
-      ReqState st;
-      st.row_max = M, st.row_logsum = lS, st.res_mass = 0.0, st.n = n, st.pending = 1;
-      a.req[b] = st;
-      a.slot_req[atomicAdd(a.slot_count, 1u)] = b;
+    if (wave == 0) y = sample_row(trow0 + (size_t)n * V, bs + (size_t)n * nb, nb, V, invT, a.seed, b, n + 1 + off, lane);
+  } else if (tid == 0) {
+    ReqState st;
+    st.row_max = s_M[n], st.row_logsum = s_logS[n], st.res_mass = 0.0, st.n = n, st.pending = 1;
+    a.req[b] = st;
+    a.slot_req[atomicAdd(a.slot_count, 1u)] = b;
+  }
+  if (wave == 0) {
+    for (int i = lane; i <= gamma; i += 64) {
+      int t = -1;
+      if (i < n) t = xs[i];
+      else if (i == n) t = y;
+      a.out_tokens[(size_t)b * (gamma + 1) + i] = t;
     }
-  }
-  for (int i = lane; i <= gamma; i += 64) {
-    int t = -1;
-    if (i < n) t = xs[i];
-    else if (i == n) t = y;
-    a.out_tokens[(size_t)b * (gamma + 1) + i] = t;
-  }
-  if (lane == 0) {
-    a.num_accepted[b] = n;
-    a.num_emitted[b] = n + 1;
+    if (lane == 0) {
+      a.num_accepted[b] = n;
+      a.num_emitted[b] = n + 1;
+    }
   }
 }
 
-// fp64 residual r(v) = max(0, p(v) - q(v)) at one column of the rejected row.
-template <typename TL, typename TF>
-__device__ __forceinline__ double residual_at(const VerifyArgs& a, int b, const ReqState& st,
-                                              int prev, double invT, double lse_q, int v,
-                                              double* p_out) {
-  const int V = a.V, r = a.r, n = st.n;
+template <typename TF>
+__device__ __forceinline__ double dot_range(const TF* h, const TF* w, int k0, int k1) {
+  double acc = 0.0;
+  if constexpr (sizeof(TF) == 2) {
+    if ((((k1 - k0) | k0) & 7) == 0) {
+      for (int k = k0; k < k1; k += 8) {
+        const uint4 hv = *reinterpret_cast<const uint4*>(h + k);
+        const uint4 wv = *reinterpret_cast<const uint4*>(w + k);
+        const uint32_t hh[4] = {hv.x, hv.y, hv.z, hv.w}, ww[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc += (double)__uint_as_float(hh[q] << 16) * (double)__uint_as_float(ww[q] << 16);
+          acc += (double)__uint_as_float(hh[q] & 0xffff0000u) * (double)__uint_as_float(ww[q] & 0xffff0000u);
+        }
+      }
+      return acc;
+    }
+  }
+  for (int k = k0; k < k1; ++k) acc += (double)load_logit(h + k) * (double)load_logit(w + k);
+  return acc;
+}
+
+// fp64 residual r(v) = max(0, p(v) - q(v)) at one column of the rejected row,
+// given the Markov bias of that column.
+template <typename TL>
+__device__ __forceinline__ double residual_at(const VerifyArgs& a, int b, const ReqState& st, double invT,
+                                              double lse_q, int v, double bias, double* p_out) {
+  const int V = a.V, n = st.n;
   const TL* trow = static_cast<const TL*>(a.target) + ((size_t)b * (a.gamma + 1) + n) * V;
   const TL* brow = static_cast<const TL*>(a.base) + ((size_t)b * a.gamma + n) * V;
-  const TF* h = static_cast<const TF*>(a.U) + (size_t)prev * r;
-  const TF* w = static_cast<const TF*>(a.Wt) + (size_t)v * r;
-  double acc = 0.0;
-  for (int k = 0; k < r; ++k) acc += (double)load_logit(h + k) * (double)load_logit(w + k);
-  const double d = (double)load_logit(brow + v) + acc;
+  const double d = (double)load_logit(brow + v) + bias;
   const double p = exp(((double)load_logit(trow + v) - st.row_max) * invT - st.row_logsum);
   const double q = exp(d * invT - lse_q);
   if (p_out) *p_out = p;
   return p > q ? p - q : 0.0;
 }
 
+// One workgroup of 4 wavefronts per request that rejected: block and tile from
+// the residual tile masses, column from an fp64 recompute of the chosen tile
+// (rank split over the wavefronts).
 template <typename TL, typename TF>
-__global__ __launch_bounds__(64) void residual_select_kernel(VerifyArgs a) {
-  const int b = blockIdx.x, lane = threadIdx.x;
+__global__ __launch_bounds__(256) void residual_select_kernel(VerifyArgs a) {
+  __shared__ double s_val[4], s_tot[4], s_part[4][64];
+  __shared__ int s_idx[4];
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const ReqState st = a.req[b];
-  if (!st.pending) return;
-  const int gamma = a.gamma, V = a.V, nt = a.n_tiles, n = st.n;
+  if (!st.pending) return;  // uniform across the workgroup
+  const int gamma = a.gamma, V = a.V, nt = a.n_tiles, n = st.n, r = a.r;
   const double invT = 1.0 / (double)a.temperature[b];
   const uint32_t off = a.pos_offset ? (uint32_t)a.pos_offset[b] : 0u;
   const uint32_t rpos = n + 1 + off;
@@ -280,54 +347,71 @@ __global__ __launch_bounds__(64) void residual_select_kernel(VerifyArgs a) {
   const float* R = a.rsum + (size_t)b * nt;
   const int nblk = (nt + kTilesPerBlock - 1) / kTilesPerBlock;
 
+  // block masses: wavefront w sums blocks w, w+4, ... (one coalesced read each)
   double tot = 0.0, best = -INFINITY;
   int bi = 0x7fffffff;
-  for (int blk = lane; blk < nblk; blk += 64) {
-    double rb = 0.0;
-    for (int t = blk * kTilesPerBlock; t < min((blk + 1) * kTilesPerBlock, nt); ++t) rb += (double)R[t];
+  for (int blk = wave; blk < nblk; blk += 4) {
+    const int t = blk * kTilesPerBlock + lane;
+    const double rb = wave_sum(t < nt ? (double)R[t] : 0.0);
     tot += rb;
     if (rb > 0.0) {
       const double val = log(rb) + gumbel(a.seed, kFinalTop, b, rpos, blk);
       if (val > best) best = val, bi = blk;
     }
   }
-  tot = wave_sum(tot);
-  wave_argmax(best, bi);
+  if (lane == 0) s_val[wave] = best, s_idx[wave] = bi, s_tot[wave] = tot;
+  __syncthreads();
+  tot = (s_tot[0] + s_tot[1]) + (s_tot[2] + s_tot[3]);
+  best = -INFINITY, bi = 0x7fffffff;
+  for (int w = 0; w < 4; ++w)
+    if (s_val[w] > best || (s_val[w] == best && s_idx[w] < bi)) best = s_val[w], bi = s_idx[w];
 
-  int y;
   const TL* trow = static_cast<const TL*>(a.target) + ((size_t)b * (gamma + 1) + n) * V;
-  if (!(tot > 0.0)) {
-    // no residual mass: draw from p itself
-    y = sample_row(trow, a.bstat + ((size_t)b * (gamma + 1) + n) * a.n_blk, a.n_blk, V, invT, a.seed,
-                   b, rpos, lane);
-  } else {
-    bi = index_or(bi, nblk, 0);
-    const int t0 = bi * kTilesPerBlock, t1 = min(t0 + kTilesPerBlock, nt);
-    double val = -INFINITY;
-    int ti = 0x7fffffff;
-    if (t0 + lane < t1 && R[t0 + lane] > 0.0f) {
-      val = log((double)R[t0 + lane]) + gumbel(a.seed, kFinalMid, b, rpos, lane);
-      ti = t0 + lane;
+  if (!(tot > 0.0)) {  // no residual mass: draw from p itself
+    if (wave == 0) {
+      const int y = sample_row(trow, a.bstat + ((size_t)b * (gamma + 1) + n) * a.n_blk, a.n_blk, V, invT, a.seed,
+                               b, rpos, lane);
+      if (lane == 0) {
+        a.out_tokens[(size_t)b * (gamma + 1) + n] = y;
+        a.req[b].res_mass = tot;
+      }
     }
-    wave_argmax(val, ti);
-    ti = index_or(ti, t1, t0);
-    const int v = ti * kTile + lane;
-    double lv = -INFINITY, lp = -INFINITY;
-    int vi = 0x7fffffff;
-    if (v < V) {
-      double p;
-      const double rv = residual_at<TL, TF>(a, b, st, prev, invT, lse_q, v, &p);
-      const double g = gumbel(a.seed, kFinalLeaf, b, rpos, lane);
-      if (rv > 0.0) lv = log(rv) + g, vi = v;
-      lp = log(p) + g;
-    }
-    wave_argmax(lv, vi);
-    if (vi == 0x7fffffff) {  // the chosen tile lost all residual mass in fp64
-      vi = v < V ? v : 0x7fffffff;
-      wave_argmax(lp, vi);
-    }
-    y = index_or(vi, min(V, (ti + 1) * kTile), ti * kTile);
+    return;
   }
+  bi = index_or(bi, nblk, 0);
+  const int t0 = bi * kTilesPerBlock, t1 = min(t0 + kTilesPerBlock, nt);
+  double val = -INFINITY;
+  int ti = 0x7fffffff;
+  if (t0 + lane < t1 && R[t0 + lane] > 0.0f) {
+    val = log((double)R[t0 + lane]) + gumbel(a.seed, kFinalMid, b, rpos, lane);
+    ti = t0 + lane;
+  }
+  wave_argmax(val, ti);
+  ti = index_or(ti, t1, t0);
+
+  // Markov bias of the chosen tile in fp64, rank split over the wavefronts
+  const int v = ti * kTile + lane;
+  const int kq = (r + 3) / 4, k0 = min(wave * kq, r), k1 = min(k0 + kq, r);
+  const TF* h = static_cast<const TF*>(a.U) + (size_t)prev * r;
+  s_part[wave][lane] = v < V ? dot_range<TF>(h, static_cast<const TF*>(a.Wt) + (size_t)v * r, k0, k1) : 0.0;
+  __syncthreads();
+  if (wave != 0) return;
+  double lv = -INFINITY, lp = -INFINITY;
+  int vi = 0x7fffffff;
+  if (v < V) {
+    double p;
+    const double bias = (s_part[0][lane] + s_part[1][lane]) + (s_part[2][lane] + s_part[3][lane]);
+    const double rv = residual_at<TL>(a, b, st, invT, lse_q, v, bias, &p);
+    const double g = gumbel(a.seed, kFinalLeaf, b, rpos, lane);
+    if (rv > 0.0) lv = log(rv) + g, vi = v;
+    lp = log(p) + g;
+  }
+  wave_argmax(lv, vi);
+  if (vi == 0x7fffffff) {  // the chosen tile lost all residual mass in fp64
+    vi = v < V ? v : 0x7fffffff;
+    wave_argmax(lp, vi);
+  }
+  const int y = index_or(vi, min(V, (ti + 1) * kTile), ti * kTile);
   if (lane == 0) {
     a.out_tokens[(size_t)b * (gamma + 1) + n] = y;
     a.req[b].res_mass = tot;
@@ -341,12 +425,14 @@ __global__ __launch_bounds__(64) void residual_debug_kernel(VerifyArgs a) {
   if (!st.pending) return;
   const int v = tile * kTile + lane;
   if (v >= a.V) return;
-  const int gamma = a.gamma, n = st.n;
+  const int gamma = a.gamma, n = st.n, r = a.r;
   int prev = n == 0 ? a.prev0[b] : a.draft[(size_t)b * gamma + n - 1];
   prev = prev < 0 ? 0 : (prev >= a.V ? a.V - 1 : prev);
   const double invT = 1.0 / (double)a.temperature[b];
+  const TF* h = static_cast<const TF*>(a.U) + (size_t)prev * r;
+  const double bias = dot_range<TF>(h, static_cast<const TF*>(a.Wt) + (size_t)v * r, 0, r);
   double p;
-  const double rv = residual_at<TL, TF>(a, b, st, prev, invT, a.draft_lse[(size_t)b * gamma + n], v, &p);
+  const double rv = residual_at<TL>(a, b, st, invT, a.draft_lse[(size_t)b * gamma + n], v, bias, &p);
   a.debug_residual[(size_t)b * a.V + v] = (float)(st.res_mass > 0.0 ? rv / st.res_mass : p);
 }
 
@@ -370,19 +456,19 @@ hipError_t launch_row_stats(const VerifyArgs& a, int logits_dtype, hipStream_t s
 }
 
 hipError_t launch_accept(const VerifyArgs& a, int logits_dtype, hipStream_t s) {
-  if (logits_dtype == DSPARK_BF16) accept_kernel<uint16_t><<<a.B, 64, 0, s>>>(a);
-  else accept_kernel<float><<<a.B, 64, 0, s>>>(a);
+  if (logits_dtype == DSPARK_BF16) accept_kernel<uint16_t><<<a.B, 256, 0, s>>>(a);
+  else accept_kernel<float><<<a.B, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_residual_select(const VerifyArgs& a, int logits_dtype, int factor_dtype,
                                   hipStream_t s) {
   if (logits_dtype == DSPARK_BF16) {
-    if (factor_dtype == DSPARK_BF16) residual_select_kernel<uint16_t, uint16_t><<<a.B, 64, 0, s>>>(a);
-    else residual_select_kernel<uint16_t, float><<<a.B, 64, 0, s>>>(a);
+    if (factor_dtype == DSPARK_BF16) residual_select_kernel<uint16_t, uint16_t><<<a.B, 256, 0, s>>>(a);
+    else residual_select_kernel<uint16_t, float><<<a.B, 256, 0, s>>>(a);
   } else {
-    if (factor_dtype == DSPARK_BF16) residual_select_kernel<float, uint16_t><<<a.B, 64, 0, s>>>(a);
-    else residual_select_kernel<float, float><<<a.B, 64, 0, s>>>(a);
+    if (factor_dtype == DSPARK_BF16) residual_select_kernel<float, uint16_t><<<a.B, 256, 0, s>>>(a);
+    else residual_select_kernel<float, float><<<a.B, 256, 0, s>>>(a);
   }
   return hipGetLastError();
 }
