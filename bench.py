@@ -3,7 +3,7 @@
 A step is one whole round over the batch: dspark_draft_round (Markov-bias GEMM
 + softmax statistics and a draw per block position), dspark_schedule (verify
 budgets from the confidence scores) and dspark_verify (target row statistics,
-accept tests, residual or bonus draw).  Workload: B = 256 requests, gamma = 5,
+accept tests, residual or bonus draw), in that order on one stream.  Workload: B = 256 requests, gamma = 5,
 V = 151936, Markov rank r = 256, bf16 logits and factors (the DSpark-5 generator
 at B = 256), confidence scores sigmoid(N(1.5 - 0.4 j, 1)) and the synthetic
 16-point step-rate table; inputs are seeded synthetic tensors resident in HBM.

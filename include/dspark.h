@@ -23,8 +23,12 @@
  *   - Tensor arguments are DEVICE pointers owned by the caller; the library
  *     never allocates, frees or keeps them.  Layouts are dense row-major.
  *   - `workspace` is a device buffer of at least dspark_workspace_bytes(B,
- *     gamma, V, r) bytes, 256-byte aligned, owned by the caller.  Calls that
- *     share a workspace must be ordered on one stream.
+ *     gamma, V, r) bytes (dspark_schedule alone: dspark_schedule_workspace_bytes
+ *     (B, gamma)), 256-byte aligned, zero-filled before its first use, owned by
+ *     the caller.  Calls that share a workspace must be ordered on one stream,
+ *     with one exception: dspark_schedule touches only its own part of the
+ *     workspace and the status word (atomically), so it may run on another
+ *     stream concurrently with dspark_draft_round of the same round.
  *   - `stream` is a hipStream_t passed as void* (NULL = default stream).  Every
  *     call only enqueues work on it and returns; nothing synchronises the host
  *     except dspark_status().
@@ -50,7 +54,7 @@
 extern "C" {
 #endif
 
-#define DSPARK_ABI_VERSION 1
+#define DSPARK_ABI_VERSION 2
 
 enum dspark_status_code {
   DSPARK_OK = 0,
@@ -73,6 +77,11 @@ const char* dspark_error_string(int code);
 /* Bytes of device workspace the three calls need for these sizes (0 if a size
  * is out of range).  One workspace serves draft, schedule and verify. */
 size_t dspark_workspace_bytes(int B, int gamma, int V, int r);
+
+/* Bytes of device workspace dspark_schedule needs on its own (0 if a size is
+ * out of range: B >= 1, 1 <= gamma <= 16, B * gamma <= 8192); never more than
+ * dspark_workspace_bytes for the same B and gamma. */
+size_t dspark_schedule_workspace_bytes(int B, int gamma);
 
 /*
  * dspark_draft_round -- [P1] eq. p_k with the Markov head.
@@ -125,7 +134,10 @@ int dspark_draft_round(const void* base_logits, int logits_dtype,
  *   sps_B    [n_points] float64  batch sizes in tokens, strictly increasing
  *   sps_val  [n_points] float64  steps per second at those sizes, > 0
  *   budget   [B] int32 out       verify budgets in [0, gamma]
- * Limits: n_points in [2, 1024], B * gamma <= 8192.
+ * Limits: n_points in [2, 1024], B * gamma <= 8192.  The position of each
+ * candidate in the order above is computed directly (the number of candidates
+ * before it) rather than by sorting, so every admission test runs in parallel
+ * with exactly the stated arithmetic.
  */
 int dspark_schedule(const float* conf, const double* sps_B, const double* sps_val,
                     int n_points, int B, int gamma, int32_t* budget,

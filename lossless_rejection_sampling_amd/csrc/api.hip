@@ -15,11 +15,19 @@ namespace {
 constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-// Workspace: [header | tile stats | block stats | request state | slot list | residual tile mass]
+// Workspace: [header | scheduler ranks | tile stats | block stats | request state | slot list |
+// residual tile mass].  Header words: 0 status, 1 residual slot count, 2 scheduler
+// ticket, 3 scheduler first failure.  The header and the scheduler ranks are all
+// that dspark_schedule touches, at offsets that do not depend on V and r.
+constexpr size_t kHeaderBytes = 256;
 struct Layout {
-  size_t header, tstat, bstat, req, slots, rsum, total;
+  size_t header, sched, tstat, bstat, req, slots, rsum, total;
   int n_tiles, n_blk;
 };
+
+bool schedule_sizes_ok(int B, int gamma) {
+  return B >= 1 && gamma >= 1 && gamma <= 16 && (long long)B * gamma <= 8192;
+}
 
 bool sizes_ok(int B, int gamma, int V, int r) {
   return B >= 1 && gamma >= 1 && gamma <= 16 && V >= 1 && r >= 1 &&
@@ -33,7 +41,9 @@ Layout layout(int B, int gamma, int V, int r) {
   L.n_blk = (V + kBlock - 1) / kBlock;
   size_t off = 0;
   L.header = off;
-  off = align_up(off + 256);
+  off = align_up(off + kHeaderBytes);
+  L.sched = off;
+  off = align_up(off + (size_t)B * gamma * sizeof(int32_t));
   L.tstat = off;
   off = align_up(off + (size_t)B * L.n_tiles * sizeof(TileStat));
   L.bstat = off;
@@ -113,6 +123,11 @@ size_t dspark_workspace_bytes(int B, int gamma, int V, int r) {
   return layout(B, gamma, V, r).total;
 }
 
+size_t dspark_schedule_workspace_bytes(int B, int gamma) {
+  if (!schedule_sizes_ok(B, gamma)) return 0;
+  return align_up(kHeaderBytes) + align_up((size_t)B * gamma * sizeof(int32_t));
+}
+
 int dspark_draft_round(const void* base_logits, int logits_dtype, const void* U, const void* W,
                        int factor_dtype, const int32_t* prev0, const float* temperature,
                        uint64_t seed, const int32_t* pos_offset, int B, int gamma, int V, int r,
@@ -157,7 +172,7 @@ int dspark_draft_round(const void* base_logits, int logits_dtype, const void* U,
 
 int dspark_schedule(const float* conf, const double* sps_B, const double* sps_val, int n_points,
                     int B, int gamma, int32_t* budget, void* workspace, void* stream) {
-  if (B < 1 || gamma < 1 || gamma > 16 || (long long)B * gamma > 8192) return DSPARK_EINVAL;
+  if (!schedule_sizes_ok(B, gamma)) return DSPARK_EINVAL;
   if (n_points < 2 || n_points > 1024) return DSPARK_EINVAL;
   if (!conf || !sps_B || !sps_val || !budget || !workspace) return DSPARK_EINVAL;
   if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return DSPARK_EINVAL;
@@ -166,6 +181,8 @@ int dspark_schedule(const float* conf, const double* sps_B, const double* sps_va
   a.conf = conf, a.sps_B = sps_B, a.sps_val = sps_val, a.n_points = n_points;
   a.B = B, a.gamma = gamma, a.budget = budget;
   a.status = at<uint32_t>(workspace, 0);
+  a.ticket = a.status + 2, a.stop_enc = a.status + 3;
+  a.rank = at<int32_t>(workspace, align_up(kHeaderBytes));
   ProfileScope ps(kClsSchedule, s);
   DSPARK_TRY(launch_schedule(a, s));
   return DSPARK_OK;

@@ -10,6 +10,8 @@
 // contraction are contiguous along r.
 #include <math.h>
 
+#include <type_traits>
+
 #include "dspark.h"
 #include "kernels.hpp"
 
@@ -572,36 +574,43 @@ __global__ __launch_bounds__(256) void draft_select_kernel(DraftSelectArgs a) {
     const double mref = (double)ts[0].ref + (double)ts[0].mx;
     double best = -INFINITY, row_m = -INFINITY, row_s = 0.0;
     int best_blk = 0x7fffffff;
-    // blocks of this wavefront in chunks of 16: all tile records of a chunk are
-    // requested first, then reduced block by block; lane j keeps block j's
-    // (max, mass), and the 16 Gumbels and logarithms are computed in parallel
-    for (int c0 = wave; c0 < nblk; c0 += 64) {
-      TileStat rec[16];
+    // Chunks of 16 blocks (1024 tile records): thread tid reads the records of
+    // tiles 4 tid .. 4 tid + 3 of the chunk, so the 16 lanes 16 k .. 16 k + 15
+    // of a wavefront hold one block; its max and mass reduce within those
+    // lanes.  The first lane of each block keeps the running Gumbel-max choice
+    // (blocks in increasing order, so ties keep the lowest) and the running
+    // log-sum-exp.
+    for (int c = 0; c < nblk; c += 16) {
+      const int blk = c + wave * 4 + (lane >> 4);
+      const int tb = c * kTilesPerBlock + 4 * tid;
+      double d[4];
+      float sm[4];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int t = (c0 + 4 * j) * kTilesPerBlock + lane;
-        if (c0 + 4 * j < nblk && t < nt) rec[j] = ts[t];
-        else rec[j].ref = -INFINITY, rec[j].mx = 0.0f, rec[j].sum = 0.0f;
-      }
-      double my_d = -INFINITY, my_s = 0.0;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        if (c0 + 4 * j >= nblk) break;  // uniform
-        const double d = (double)rec[j].ref + (double)rec[j].mx;
-        const double dmax = wave_max(d);
-        const float e = rec[j].sum > 0.0f ? rec[j].sum * expf((float)((d - dmax) * invT)) : 0.0f;
-        const float sblk = wave_sum(e);
-        if (lane == j) my_d = dmax, my_s = (double)sblk;
-      }
-      const int blk = c0 + 4 * lane;
-      if (lane < 16 && blk < nblk) {
-        const double val = (my_d - mref) * invT + log(my_s) + gumbel(a.seed, kDraftTop, b, rpos, blk);
-        if (val > best) best = val, best_blk = blk;
-        if (my_d > row_m) {
-          row_s = row_s * exp((row_m - my_d) * invT) + my_s;
-          row_m = my_d;
+      for (int q = 0; q < 4; ++q) {
+        if (tb + q < nt) {
+          const TileStat st = ts[tb + q];
+          d[q] = (double)st.ref + (double)st.mx, sm[q] = st.sum;
         } else {
-          row_s += my_s * exp((my_d - row_m) * invT);
+          d[q] = -INFINITY, sm[q] = 0.0f;
+        }
+      }
+      double m = fmax(fmax(d[0], d[1]), fmax(d[2], d[3]));
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) m = fmax(m, __shfl_xor(m, o));
+      float e = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (sm[q] > 0.0f) e += sm[q] * expf((float)((d[q] - m) * invT));
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) e += __shfl_xor(e, o);
+      if ((lane & 15) == 0 && blk < nblk) {
+        const double val = (m - mref) * invT + log((double)e) + gumbel(a.seed, kDraftTop, b, rpos, blk);
+        if (val > best) best = val, best_blk = blk;
+        if (m > row_m) {
+          row_s = row_s * exp((row_m - m) * invT) + (double)e;
+          row_m = m;
+        } else {
+          row_s += (double)e * exp((m - row_m) * invT);
         }
       }
     }
@@ -683,44 +692,341 @@ __global__ __launch_bounds__(256) void draft_select_kernel(DraftSelectArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Coalesced variant for bf16 logits (V a multiple of 8), the one the headline
-// round runs.  Both streams of a tile go through LDS by direct loads whose every
-// instruction reads whole rows:
-//   * W2 tile: 64 rows x R bf16.  Instruction f reads 64/NC full rows (NC = R/8
-//     16-byte chunks per row); lane l takes chunk (l % NC) ^ (row % NC) of its
-//     row, so LDS holds the rows with their chunks xor-swizzled by the row and
-//     the MFMA operand reads (32 rows, one chunk each) spread over all banks.
-//   * backbone logits: 256 slots x 64 columns x 2 B; instruction f reads 8 full
-//     128-byte slot rows, chunk (l % 8) ^ (slot % 8) per lane, swizzled alike
-//     for the epilogue's 8-byte reads.
-// Two-slot rings for both (128 KB of LDS at R = 256).
+// Coalesced draft kernel for bf16 logits (V a multiple of 8) and bf16 factors.
+// A workgroup of 8 wavefronts owns 256 slots (32 per wavefront, the MFMA B
+// operand columns, with their U rows held in registers) and walks the tiles
+// t = blockIdx.x, + gridDim.x, ...  Both streams of a tile, the W2 rows and the
+// backbone logits of the 256 slots, reach LDS by direct loads of whole rows
+// into two-slot rings (layouts below); one barrier per tile.
 // ---------------------------------------------------------------------------
-template <bool RESIDUAL, int R>
-__global__ __launch_bounds__(512, 1) void gemm_stats_coalesced(GemmArgs a) {
-  constexpr int NC = R / 8;                       // 16-byte chunks per W2 row
-  constexpr int W_BYTES = kTile * R * 2;          // 32 KB at R = 256
-  constexpr int X_BYTES = kSlotsPerGroup * kTile * 2;  // 32 KB
-  constexpr int W_INSTR = W_BYTES / 1024, X_INSTR = X_BYTES / 1024;
+// Reduction with the partner lane (lane ^ 32) through v_permlane32_swap: the
+// swap of a register with itself returns the low half of the wave in both
+// halves of the first result and the high half in both halves of the second,
+// so op(first, second) is the pairwise result, identical in both lanes.
+__device__ __forceinline__ float pair_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// LDS layouts of the streamed tiles.  Every direct load writes one contiguous
+// 1 KB block from whole rows; inside a block the 16-byte chunks are ordered
+// chunk-major, and the blocks are spaced so that the operand reads of 16
+// consecutive lanes fall in distinct bank groups while every lane's address for
+// chunk c is its own base plus a constant (an instruction immediate).
+//   W2 tile (64 rows x R bf16): RB = 1024 / (2R) rows per block, row rho's
+//   chunk c at byte 16 (RB c + rho) of block b = row / RB, blocks 1024 + 16 RB
+//   bytes apart.
+//   logit tile (slots x 64 bf16): 8 slots per block, slot rho's chunk c at byte
+//   16 (8 c + rho); block b starts at 1024 b + 8 (b % 2) + 128 ((b / 2) % 2)
+//   + 256 (b / 4), so that 32 lanes' 8-byte reads of one chunk are disjoint.
+template <int R>
+struct WLayout {
+  static constexpr int RB = 1024 / (2 * R);
+  static constexpr int NB = kTile / RB;
+  static constexpr int STRIDE = 1024 + 16 * RB;
+  static constexpr int BYTES = NB * STRIDE;
+  __device__ static int block(int b) { return b * STRIDE; }
+  // byte offset of row v, chunk c
+  __device__ static int at(int v, int c) { return (v / RB) * STRIDE + 16 * (RB * c + v % RB); }
+};
+struct XLayout {
+  __device__ static int block(int b) { return b * 1024 + 8 * (b & 1) + 128 * ((b >> 1) & 1) + 256 * (b >> 2); }
+  static constexpr int bytes(int slots) { return (slots / 8) * 1024 + 136 + 256 * (slots / 32); }
+  __device__ static int at(int s, int c) { return block(s >> 3) + 16 * (8 * c + (s & 7)); }
+};
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int R>
+__global__ __launch_bounds__(512, 1) void gemm_draft_coalesced(GemmArgs a) {
+  using WL = WLayout<R>;
+  constexpr int W_SLOT = (WL::BYTES + 1023) / 1024 * 1024;
+  constexpr int X_SLOT = (XLayout::bytes(kSlotsPerGroup) + 1023) / 1024 * 1024;
+  constexpr int KS = R / 16;                     // MFMA k-steps per tile
+  constexpr int W_DMA = WL::NB / 8;              // direct loads per wave per tile: W2
+  constexpr int X_DMA = kSlotsPerGroup / 64;     // and backbone logits
   extern __shared__ __attribute__((aligned(1024))) char lds[];
-  char* const wring = lds;                        // 2 x W_BYTES
-  char* const xring = lds + 2 * W_BYTES;          // 2 x X_BYTES
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nwaves = blockDim.x >> 6;
+  char* const wring = lds;                        // 2 x W_SLOT
+  char* const xring = lds + 2 * W_SLOT;           // 2 x X_SLOT
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, l32 = lane & 31;
-  const int nslots = RESIDUAL ? (int)*a.slot_count : a.B;
+  const int nslots = a.B;
   const int sg0 = blockIdx.y * kSlotsPerGroup;
   const int nt = a.n_tiles, G = gridDim.x;
   if (sg0 >= nslots || (int)blockIdx.x >= nt) return;  // uniform across the workgroup
   const int V = a.V;
-  const uint16_t* Wt = static_cast<const uint16_t*>(a.Wt);
+  // byte offsets from uniform bases are 32-bit (the launcher checks the sizes)
+  const char* const Wb = static_cast<const char*>(a.Wt);
+  const char* const Xb = static_cast<const char*>(a.base);
+
+  // direct load k of this wave for the W2 tile `tile` into ring slot buf
+  auto dma_w = [&](int k, int tile, int buf) {
+    const int f = wave + 8 * k;
+    const int rho = lane % WL::RB, c = lane / WL::RB;
+    const int v = min(tile * kTile + f * WL::RB + rho, V - 1);  // rows beyond V only feed masked columns
+    __builtin_amdgcn_global_load_lds(Wb + ((uint32_t)v * (R * 2) + c * 16),
+                                     (lds_ptr_t)(wring + buf * W_SLOT + WL::block(f)), 16, 0, 0);
+  };
+  // W2 needs nothing from the slots: the first two tiles start loading at once
+  int t = blockIdx.x;
+#pragma unroll
+  for (int k = 0; k < W_DMA; ++k) dma_w(k, t, 0);
+  if (t + G < nt) {
+#pragma unroll
+    for (int k = 0; k < W_DMA; ++k) dma_w(k, t + G, 1);
+  }
 
   // this wave's 32 slots (MFMA B operand columns)
   const bool active = sg0 + wave * 32 < nslots;
   int rq, pos, prev;
   bool valid;
-  slot_info<RESIDUAL>(a, sg0 + wave * 32 + l32, nslots, rq, pos, prev, valid);
-  const uint16_t* trow = RESIDUAL
-      ? static_cast<const uint16_t*>(a.target) + ((size_t)rq * (a.gamma + 1) + pos) * V : nullptr;
+  slot_info<false>(a, sg0 + wave * 32 + l32, nslots, rq, pos, prev, valid);
+  // backbone-logit rows this lane loads: slot 8 f + lane % 8 of the direct loads
+  // f = wave + 8 k
+  uint32_t xoff[X_DMA];  // element offset of the row in the backbone logits [B * gamma, V]
+#pragma unroll
+  for (int k = 0; k < X_DMA; ++k) {
+    const int sx = (wave + 8 * k) * 8 + (lane & 7);
+    int b2, p2, pr2;
+    bool v2;
+    slot_info<false>(a, sg0 + sx, nslots, b2, p2, pr2, v2);
+    xoff[k] = (uint32_t)(b2 * a.gamma + p2) * (uint32_t)V;
+  }
+  auto dma_x = [&](int k, int tile, int buf) {
+    const int f = wave + 8 * k;
+    const int col = min(tile * kTile + ((lane >> 3) << 3), V - 8);  // the ragged tile is masked later
+    __builtin_amdgcn_global_load_lds(Xb + (xoff[k] + col) * 2,
+                                     (lds_ptr_t)(xring + buf * X_SLOT + XLayout::block(f)), 16, 0, 0);
+  };
+#pragma unroll
+  for (int k = 0; k < X_DMA; ++k) dma_x(k, t, 0);
+
   const float T = valid ? effective_temp(a.temperature[rq]) : 1.0f;
+  const float cT = T > 0.0f ? kLog2e / T : 0.0f;
+  bf16x8 H[KS];
+  {
+    const uint16_t* h = static_cast<const uint16_t*>(a.U) + (size_t)prev * R + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 zero = {};
+      H[ks] = valid ? *reinterpret_cast<const bf16x8*>(h + ks * 16) : zero;
+    }
+  }
+  // operand bases: W2 row l32 (column block 0) with chunk half; logits of this
+  // lane's slot, 8-byte half
+  const int wbase = WL::at(l32, half);
+  const int xbase = XLayout::at(wave * 32 + l32, 0) + 8 * half;
+  const uint32_t st_base = (uint32_t)rq * (uint32_t)nt;
+
+  auto read_x = [&](int buf, TileBuf<uint16_t>& x) {
+    const char* p = xring + buf * X_SLOT + xbase;
+#pragma unroll
+    for (int vb = 0; vb < 2; ++vb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const uint2 u = *reinterpret_cast<const uint2*>(p + 128 * (vb * 4 + g));
+        x.w[vb][2 * g] = u.x, x.w[vb][2 * g + 1] = u.y;
+      }
+  };
+  // streaming store of a tile record (nothing reads it before the next launch)
+  auto put = [&](int tile, const TileStat& st) {
+    const f32x4 v = {st.ref, st.mx, st.sum, 0.0f};
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(reinterpret_cast<char*>(a.tstat) +
+                                                            (st_base + (uint32_t)tile) * 16u));
+  };
+  // MFMAs of the next tile (W2 slot wb) interleaved by hand with the statistics
+  // of the current one: k-step ks reads the operands of step ks + 1, issues its
+  // two MFMAs and one slice of the epilogue, fenced so that the MFMA pipe and
+  // the VALU work side by side within the wave.  The epilogue's phases (unpack
+  // and tile max of the logits; t = (x - ref) + bias and its max; exp2 sum)
+  // take the first, second and last two quarters of the k-steps.
+  auto fused = [&](auto masked, int wb, int tile, const f32x16 (&cur)[2], f32x16 (&next)[2],
+                   const TileBuf<uint16_t>& x, TileStat& st) {
+    constexpr bool MASK = decltype(masked)::value;
+    const char* base = wring + wb * W_SLOT + wbase;
+    auto rd = [&](int ks, int vb) {  // rows vb * 32 + l32, chunk 2 ks + half
+      return *reinterpret_cast<const bf16x8*>(base + 32 * WL::RB * ks + (32 / WL::RB) * WL::STRIDE * vb);
+    };
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) next[i][e] = 0.0f;
+    float xv[32];  // element j = 16 vb + e; becomes t in place
+    float ref = -INFINITY, tmax = -INFINITY, mc = 0.0f, sum = 0.0f;
+    bf16x8 A[2][2];
+    A[0][0] = rd(0, 0), A[0][1] = rd(0, 1);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int cb = ks & 1;
+      if (ks + 1 < KS) A[cb ^ 1][0] = rd(ks + 1, 0), A[cb ^ 1][1] = rd(ks + 1, 1);
+      next[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[cb][0], H[ks], next[0], 0, 0, 0);
+      next[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[cb][1], H[ks], next[1], 0, 0, 0);
+      constexpr int PA = KS / 4, PB = KS / 2;  // phase boundaries
+      if (ks < PA) {
+        constexpr int n = 32 / PA;
+#pragma unroll
+        for (int j = ks * n; j < ks * n + n; ++j) {
+          const int vb = j >> 4, e = j & 15;
+          xv[j] = x.get(vb, e);
+          if (MASK && acc_col(tile * kTile, vb, e, half) >= V) xv[j] = -INFINITY;
+          ref = fmaxf(ref, xv[j]);
+        }
+        asm volatile("" : "+v"(ref));  // keeps this slice in its k-step
+      } else if (ks < PB) {
+        if (ks == PA) ref = pair_max(ref);
+        constexpr int n = 32 / (PB - PA);
+#pragma unroll
+        for (int j = (ks - PA) * n; j < (ks - PA) * n + n; ++j) {
+          xv[j] = (xv[j] - ref) + cur[j >> 4][j & 15];
+          tmax = fmaxf(tmax, xv[j]);
+        }
+        asm volatile("" : "+v"(tmax));  // keeps this slice in its k-step
+      } else {
+        if (ks == PB) tmax = pair_max(tmax), mc = tmax * cT;
+        constexpr int n = 32 / (KS - PB);
+#pragma unroll
+        for (int j = (ks - PB) * n; j < (ks - PB) * n + n; ++j) sum += __builtin_amdgcn_exp2f(fmaf(xv[j], cT, -mc));
+        asm volatile("" : "+v"(sum));  // keeps this slice in its k-step
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    st.ref = ref, st.mx = tmax, st.sum = pair_sum(sum), st.pad = 0.0f;
+  };
+
+  f32x16 acc0[2] = {}, acc1[2] = {};
+  TileStat st;
+  int st_tile = -1;
+  wait_vmcnt(0);
+  __syncthreads();
+  if (active) {
+    TileBuf<uint16_t> none = {};
+    fused(std::false_type{}, 0, t, acc1, acc0, none, st);  // MFMAs of the first tile only
+  }
+  __syncthreads();
+  // Ring discipline: in iteration i (tile t_i) W2 slot i%2, last read by the
+  // MFMAs of t_i, receives W2 of t_{i+2}; logit slot (i+1)%2, emptied at the top
+  // of iteration i-1, receives the logits of t_{i+1}.  The logits of t_i leave
+  // LDS and the record of t_{i-1} goes out before any load is issued.
+  auto step = [&](int c0, const f32x16 (&cur)[2], f32x16 (&next)[2]) {
+    const int c1 = c0 ^ 1;
+    TileBuf<uint16_t> x;
+    if (active) {
+      read_x(c0, x);
+      if (st_tile >= 0 && half == 0 && valid) put(st_tile, st);
+    }
+    if (t + 2 * G < nt) {
+#pragma unroll
+      for (int k = 0; k < W_DMA; ++k) dma_w(k, t + 2 * G, c0);
+    }
+    if (t + G < nt) {
+#pragma unroll
+      for (int k = 0; k < X_DMA; ++k) dma_x(k, t + G, c1);
+    }
+    if (active) {
+      // the MFMAs of the last tile's successor read a stale slot and are discarded
+      if ((t + 1) * kTile <= V) fused(std::false_type{}, c1, t, cur, next, x, st);
+      else fused(std::true_type{}, c1, t, cur, next, x, st);
+      st_tile = t;
+    }
+    wait_vmcnt(0);
+    __syncthreads();
+    t += G;
+  };
+  for (;;) {
+    step(0, acc0, acc1);
+    if (t >= nt) break;
+    step(1, acc1, acc0);
+    if (t >= nt) break;
+  }
+  if (active && st_tile >= 0 && half == 0 && valid) put(st_tile, st);
+}
+
+template <int R>
+hipError_t launch_coalesced(const GemmArgs& a, hipStream_t s) {
+  static int max_wg = 0;
+  const size_t lds = (size_t)2 * ((WLayout<R>::BYTES + 1023) / 1024 * 1024) +
+                     (size_t)2 * ((XLayout::bytes(kSlotsPerGroup) + 1023) / 1024 * 1024);
+  const void* fn = reinterpret_cast<const void*>(&gemm_draft_coalesced<R>);
+  if (!max_wg) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return hipErrorUnknown;
+    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+      return hipErrorUnknown;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 512, lds) != hipSuccess || per_cu < 1)
+      per_cu = 1;
+    max_wg = cus * per_cu;
+  }
+  const int groups = (a.B + kSlotsPerGroup - 1) / kSlotsPerGroup;
+  const int wg_x = max(1, min(a.n_tiles, max_wg / groups));
+  gemm_draft_coalesced<R><<<dim3(wg_x, groups), 512, lds, s>>>(a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Residual pass over bf16 logits (V a multiple of 8): for every request whose
+// draft token at row n was rejected, the mass of max(0, p - q) in each tile,
+// with q the draft distribution of row n recomputed from the backbone logits
+// and the Markov bias.
+//
+// 128 slots per workgroup of 8 wavefronts: wavefront w holds the 32 slots
+// 32 (w % 4) .. and computes column block w / 4 (32 columns) of every tile, 16
+// MFMAs per tile.  The W2 tile (32 KB at R = 256), the backbone logits and the
+// target logits of the 128 slots (16 KB each) stream through two-slot LDS rings
+// by whole-row direct loads, swizzled as in the draft kernel; the two column
+// halves of a slot's tile mass meet in a small LDS exchange.  Workgroups map to
+// slot groups at run time from the device-side count of pending requests, so
+// the whole grid works whatever that count is.
+// ---------------------------------------------------------------------------
+constexpr int kResSlots = 128;
+
+template <int R>
+__global__ __launch_bounds__(512, 1) void gemm_residual_coalesced(GemmArgs a) {
+  constexpr int NC = R / 8;
+  constexpr int W_BYTES = kTile * R * 2;
+  constexpr int X_BYTES = kResSlots * kTile * 2;  // 16 KB
+  constexpr int W_INSTR = W_BYTES / 1024, X_INSTR = X_BYTES / 1024;
+  extern __shared__ __attribute__((aligned(1024))) char lds[];
+  __shared__ float part[2][kResSlots];
+  char* const wring = lds;                  // 2 x W_BYTES
+  char* const xring = lds + 2 * W_BYTES;    // 2 x X_BYTES backbone logits
+  char* const zring = xring + 2 * X_BYTES;  // 2 x X_BYTES target logits
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int vb = wave >> 2, sl = (wave & 3) * 32 + l32;  // column block, slot in the group
+  const int nslots = (int)*a.slot_count;
+  if (nslots <= 0) return;
+  const int ngroups = (nslots + kResSlots - 1) / kResSlots;
+  // walkers per slot group, a multiple of 8 so that the workgroups of one tile
+  // share an XCD (and its L2) across groups
+  int walkers = (int)gridDim.x / ngroups;
+  if (walkers >= 8) walkers &= ~7;
+  if (walkers < 1) walkers = 1;
+  const int group = (int)blockIdx.x / walkers;
+  const int nt = a.n_tiles, V = a.V;
+  if (group >= ngroups || (int)blockIdx.x - group * walkers >= nt) return;  // uniform
+  const int sg0 = group * kResSlots;
+  const uint16_t* Wt = static_cast<const uint16_t*>(a.Wt);
+
+  int rq, pos, prev;
+  bool valid;
+  slot_info<true>(a, sg0 + sl, nslots, rq, pos, prev, valid);
+  const bool active = sg0 + (wave & 3) * 32 < nslots;
+  float T = 1.0f, kp = 0.0f;
+  double lse_q = 0.0;
+  if (valid) {
+    T = effective_temp(a.temperature[rq]);
+    const ReqState st = a.req[rq];
+    kp = (float)(((double)st.row_max / (double)T + st.row_logsum) * 1.4426950408889634);
+    lse_q = a.draft_lse[(size_t)rq * a.gamma + pos];
+  }
+  if (!(T > 0.0f)) T = 1.0f;  // greedy rows never hold a residual draw
+  const float c = kLog2e / T;
   bf16x8 H[R / 16];
   {
     const uint16_t* h = static_cast<const uint16_t*>(a.U) + (size_t)prev * R + half * 8;
@@ -730,154 +1036,165 @@ __global__ __launch_bounds__(512, 1) void gemm_stats_coalesced(GemmArgs a) {
       H[ks] = valid ? *reinterpret_cast<const bf16x8*>(h + ks * 16) : zero;
     }
   }
-  // rows of the backbone logits this lane loads for the logit stream: slot
-  // f*8 + lane/8 of each of this wave's instructions f = wave, wave+nwaves, ...
-  constexpr int XMAX = X_INSTR;  // at most one instruction per wave per 8 slots
-  const uint16_t* xsrc[4];
-  int nx = 0;
-  for (int f = wave; f < X_INSTR && nx < 4; f += nwaves, ++nx) {
-    const int s = f * 8 + (lane >> 3);
+  // rows this lane loads for the logit streams: slot f * 8 + lane / 8 of
+  // instructions f = wave, wave + 8
+  const uint16_t* xsrc[X_INSTR / 8];
+  const uint16_t* zsrc[X_INSTR / 8];
+#pragma unroll
+  for (int k = 0; k < X_INSTR / 8; ++k) {
+    const int sx = (wave + 8 * k) * 8 + (lane >> 3);
     int b2, p2, pr2;
     bool v2;
-    slot_info<RESIDUAL>(a, sg0 + s, nslots, b2, p2, pr2, v2);
-    xsrc[nx] = static_cast<const uint16_t*>(a.base) + ((size_t)b2 * a.gamma + p2) * V;
+    slot_info<true>(a, sg0 + sx, nslots, b2, p2, pr2, v2);
+    xsrc[k] = static_cast<const uint16_t*>(a.base) + ((size_t)b2 * a.gamma + p2) * V;
+    zsrc[k] = static_cast<const uint16_t*>(a.target) + ((size_t)b2 * (a.gamma + 1) + p2) * V;
   }
-  (void)XMAX;
 
   auto fill_w = [&](int tile, int buf) {
-    for (int f = wave; f < W_INSTR; f += nwaves) {
+#pragma unroll
+    for (int k = 0; k < W_INSTR / 8; ++k) {
+      const int f = wave + 8 * k;
       const int r = f * (64 / NC) + lane / NC, p = lane % NC;
       int v = tile * kTile + r;
       v = v < V ? v : V - 1;  // rows beyond V only feed masked columns
-      const int c = p ^ (r % NC);
-      __builtin_amdgcn_global_load_lds(Wt + (size_t)v * R + c * 8,
+      __builtin_amdgcn_global_load_lds(Wt + (size_t)v * R + (p ^ (r % NC)) * 8,
                                        (lds_ptr_t)(wring + buf * W_BYTES + f * 1024), 16, 0, 0);
     }
   };
-  auto fill_x = [&](int tile, int buf) {
-    int k = 0;
-    for (int f = wave; f < X_INSTR && k < 4; f += nwaves, ++k) {
-      const int s = f * 8 + (lane >> 3), p = lane & 7;
-      const int c = p ^ (s & 7);
-      const int col = min(tile * kTile + c * 8, V - 8);  // the ragged tile is masked later
+  auto fill_xz = [&](int tile, int buf) {
+#pragma unroll
+    for (int k = 0; k < X_INSTR / 8; ++k) {
+      const int f = wave + 8 * k;
+      const int sx = f * 8 + (lane >> 3), p = lane & 7;
+      const int col = min(tile * kTile + ((p ^ ((sx >> 1) & 7)) << 3), V - 8);  // ragged tile masked later
       __builtin_amdgcn_global_load_lds(xsrc[k] + col, (lds_ptr_t)(xring + buf * X_BYTES + f * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(zsrc[k] + col, (lds_ptr_t)(zring + buf * X_BYTES + f * 1024), 16, 0, 0);
     }
   };
-  auto mma = [&](int buf, f32x16 (&acc)[2]) {
+  auto mma = [&](int buf, f32x16& acc) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][e] = 0.0f;
+    for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
     const char* base = wring + buf * W_BYTES;
-    bf16x8 A[2][2][4];
-    auto rd = [&](int ks, int vb) {
-      const int v = vb * 32 + l32, c = 2 * ks + half;
-      return *reinterpret_cast<const bf16x8*>(base + v * (R * 2) + ((c ^ (v % NC)) << 4));
+    const int v = vb * 32 + l32;
+    auto rd = [&](int ks) {
+      return *reinterpret_cast<const bf16x8*>(base + v * (R * 2) + (((2 * ks + half) ^ (v % NC)) << 4));
     };
+    bf16x8 A[2][4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int vb = 0; vb < 2; ++vb) A[0][vb][q] = rd(q, vb);
+    for (int q = 0; q < 4; ++q) A[0][q] = rd(q);
 #pragma unroll
     for (int g = 0; g < R / 64; ++g) {
       const int cur = g & 1;
       if (g + 1 < R / 64) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int vb = 0; vb < 2; ++vb) A[cur ^ 1][vb][q] = rd((g + 1) * 4 + q, vb);
+        for (int q = 0; q < 4; ++q) A[cur ^ 1][q] = rd((g + 1) * 4 + q);
       }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int vb = 0; vb < 2; ++vb)
-          acc[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[cur][vb][q], H[g * 4 + q], acc[vb], 0, 0, 0);
+      for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[cur][q], H[g * 4 + q], acc, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
-  auto read_x = [&](int buf, TileBuf<uint16_t>& x) {
-    const int s = wave * 32 + l32;
-    const char* rowp = xring + buf * X_BYTES + s * 128 + half * 8;
+  // this lane's 16 columns of the tile: vb * 32 + 8 g + 4 half + (0..3), g = 0..3
+  auto read_logits = [&](const char* ring, int buf, uint2 (&out)[4]) {
+    const char* rowp = ring + buf * X_BYTES + sl * 128 + half * 8;
 #pragma unroll
-    for (int vb = 0; vb < 2; ++vb)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int c = vb * 4 + g;
-        const uint2 u = *reinterpret_cast<const uint2*>(rowp + ((c ^ (s & 7)) << 4));
-        x.w[vb][2 * g] = u.x, x.w[vb][2 * g + 1] = u.y;
-      }
+    for (int g = 0; g < 4; ++g)
+      out[g] = *reinterpret_cast<const uint2*>(rowp + (((vb * 4 + g) ^ ((sl >> 1) & 7)) << 4));
   };
-  auto full_tile = [&](int tile) { return (tile + 1) * kTile <= V; };
+  auto unpack = [](const uint2 (&w)[4], float (&v)[16]) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      v[4 * g + 0] = __uint_as_float(w[g].x << 16);
+      v[4 * g + 1] = __uint_as_float(w[g].x & 0xFFFF0000u);
+      v[4 * g + 2] = __uint_as_float(w[g].y << 16);
+      v[4 * g + 3] = __uint_as_float(w[g].y & 0xFFFF0000u);
+    }
+  };
+  auto epilogue = [&](const f32x16& acc, const uint2 (&xw)[4], const uint2 (&zw)[4], int tile) {
+    float xv[16], zv[16];
+    unpack(xw, xv);
+    unpack(zw, zv);
+    if ((tile + 1) * kTile > V) {  // the ragged last tile: columns >= V do not exist
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (tile * kTile + vb * 32 + (e >> 2) * 8 + half * 4 + (e & 3) >= V) xv[e] = -INFINITY, zv[e] = -INFINITY;
+    }
+    float ref = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) ref = fmaxf(ref, xv[e]);
+    ref = fmaxf(ref, __shfl_xor(ref, 32));
+    ref = ref > -INFINITY ? ref : 0.0f;  // a half tile wholly beyond V
+    const float kq = (float)((lse_q - (double)ref / (double)T) * 1.4426950408889634);
+    float rs = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(zv[e], c, -kp));
+      const float q = __builtin_amdgcn_exp2f(fmaf((xv[e] - ref) + acc[e], c, -kq));
+      rs += fmaxf(p - q, 0.0f);
+    }
+    return rs + __shfl_xor(rs, 32);
+  };
 
-  f32x16 acc0[2], acc1[2];
-  int t = blockIdx.x;
-  // Ring discipline: at the start of iteration i (tile t_i) the W2 slot i%2
-  // (last read by the MFMAs of t_i in iteration i-1) receives W2 of t_{i+2}, and
-  // the logit slot (i+1)%2 (last read by the epilogue of t_{i-1}) receives the
-  // logits of t_{i+1}; both loads have the whole iteration to land.
+  const int G = walkers;
+  int t = (int)blockIdx.x - group * walkers;
+  f32x16 acc0, acc1;
   fill_w(t, 0);
   if (t + G < nt) fill_w(t + G, 1);
-  fill_x(t, 0);
+  fill_xz(t, 0);
   wait_vmcnt(0);
   __syncthreads();
   if (active) mma(0, acc0);
   __syncthreads();
-
-  int i = 0;
+  // Ring discipline as in the draft kernel: in iteration i (tile t_i) W2 slot
+  // i%2 receives W2 of t_{i+2} and logit slot (i+1)%2 the logits of t_{i+1};
+  // the logits of t_i leave LDS first, before any load is in flight.
+  auto step = [&](int c0, f32x16& cur, f32x16& next) {
+    const int c1 = c0 ^ 1;
+    uint2 xw[4], zw[4];
+    if (active) read_logits(xring, c0, xw), read_logits(zring, c0, zw);
+    if (t + 2 * G < nt) fill_w(t + 2 * G, c0);
+    if (t + G < nt) fill_xz(t + G, c1);
+    if (t + G < nt && active) mma(c1, next);
+    float rs = 0.0f;
+    if (active) {
+      rs = epilogue(cur, xw, zw, t);
+      if (vb == 1 && half == 0) part[c0][sl] = rs;
+    }
+    wait_vmcnt(0);
+    __syncthreads();
+    if (vb == 0 && half == 0 && valid) a.rsum[(size_t)rq * nt + t] = rs + part[c0][sl];
+    t += G;
+  };
   for (;;) {
-    // tile t = t_i with accumulators acc0
-    {
-      const int c0 = i & 1, c1 = c0 ^ 1;
-      if (t + 2 * G < nt) fill_w(t + 2 * G, c0);
-      if (t + G < nt) fill_x(t + G, c1);
-      if (t + G < nt && active) mma(c1, acc1);
-      if (active) {
-        TileBuf<uint16_t> x;
-        read_x(c0, x);
-        epilogue_tile<uint16_t, RESIDUAL>(a, acc0, x, trow, rq, pos, valid, T, t, half, full_tile(t));
-      }
-      wait_vmcnt(0);
-      __syncthreads();
-      t += G, ++i;
-      if (t >= nt) break;
-    }
-    // tile t = t_i with accumulators acc1
-    {
-      const int c0 = i & 1, c1 = c0 ^ 1;
-      if (t + 2 * G < nt) fill_w(t + 2 * G, c0);
-      if (t + G < nt) fill_x(t + G, c1);
-      if (t + G < nt && active) mma(c1, acc0);
-      if (active) {
-        TileBuf<uint16_t> x;
-        read_x(c0, x);
-        epilogue_tile<uint16_t, RESIDUAL>(a, acc1, x, trow, rq, pos, valid, T, t, half, full_tile(t));
-      }
-      wait_vmcnt(0);
-      __syncthreads();
-      t += G, ++i;
-      if (t >= nt) break;
-    }
+    step(0, acc0, acc1);
+    if (t >= nt) break;
+    step(1, acc1, acc0);
+    if (t >= nt) break;
   }
 }
 
-template <bool RESIDUAL, int R>
-hipError_t launch_coalesced(const GemmArgs& a, hipStream_t s) {
+template <int R>
+hipError_t launch_residual_coalesced(const GemmArgs& a, hipStream_t s) {
   static int max_wg = 0;
-  const size_t lds = (size_t)2 * (kTile * R * 2) + (size_t)2 * (kSlotsPerGroup * kTile * 2);
-  const void* fn = reinterpret_cast<const void*>(&gemm_stats_coalesced<RESIDUAL, R>);
+  const size_t lds = (size_t)2 * (kTile * R * 2) + (size_t)4 * (kResSlots * kTile * 2);
+  const void* fn = reinterpret_cast<const void*>(&gemm_residual_coalesced<R>);
   if (!max_wg) {
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return hipErrorUnknown;
-    if (lds > 64 * 1024 && hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
       return hipErrorUnknown;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64 * kLdsWaves, lds) != hipSuccess || per_cu < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 512, lds) != hipSuccess || per_cu < 1)
       per_cu = 1;
     max_wg = cus * per_cu;
   }
-  const int groups = (a.B + kSlotsPerGroup - 1) / kSlotsPerGroup;
-  const int wg_x = max(1, min(a.n_tiles, max_wg / groups));
-  gemm_stats_coalesced<RESIDUAL, R><<<dim3(wg_x, groups), 64 * kLdsWaves, lds, s>>>(a);
+  // enough workgroups to give every CU one, and at least one per tile of every
+  // possible slot group when the batch is small
+  const int groups = (a.B + kResSlots - 1) / kResSlots;
+  const int grid = max(8, min(max_wg, groups * a.n_tiles));
+  gemm_residual_coalesced<R><<<grid, 512, lds, s>>>(a);
   return hipGetLastError();
 }
 
@@ -907,9 +1224,17 @@ hipError_t launch_pipelined(const GemmArgs& a, hipStream_t s) {
 template <typename TL, bool RESIDUAL>
 hipError_t gemm_dispatch(const GemmArgs& a, int factor_dtype, bool vec, hipStream_t s) {
   if constexpr (sizeof(TL) == 2) {
-    if (factor_dtype == DSPARK_BF16 && a.V % 8 == 0 && a.V >= 64 && (a.r == 128 || a.r == 256)) {
-      if (a.r == 256) return launch_coalesced<RESIDUAL, 256>(a, s);
-      return launch_coalesced<RESIDUAL, 128>(a, s);
+    // the coalesced kernels address their inputs with 32-bit byte offsets
+    const bool fits = (size_t)a.B * (a.gamma + 1) * a.V * 2 < (1ull << 32) &&
+                      (size_t)a.V * a.r * 2 < (1ull << 32) && (size_t)a.B * a.n_tiles * 16 < (1ull << 32);
+    if (factor_dtype == DSPARK_BF16 && a.V % 8 == 0 && a.V >= 64 && (a.r == 128 || a.r == 256) && fits) {
+      if constexpr (RESIDUAL) {
+        if (a.r == 256) return launch_residual_coalesced<256>(a, s);
+        return launch_residual_coalesced<128>(a, s);
+      } else {
+        if (a.r == 256) return launch_coalesced<256>(a, s);
+        return launch_coalesced<128>(a, s);
+      }
     }
   }
   if (factor_dtype == DSPARK_BF16 && vec && (a.r == 64 || a.r == 128 || a.r == 256)) {

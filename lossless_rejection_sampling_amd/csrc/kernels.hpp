@@ -109,6 +109,9 @@ struct ScheduleArgs {
   int n_points, B, gamma;
   int32_t* budget;
   uint32_t* status;
+  int32_t* rank;       // [B * gamma] position of each candidate in the admission order
+  uint32_t* ticket;    // workgroups finished (returns to 0)
+  uint32_t* stop_enc;  // first failing position m as 0x7fffffff - m, 0 if none (returns to 0)
 };
 
 hipError_t launch_schedule(const ScheduleArgs& a, hipStream_t s);

@@ -3,16 +3,19 @@
 // tau * SPS(B), candidates admitted in decreasing a while Theta grows, with an
 // early stop at the first candidate that does not raise it).
 //
-// One workgroup of 1024 threads:
-//   1. a lane per request forms the prefix products in fp32, left to right,
-//      and the integer keys Q = floor(a * 2^32);
-//   2. the (Q desc, request asc, position asc) keys are sorted in LDS
-//      (bitonic network);
-//   3. every thread owns a run of consecutive sorted candidates: an integer
-//      scan gives tau before each candidate exactly, so the admission test of
-//      every candidate is evaluated at once, in fp64 in the stated order;
-//   4. the first failing candidate ends the admitted prefix; budgets count the
-//      admitted candidates of each request.
+// The admitted prefix is found without sorting.  The position (rank) m of a
+// candidate in the order (Q desc, request asc, position asc) is the number of
+// keys ordered before it, and tau_m - B 2^32 is the sum of their Q; both come
+// from one pass over all keys, in exact integer arithmetic, so the admission
+// test of every candidate is evaluated independently:
+//   1. every workgroup forms all keys in LDS (a lane per request: fp32 prefix
+//      products left to right, Q = floor(a * 2^32)) and the step-time table;
+//   2. 16 lanes per candidate count and sum the keys before it, the test runs in
+//      fp64 in the stated order, and a failing candidate lowers the device-wide
+//      first failure (an atomic max of kNoFail - m);
+//   3. ranks go to the workspace; the last workgroup to finish (a ticket
+//      counter) sets budget[b] = number of b's candidates ranked before the
+//      first failure, and resets the counter and the failure word.
 #include <math.h>
 
 #include "dspark.h"
@@ -21,15 +24,16 @@
 namespace dspark {
 namespace {
 
-constexpr int kThreads = 1024;
-constexpr int kMaxKeys = 8192;
-constexpr int kMaxPoints = 1024;
+constexpr int kThreads = 256;
+constexpr int kLanesPerCand = 16;
+constexpr int kCandPerGroup = kThreads / kLanesPerCand;
+constexpr uint32_t kNoFail = 0x7fffffffu;
 
 #pragma clang fp contract(off)
 
 // 1/SPS at a verify batch of N tokens (see the ABI header for the rule), from
-// the table held in LDS: batch sizes Bs and step times ts = 1/SPS.  The
-// segment is the last i <= np-2 with Bs[i] <= N (binary search).
+// the table in LDS: batch sizes Bs and step times ts = 1/SPS.  The segment is
+// the last i <= np-2 with Bs[i] <= N (binary search).
 __device__ double step_time(double N, const double* Bs, const double* ts, int np) {
   if (N <= Bs[0]) return ts[0];
   int lo = 0, hi = np - 2;
@@ -45,14 +49,13 @@ __device__ double step_time(double N, const double* Bs, const double* ts, int np
 }
 
 __global__ __launch_bounds__(kThreads) void schedule_kernel(ScheduleArgs a) {
-  __shared__ unsigned long long keys[kMaxKeys];
-  __shared__ unsigned long long part[kThreads];
-  __shared__ double tB[kMaxPoints], tT[kMaxPoints];
-  __shared__ int first_fail;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  __shared__ int s_last;
   const int tid = threadIdx.x, B = a.B, gamma = a.gamma, np = a.n_points;
   const int nk = B * gamma;
-  int M = 1;
-  while (M < nk) M <<= 1;
+  uint32_t* const qinv = reinterpret_cast<uint32_t*>(smem);  // 0xFFFFFFFF - Q, candidate b * gamma + j
+  double* const tB = reinterpret_cast<double*>(smem + ((nk * 4 + 15) & ~15));
+  double* const tT = tB + np;
 
   for (int i = tid; i < np; i += kThreads) {
     tB[i] = a.sps_B[i];
@@ -60,81 +63,76 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(ScheduleArgs a) {
   }
   bool bad = false;
   for (int b = tid; b < B; b += kThreads) {
-    float c[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) c[j] = j < gamma ? a.conf[(size_t)b * gamma + j] : 0.5f;
     float acc = 1.0f;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      if (j >= gamma) break;
-      float cj = c[j];
+    for (int j = 0; j < gamma; ++j) {
+      float cj = a.conf[(size_t)b * gamma + j];
       if (!(cj > 0.0f && cj < 1.0f)) {
         bad = true;
         cj = cj > 0.0f ? 0x1.fffffep-1f : 0x1p-126f;  // clamp into (0, 1); NaN -> tiny
       }
       acc = acc * cj;
-      const unsigned long long q = (unsigned long long)floor((double)acc * 4294967296.0);
-      keys[b * gamma + j] = ((0xFFFFFFFFull - q) << 32) | ((unsigned long long)b << 4) | (unsigned)j;
+      const uint32_t q = (uint32_t)floor((double)acc * 4294967296.0);
+      qinv[b * gamma + j] = 0xFFFFFFFFu - q;
     }
   }
-  if (bad) flag_status(a.status, kBadConf);
-  for (int i = nk + tid; i < M; i += kThreads) keys[i] = ~0ull;
-  if (tid == 0) first_fail = nk;
-  for (int b = tid; b < B; b += kThreads) a.budget[b] = 0;
+  if (bad && blockIdx.x == 0) flag_status(a.status, kBadConf);
+  __syncthreads();
+
+  // candidate i: keys before it and the sum of their Q
+  const int i = blockIdx.x * kCandPerGroup + (tid / kLanesPerCand), sub = tid % kLanesPerCand;
+  uint32_t cnt = 0;
+  unsigned long long tau = 0;
+  const uint32_t qi = i < nk ? qinv[i] : 0u;
+  if (i < nk) {
+    for (int k = sub; k < nk; k += kLanesPerCand) {
+      const uint32_t qk = qinv[k];
+      const bool before = qk < qi || (qk == qi && k < i);
+      cnt += before ? 1u : 0u;
+      tau += before ? (unsigned long long)(0xFFFFFFFFu - qk) : 0ull;
+    }
+  }
+#pragma unroll
+  for (int o = 1; o < kLanesPerCand; o <<= 1) {
+    cnt += __shfl_xor(cnt, o);
+    tau += __shfl_xor(tau, o);
+  }
+  if (i < nk && sub == 0) {
+    const unsigned long long q = 0xFFFFFFFFull - qi;
+    const unsigned long long T = ((unsigned long long)B << 32) + tau;
+    const double N = (double)(B + (int)cnt);
+    const double lhs = (double)(T + q) * step_time(N, tB, tT, np);
+    const double rhs = (double)T * step_time(N + 1.0, tB, tT, np);
+    if (!(lhs > rhs)) atomicMax(a.stop_enc, kNoFail - cnt);
+    a.rank[i] = (int)cnt;
+  }
+
+  // the last workgroup to finish turns ranks into budgets
   __threadfence();
   __syncthreads();
-
-  for (int k = 2; k <= M; k <<= 1) {
-    for (int jj = k >> 1; jj > 0; jj >>= 1) {
-      for (int i = tid; i < M; i += kThreads) {
-        const int ixj = i ^ jj;
-        if (ixj > i) {
-          const unsigned long long x = keys[i], y = keys[ixj];
-          const bool up = (i & k) == 0;
-          if ((x > y) == up) keys[i] = y, keys[ixj] = x;
-        }
-      }
-      __syncthreads();
-    }
-  }
-
-  // thread tid owns sorted candidates [lo, hi)
-  const int per = (nk + kThreads - 1) / kThreads;
-  const int lo = min(tid * per, nk), hi = min(lo + per, nk);
-  unsigned long long local = 0;
-  for (int i = lo; i < hi; ++i) local += 0xFFFFFFFFull - (keys[i] >> 32);
-  part[tid] = local;
+  if (tid == 0) s_last = atomicAdd(a.ticket, 1u) == gridDim.x - 1;
   __syncthreads();
-  for (int o = 1; o < kThreads; o <<= 1) {  // inclusive scan of the thread sums
-    const unsigned long long v = tid >= o ? part[tid - o] : 0ull;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  const uint32_t enc = __hip_atomic_load(a.stop_enc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int stop = enc ? (int)(kNoFail - enc) : nk;
+  for (int b = tid; b < B; b += kThreads) {
+    int n = 0;
+    for (int j = 0; j < gamma; ++j) n += __builtin_nontemporal_load(a.rank + b * gamma + j) < stop ? 1 : 0;
+    a.budget[b] = n;
   }
-  unsigned long long tau = ((unsigned long long)B << 32) + part[tid] - local;
-  for (int i = lo; i < hi; ++i) {
-    const unsigned long long q = 0xFFFFFFFFull - (keys[i] >> 32);
-    const double N = (double)(B + i);
-    const double lhs = (double)(tau + q) * step_time(N, tB, tT, np);
-    const double rhs = (double)tau * step_time(N + 1.0, tB, tT, np);
-    if (!(lhs > rhs)) {
-      atomicMin(&first_fail, i);
-      break;
-    }
-    tau += q;
-  }
-  __syncthreads();
-  const int stop = first_fail;
-  for (int i = tid; i < stop; i += kThreads) {
-    const int b = (int)((keys[i] >> 4) & 0x0FFFFFFFull);
-    atomicAdd(&a.budget[b], 1);
+  if (tid == 0) {
+    __hip_atomic_store(a.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(a.stop_enc, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
 }  // namespace
 
 hipError_t launch_schedule(const ScheduleArgs& a, hipStream_t s) {
-  schedule_kernel<<<1, kThreads, 0, s>>>(a);
+  const int nk = a.B * a.gamma;
+  const size_t lds = (size_t)((nk * 4 + 15) & ~15) + (size_t)a.n_points * 16;
+  const int groups = (nk + kCandPerGroup - 1) / kCandPerGroup;
+  schedule_kernel<<<groups, kThreads, lds, s>>>(a);
   return hipGetLastError();
 }
 

@@ -39,6 +39,7 @@ _SIG = {
     "dspark_abi_version": (_I, []),
     "dspark_error_string": (ctypes.c_char_p, [_I]),
     "dspark_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
+    "dspark_schedule_workspace_bytes": (ctypes.c_size_t, [_I, _I]),
     "dspark_draft_round": (_I, [_P, _I, _P, _P, _I, _P, _P, ctypes.c_uint64, _P,
                                 _I, _I, _I, _I, _P, _P, _P, _P, _P]),
     "dspark_schedule": (_I, [_P, _P, _P, _I, _I, _I, _P, _P, _P]),
@@ -116,6 +117,10 @@ def dspark_abi_version() -> int:
 
 def dspark_workspace_bytes(B: int, gamma: int, V: int, r: int) -> int:
     return int(lib().dspark_workspace_bytes(B, gamma, V, r))
+
+
+def dspark_schedule_workspace_bytes(B: int, gamma: int) -> int:
+    return int(lib().dspark_schedule_workspace_bytes(B, gamma))
 
 
 def dspark_draft_round(base_logits, U, W, prev0, temperature, seed, pos_offset,

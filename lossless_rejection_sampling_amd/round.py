@@ -72,7 +72,19 @@ def verify(rnd: Round, buf: Buffers, stream=None):
                      buf.debug_logp_logq, buf.debug_residual, stream)
 
 
-def run_round(rnd: Round, buf: Buffers, stream=None):
-    draft(rnd, buf, stream)
-    schedule(rnd, buf, stream)
-    verify(rnd, buf, stream)
+def run_round(rnd: Round, buf: Buffers, stream=None, side_stream=None):
+    """One round on ``stream`` (default: the current stream).  With a
+    ``side_stream`` the scheduler, which reads only the confidence scores, runs
+    there concurrently with drafting, and verification waits for it."""
+    main = torch.cuda.current_stream() if stream is None else stream
+    if side_stream is not None and rnd.scheduled:
+        side_stream.wait_stream(main)
+        schedule(rnd, buf, side_stream)
+        done = torch.cuda.Event()
+        done.record(side_stream)
+        draft(rnd, buf, main)
+        main.wait_event(done)
+    else:
+        draft(rnd, buf, main)
+        schedule(rnd, buf, main)
+    verify(rnd, buf, main)

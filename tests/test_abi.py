@@ -25,7 +25,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_error_strings(lib):
-    assert ds.dspark_abi_version() == 1
+    assert ds.dspark_abi_version() == 2
     assert ds.error_string(0) == "ok"
     assert "argument" in ds.error_string(-1)
     assert "device" in ds.error_string(-3)
@@ -39,6 +39,13 @@ def test_workspace_size_rules(lib):
     assert ds.dspark_workspace_bytes(4, 5, 0, 8) == 0
     small = ds.dspark_workspace_bytes(4, 4, 1024, 16)
     assert small % 256 == 0 and small < ds.dspark_workspace_bytes(8, 4, 1024, 16)
+    # the scheduler's own part: header + one int per candidate, within the full workspace
+    assert ds.dspark_schedule_workspace_bytes(256, 5) == 256 + 256 * 5 * 4
+    assert ds.dspark_schedule_workspace_bytes(1024, 8) == 256 + 1024 * 8 * 4
+    assert ds.dspark_schedule_workspace_bytes(1024, 9) == 0      # B * gamma > 8192
+    assert ds.dspark_schedule_workspace_bytes(0, 4) == 0
+    for B, g, V, r in [(1, 1, 8, 1), (7, 16, 65, 20), (256, 5, 151936, 256)]:
+        assert ds.dspark_schedule_workspace_bytes(B, g) <= ds.dspark_workspace_bytes(B, g, V, r)
 
 
 def test_host_argument_checks_return_einval(lib):

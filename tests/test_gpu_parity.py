@@ -108,7 +108,7 @@ def test_scheduler_bit_exact():
         g = torch.Generator(device=DEV).manual_seed(seed)
         conf = wl.confidence_scores(B, gamma, g, DEV)
         budget = torch.empty(B, dtype=torch.int32, device=DEV)
-        ws = torch.zeros(4096, dtype=torch.uint8, device=DEV)
+        ws = torch.zeros(ds.dspark_schedule_workspace_bytes(B, gamma), dtype=torch.uint8, device=DEV)
         ds.dspark_schedule(conf, torch.tensor(Bs, device=DEV), torch.tensor(sps, device=DEV), budget, ws)
         ref = od.schedule(conf.cpu().numpy(), Bs, sps)
         assert ref.min_gap > od.SCHED_FLAG
@@ -116,7 +116,7 @@ def test_scheduler_bit_exact():
     # special tables: constant rate admits every candidate with Q > 0; t ~ N admits none
     conf = torch.full((64, 4), 0.5, device=DEV)
     budget = torch.empty(64, dtype=torch.int32, device=DEV)
-    ws = torch.zeros(4096, dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(ds.dspark_schedule_workspace_bytes(64, 4), dtype=torch.uint8, device=DEV)
     ds.dspark_schedule(conf, torch.tensor([1.0, 1024.0], device=DEV, dtype=torch.float64),
                        torch.tensor([50.0, 50.0], device=DEV, dtype=torch.float64), budget, ws)
     assert torch.all(budget == 4)
