@@ -103,34 +103,121 @@ __device__ __forceinline__ double gumbel(uint64_t seed, uint32_t stream, uint32_
 }
 
 // ---------------------------------------------------------------------------
-// 64-lane reductions (every lane receives the result).
+// Lane exchanges without LDS.  Inside a row of 16 lanes: DPP quad permutes
+// (lane ^ 1, lane ^ 2) and the mirrors (lane i <-> 7 - i within 8, 15 - i within
+// 16).  Across rows: gfx950's v_permlane16_swap / v_permlane32_swap; swapping a
+// register with itself returns, in both results, the even and the odd row (row
+// pair) of each pair, so op(first, second) is the pairwise result.  Each step of
+// a reduction combines two values that are identical in the two lanes it joins,
+// so every lane ends with the bitwise same result; a 16-lane reduction is four
+// dependent VALU moves, a 64-lane one six.
 // ---------------------------------------------------------------------------
-template <typename T> __device__ __forceinline__ T wave_max(T v) {
-#pragma unroll
-  for (int o = 32; o; o >>= 1) v = fmax(v, __shfl_xor(v, o));
-  return v;
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+template <int CTRL> __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
 }
-template <typename T> __device__ __forceinline__ T wave_sum(T v) {
-#pragma unroll
-  for (int o = 32; o; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+template <typename T> __device__ __forceinline__ uint64_t to_bits(T v) {
+  if constexpr (sizeof(T) == 8) return __builtin_bit_cast(uint64_t, v);
+  else return (uint64_t)__builtin_bit_cast(uint32_t, v);
 }
-__device__ __forceinline__ int wave_min_int(int v) {
-#pragma unroll
-  for (int o = 32; o; o >>= 1) v = min(v, __shfl_xor(v, o));
-  return v;
+template <typename T> __device__ __forceinline__ T from_bits(uint64_t b) {
+  if constexpr (sizeof(T) == 8) return __builtin_bit_cast(T, b);
+  else return __builtin_bit_cast(T, (uint32_t)b);
 }
-// Largest value; among equal values the lowest index.
-__device__ __forceinline__ void wave_argmax(double& v, int& i) {
-#pragma unroll
-  for (int o = 32; o; o >>= 1) {
-    const double ov = __shfl_xor(v, o);
-    const int oi = __shfl_xor(i, o);
-    if (ov > v || (ov == v && oi < i)) {
-      v = ov;
-      i = oi;
-    }
+template <int CTRL, typename T> __device__ __forceinline__ T dpp(T v) {
+  const uint64_t b = to_bits(v);
+  uint64_t r = dpp_u32<CTRL>((uint32_t)b);
+  if constexpr (sizeof(T) == 8) r |= (uint64_t)dpp_u32<CTRL>((uint32_t)(b >> 32)) << 32;
+  return from_bits<T>(r);
+}
+// (value of the even row of the pair, value of the odd row), rows of 16 (W = 16)
+// or halves of 32 (W = 32)
+template <int W, typename T> __device__ __forceinline__ void row_pair(T v, T& even, T& odd) {
+  const uint64_t b = to_bits(v);
+  uint64_t e, o;
+  {
+    const auto r = W == 16 ? __builtin_amdgcn_permlane16_swap((uint32_t)b, (uint32_t)b, false, false)
+                           : __builtin_amdgcn_permlane32_swap((uint32_t)b, (uint32_t)b, false, false);
+    e = r[0], o = r[1];
   }
+  if constexpr (sizeof(T) == 8) {
+    const uint32_t hi = (uint32_t)(b >> 32);
+    const auto r = W == 16 ? __builtin_amdgcn_permlane16_swap(hi, hi, false, false)
+                           : __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    e |= (uint64_t)r[0] << 32, o |= (uint64_t)r[1] << 32;
+  }
+  even = from_bits<T>(e), odd = from_bits<T>(o);
+}
+
+template <typename T, typename Op> __device__ __forceinline__ T reduce16(T v, Op op) {
+  v = op(v, dpp<kDppXor1>(v));
+  v = op(v, dpp<kDppXor2>(v));
+  v = op(v, dpp<kDppHalfMirror>(v));
+  v = op(v, dpp<kDppMirror>(v));
+  return v;
+}
+template <typename T, typename Op> __device__ __forceinline__ T reduce64(T v, Op op) {
+  v = reduce16(v, op);
+  T e, o;
+  row_pair<16>(v, e, o);
+  v = op(e, o);
+  row_pair<32>(v, e, o);
+  return op(e, o);
+}
+// lane and lane ^ 32 combined
+template <typename T, typename Op> __device__ __forceinline__ T reduce_pair32(T v, Op op) {
+  T e, o;
+  row_pair<32>(v, e, o);
+  return op(e, o);
+}
+
+struct OpMax {
+  template <typename T> __device__ __forceinline__ T operator()(T a, T b) const {
+    if constexpr (sizeof(T) == 8 && __is_same(T, double)) return fmax(a, b);
+    else if constexpr (__is_same(T, float)) return fmaxf(a, b);
+    else return a > b ? a : b;
+  }
+};
+struct OpMin {
+  template <typename T> __device__ __forceinline__ T operator()(T a, T b) const { return a < b ? a : b; }
+};
+struct OpSum {
+  template <typename T> __device__ __forceinline__ T operator()(T a, T b) const { return a + b; }
+};
+
+// 64-lane reductions (every lane receives the result).
+template <typename T> __device__ __forceinline__ T wave_max(T v) { return reduce64(v, OpMax{}); }
+template <typename T> __device__ __forceinline__ T wave_sum(T v) { return reduce64(v, OpSum{}); }
+__device__ __forceinline__ int wave_min_int(int v) { return reduce64(v, OpMin{}); }
+// 16-lane reductions (rows of 16 lanes)
+template <typename T> __device__ __forceinline__ T group16_max(T v) { return reduce16(v, OpMax{}); }
+template <typename T> __device__ __forceinline__ T group16_sum(T v) { return reduce16(v, OpSum{}); }
+
+// Largest value; among equal values the lowest index.  Value and index travel
+// together, so the pair reduction is the same total order in every lane.
+struct ArgMax {
+  double v;
+  int i;
+};
+__device__ __forceinline__ ArgMax argmax_op(ArgMax a, ArgMax b) {
+  return (b.v > a.v || (b.v == a.v && b.i < a.i)) ? b : a;
+}
+template <int CTRL> __device__ __forceinline__ ArgMax dpp_argmax(ArgMax a) {
+  return ArgMax{dpp<CTRL>(a.v), dpp<CTRL>(a.i)};
+}
+__device__ __forceinline__ void wave_argmax(double& v, int& i) {
+  ArgMax a{v, i};
+  a = argmax_op(a, dpp_argmax<kDppXor1>(a));
+  a = argmax_op(a, dpp_argmax<kDppXor2>(a));
+  a = argmax_op(a, dpp_argmax<kDppHalfMirror>(a));
+  a = argmax_op(a, dpp_argmax<kDppMirror>(a));
+  ArgMax e, o;
+  row_pair<16>(a.v, e.v, o.v), row_pair<16>(a.i, e.i, o.i);
+  a = argmax_op(e, o);
+  row_pair<32>(a.v, e.v, o.v), row_pair<32>(a.i, e.i, o.i);
+  a = argmax_op(e, o);
+  v = a.v, i = a.i;
 }
 
 __device__ __forceinline__ void flag_status(uint32_t* status, uint32_t bit) {

@@ -533,17 +533,25 @@ template <typename TF>
 __device__ __forceinline__ double dot_part(const TF* h, const TF* w, int k0, int k1) {
   double acc = 0.0;
   if constexpr (sizeof(TF) == 2) {
-    if (((k1 - k0) & 7) == 0 && (k0 & 7) == 0) {
-      for (int k = k0; k < k1; k += 8) {
-        const uint4 hv = *reinterpret_cast<const uint4*>(h + k);
-        const uint4 wv = *reinterpret_cast<const uint4*>(w + k);
-        const uint32_t hh[4] = {hv.x, hv.y, hv.z, hv.w}, ww[4] = {wv.x, wv.y, wv.z, wv.w};
+    if (((k1 - k0) & 7) == 0 && (k0 & 7) == 0 && k1 - k0 <= 64) {
+      // every load first, then the products (one memory round trip)
+      uint4 hv[8], wv[8];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          acc += (double)__uint_as_float(hh[q] << 16) * (double)__uint_as_float(ww[q] << 16);
-          acc += (double)__uint_as_float(hh[q] & 0xffff0000u) * (double)__uint_as_float(ww[q] & 0xffff0000u);
+      for (int i = 0; i < 8; ++i)
+        if (k0 + 8 * i < k1) {
+          hv[i] = *reinterpret_cast<const uint4*>(h + k0 + 8 * i);
+          wv[i] = *reinterpret_cast<const uint4*>(w + k0 + 8 * i);
         }
-      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (k0 + 8 * i < k1) {
+          const uint32_t hh[4] = {hv[i].x, hv[i].y, hv[i].z, hv[i].w}, ww[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            acc += (double)__uint_as_float(hh[q] << 16) * (double)__uint_as_float(ww[q] << 16);
+            acc += (double)__uint_as_float(hh[q] & 0xffff0000u) * (double)__uint_as_float(ww[q] & 0xffff0000u);
+          }
+        }
       return acc;
     }
   }
@@ -551,10 +559,16 @@ __device__ __forceinline__ double dot_part(const TF* h, const TF* w, int k0, int
   return acc;
 }
 
+// Draw of block position `pos` for request b = blockIdx.x from the tile
+// records (three-level exact Gumbel-max: block, tile, column), then the fp64
+// recompute of the chosen tile for the token and its log-probability.
 template <typename TL, typename TF>
 __global__ __launch_bounds__(256) void draft_select_kernel(DraftSelectArgs a) {
-  __shared__ double s_val[4], s_m[4], s_s[4], s_part[4][64];
-  __shared__ int s_idx[4];
+  constexpr int kGroup = 64;  // blocks whose statistics are gathered per pass
+  __shared__ double s_bm[kGroup], s_part[4][64];
+  __shared__ float s_be[kGroup];
+  __shared__ double s_val[4], s_lse;
+  __shared__ int s_idx[4], s_tile;
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int V = a.V, r = a.r, gamma = a.gamma, nt = a.n_tiles, pos = a.pos;
   const uint32_t rpos = (uint32_t)(pos + 1 + (a.pos_offset ? a.pos_offset[b] : 0));
@@ -572,78 +586,80 @@ __global__ __launch_bounds__(256) void draft_select_kernel(DraftSelectArgs a) {
   if (Tf > 0.0f) {
     invT = 1.0 / (double)Tf;
     const double mref = (double)ts[0].ref + (double)ts[0].mx;
+    // wavefront 0, lane j: running choice and log-sum-exp over the groups
     double best = -INFINITY, row_m = -INFINITY, row_s = 0.0;
     int best_blk = 0x7fffffff;
-    // Chunks of 16 blocks (1024 tile records): thread tid reads the records of
-    // tiles 4 tid .. 4 tid + 3 of the chunk, so the 16 lanes 16 k .. 16 k + 15
-    // of a wavefront hold one block; its max and mass reduce within those
-    // lanes.  The first lane of each block keeps the running Gumbel-max choice
-    // (blocks in increasing order, so ties keep the lowest) and the running
-    // log-sum-exp.
-    for (int c = 0; c < nblk; c += 16) {
-      const int blk = c + wave * 4 + (lane >> 4);
-      const int tb = c * kTilesPerBlock + 4 * tid;
-      double d[4];
-      float sm[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (tb + q < nt) {
-          const TileStat st = ts[tb + q];
-          d[q] = (double)st.ref + (double)st.mx, sm[q] = st.sum;
-        } else {
-          d[q] = -INFINITY, sm[q] = 0.0f;
-        }
-      }
-      double m = fmax(fmax(d[0], d[1]), fmax(d[2], d[3]));
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) m = fmax(m, __shfl_xor(m, o));
-      float e = 0.0f;
+    for (int g0 = 0; g0 < nblk; g0 += kGroup) {
+      // Records of 4 chunks of 16 blocks, all requested at once: thread tid
+      // holds tiles 4 tid .. 4 tid + 3 of each chunk, so the 16 lanes
+      // 16 k .. 16 k + 15 of a wavefront hold one block, whose max and mass
+      // (relative to that max) reduce within those lanes.
+      double d[4][4];
+      float sm[4][4];
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        if (sm[q] > 0.0f) e += sm[q] * expf((float)((d[q] - m) * invT));
 #pragma unroll
-      for (int o = 1; o < 16; o <<= 1) e += __shfl_xor(e, o);
-      if ((lane & 15) == 0 && blk < nblk) {
-        const double val = (m - mref) * invT + log((double)e) + gumbel(a.seed, kDraftTop, b, rpos, blk);
-        if (val > best) best = val, best_blk = blk;
-        if (m > row_m) {
-          row_s = row_s * exp((row_m - m) * invT) + (double)e;
-          row_m = m;
+        for (int k = 0; k < 4; ++k) {
+          const int t = (g0 + 16 * q) * kTilesPerBlock + 4 * tid + k;
+          if (t < nt) {
+            const TileStat st = ts[t];
+            d[q][k] = (double)st.ref + (double)st.mx, sm[q][k] = st.sum;
+          } else {
+            d[q][k] = -INFINITY, sm[q][k] = 0.0f;
+          }
+        }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        double m = fmax(fmax(d[q][0], d[q][1]), fmax(d[q][2], d[q][3]));
+        m = group16_max(m);
+        float e = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (sm[q][k] > 0.0f) e += sm[q][k] * expf((float)((d[q][k] - m) * invT));
+        e = group16_sum(e);
+        const int j = 16 * q + 4 * wave + (lane >> 4);
+        if ((lane & 15) == 0 && g0 + j < nblk) s_bm[j] = m, s_be[j] = e;
+      }
+      __syncthreads();
+      if (wave == 0) {  // lane j: block g0 + j
+        const int blk = g0 + lane;
+        double val = -INFINITY, m = -INFINITY, e = 0.0;
+        int idx = 0x7fffffff;
+        if (blk < nblk) {
+          m = s_bm[lane], e = (double)s_be[lane];
+          val = (m - mref) * invT + log(e) + gumbel(a.seed, kDraftTop, b, rpos, blk);
+          idx = blk;
+        }
+        wave_argmax(val, idx);
+        if (val > best) best = val, best_blk = idx;  // groups in increasing order: ties keep the lowest
+        const double gm = wave_max(m);
+        const double gs = wave_sum(e > 0.0 ? e * exp((m - gm) * invT) : 0.0);
+        if (gm > row_m) {
+          row_s = row_s * exp((row_m - gm) * invT) + gs;
+          row_m = gm;
         } else {
-          row_s += (double)e * exp((m - row_m) * invT);
+          row_s += gs * exp((gm - row_m) * invT);
         }
       }
+      __syncthreads();
     }
-    wave_argmax(best, best_blk);
-    {
-      const double m = wave_max(row_m);
-      row_s = wave_sum(row_s > 0.0 ? row_s * exp((row_m - m) * invT) : 0.0);
-      row_m = m;
+    // tile inside the chosen block (its records were just read: an L2 hit)
+    if (wave == 0) {
+      const int blk = index_or(best_blk, nblk, 0);
+      const int t0 = blk * kTilesPerBlock, t1 = min(t0 + kTilesPerBlock, nt);
+      double val = -INFINITY;
+      int ti = 0x7fffffff;
+      if (t0 + lane < t1) {
+        const TileStat st = ts[t0 + lane];
+        val = ((double)st.ref + (double)st.mx - mref) * invT + log((double)st.sum) +
+              gumbel(a.seed, kDraftMid, b, rpos, lane);
+        ti = t0 + lane;
+      }
+      wave_argmax(val, ti);
+      if (lane == 0) s_tile = index_or(ti, t1, t0), s_lse = row_m * invT + log(row_s);
     }
-    if (lane == 0) s_val[wave] = best, s_idx[wave] = best_blk, s_m[wave] = row_m, s_s[wave] = row_s;
     __syncthreads();
-    double M = -INFINITY;
-    for (int w = 0; w < 4; ++w) M = fmax(M, s_m[w]);
-    double S = 0.0;
-    for (int w = 0; w < 4; ++w)
-      if (s_s[w] > 0.0) S += s_s[w] * exp((s_m[w] - M) * invT);
-    lse = M * invT + log(S);
-    best = -INFINITY, best_blk = 0x7fffffff;
-    for (int w = 0; w < 4; ++w)
-      if (s_val[w] > best || (s_val[w] == best && s_idx[w] < best_blk)) best = s_val[w], best_blk = s_idx[w];
-    best_blk = index_or(best_blk, nblk, 0);
-    // tile inside the chosen block (every wavefront computes the same choice)
-    const int t0 = best_blk * kTilesPerBlock, t1 = min(t0 + kTilesPerBlock, nt);
-    double val = -INFINITY;
-    int ti = 0x7fffffff;
-    if (t0 + lane < t1) {
-      const TileStat st = ts[t0 + lane];
-      val = ((double)st.ref + (double)st.mx - mref) * invT + log((double)st.sum) +
-            gumbel(a.seed, kDraftMid, b, rpos, lane);
-      ti = t0 + lane;
-    }
-    wave_argmax(val, ti);
-    tile = index_or(ti, t1, t0);
+    tile = s_tile, lse = s_lse;
   } else {
     double best = -INFINITY;
     int bt = 0x7fffffff;
@@ -660,8 +676,10 @@ __global__ __launch_bounds__(256) void draft_select_kernel(DraftSelectArgs a) {
     tile = index_or(bt, nt, 0);
   }
 
-  // recompute the chosen tile in fp64: the rank is split over the wavefronts
+  // recompute the chosen tile in fp64: the rank is split over the wavefronts;
+  // the backbone logit is requested with the factor rows
   const int v = tile * kTile + lane;
+  const double xb = (wave == 0 && v < V) ? (double)load_logit(brow + v) : 0.0;
   const int kq = (r + 3) / 4, k0 = min(wave * kq, r), k1 = min(k0 + kq, r);
   s_part[wave][lane] = v < V ? dot_part<TF>(h, Wt + (size_t)v * r, k0, k1) : 0.0;
   __syncthreads();
@@ -669,8 +687,7 @@ __global__ __launch_bounds__(256) void draft_select_kernel(DraftSelectArgs a) {
     double lv = -INFINITY, sv = -INFINITY;
     int vi = 0x7fffffff;
     if (v < V) {
-      const double d = (double)load_logit(brow + v) + ((s_part[0][lane] + s_part[1][lane]) +
-                                                       (s_part[2][lane] + s_part[3][lane]));
+      const double d = xb + ((s_part[0][lane] + s_part[1][lane]) + (s_part[2][lane] + s_part[3][lane]));
       if (Tf > 0.0f) {
         sv = d / (double)Tf;
         lv = sv + gumbel(a.seed, kDraftLeaf, b, rpos, lane);
@@ -699,18 +716,9 @@ __global__ __launch_bounds__(256) void draft_select_kernel(DraftSelectArgs a) {
 // backbone logits of the 256 slots, reach LDS by direct loads of whole rows
 // into two-slot rings (layouts below); one barrier per tile.
 // ---------------------------------------------------------------------------
-// Reduction with the partner lane (lane ^ 32) through v_permlane32_swap: the
-// swap of a register with itself returns the low half of the wave in both
-// halves of the first result and the high half in both halves of the second,
-// so op(first, second) is the pairwise result, identical in both lanes.
-__device__ __forceinline__ float pair_max(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_sum(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
+// Reductions with the partner lane (lane ^ 32), identical in both lanes.
+__device__ __forceinline__ float pair_max(float v) { return reduce_pair32(v, OpMax{}); }
+__device__ __forceinline__ float pair_sum(float v) { return reduce_pair32(v, OpSum{}); }
 
 // LDS layouts of the streamed tiles.  Every direct load writes one contiguous
 // 1 KB block from whole rows; inside a block the 16-byte chunks are ordered
@@ -1123,7 +1131,7 @@ __global__ __launch_bounds__(512, 1) void gemm_residual_coalesced(GemmArgs a) {
     float ref = -INFINITY;
 #pragma unroll
     for (int e = 0; e < 16; ++e) ref = fmaxf(ref, xv[e]);
-    ref = fmaxf(ref, __shfl_xor(ref, 32));
+    ref = reduce_pair32(ref, OpMax{});
     ref = ref > -INFINITY ? ref : 0.0f;  // a half tile wholly beyond V
     const float kq = (float)((lse_q - (double)ref / (double)T) * 1.4426950408889634);
     float rs = 0.0f;
@@ -1133,7 +1141,7 @@ __global__ __launch_bounds__(512, 1) void gemm_residual_coalesced(GemmArgs a) {
       const float q = __builtin_amdgcn_exp2f(fmaf((xv[e] - ref) + acc[e], c, -kq));
       rs += fmaxf(p - q, 0.0f);
     }
-    return rs + __shfl_xor(rs, 32);
+    return reduce_pair32(rs, OpSum{});
   };
 
   const int G = walkers;

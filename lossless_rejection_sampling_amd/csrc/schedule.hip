@@ -91,11 +91,9 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(ScheduleArgs a) {
       tau += before ? (unsigned long long)(0xFFFFFFFFu - qk) : 0ull;
     }
   }
-#pragma unroll
-  for (int o = 1; o < kLanesPerCand; o <<= 1) {
-    cnt += __shfl_xor(cnt, o);
-    tau += __shfl_xor(tau, o);
-  }
+  static_assert(kLanesPerCand == 16, "one DPP row per candidate");
+  cnt = reduce16(cnt, OpSum{});
+  tau = reduce16(tau, OpSum{});
   if (i < nk && sub == 0) {
     const unsigned long long q = 0xFFFFFFFFull - qi;
     const unsigned long long T = ((unsigned long long)B << 32) + tau;
