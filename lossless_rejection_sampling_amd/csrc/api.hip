@@ -15,13 +15,13 @@ namespace {
 constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-// Workspace: [header | scheduler ranks | tile stats | block stats | request state | slot list |
-// residual tile mass].  Header words: 0 status, 1 residual slot count, 2 scheduler
+// Workspace: [header | scheduler ranks | tile stats (B + 1 rows) | block stats | request state | slot list |
+// residual tile mass | U rows of the last drawn tokens].  Header words: 0 status, 1 residual slot count, 2 scheduler
 // ticket, 3 scheduler first failure.  The header and the scheduler ranks are all
 // that dspark_schedule touches, at offsets that do not depend on V and r.
 constexpr size_t kHeaderBytes = 256;
 struct Layout {
-  size_t header, sched, tstat, bstat, req, slots, rsum, total;
+  size_t header, sched, tstat, bstat, req, slots, rsum, hrows, total;
   int n_tiles, n_blk;
 };
 
@@ -35,7 +35,6 @@ bool sizes_ok(int B, int gamma, int V, int r) {
 }
 
 Layout layout(int B, int gamma, int V, int r) {
-  (void)r;
   Layout L{};
   L.n_tiles = (V + kTile - 1) / kTile;
   L.n_blk = (V + kBlock - 1) / kBlock;
@@ -44,8 +43,8 @@ Layout layout(int B, int gamma, int V, int r) {
   off = align_up(off + kHeaderBytes);
   L.sched = off;
   off = align_up(off + (size_t)B * gamma * sizeof(int32_t));
-  L.tstat = off;
-  off = align_up(off + (size_t)B * L.n_tiles * sizeof(TileStat));
+  L.tstat = off;  // one spare row (B) takes the records of padding slots
+  off = align_up(off + (size_t)(B + 1) * L.n_tiles * sizeof(TileStat));
   L.bstat = off;
   off = align_up(off + (size_t)B * (gamma + 1) * L.n_blk * sizeof(BlockStat));
   L.req = off;
@@ -54,6 +53,8 @@ Layout layout(int B, int gamma, int V, int r) {
   off = align_up(off + (size_t)B * sizeof(int32_t));
   L.rsum = off;
   off = align_up(off + (size_t)B * L.n_tiles * sizeof(float));
+  L.hrows = off;  // U rows of the tokens drawn at the previous block position
+  off = align_up(off + (size_t)B * r * sizeof(uint16_t));
   L.total = off;
   return L;
 }
@@ -154,9 +155,14 @@ int dspark_draft_round(const void* base_logits, int logits_dtype, const void* U,
   d.pos_offset = pos_offset, d.tstat = g.tstat, d.seed = seed;
   d.B = B, d.gamma = gamma, d.V = V, d.r = r, d.n_tiles = L.n_tiles;
   d.draft = draft_tokens, d.logq = draft_logq, d.lse = draft_lse, d.status = status;
+  // the streaming GEMM takes the U rows of the previous tokens from this table
+  // (filled by the draw of the previous position) instead of gathering them
+  const bool table = factor_dtype == DSPARK_BF16 && (r == 128 || r == 256);
+  d.hrows = table ? at<void>(workspace, L.hrows) : nullptr;
 
   for (int pos = 0; pos < gamma; ++pos) {
     g.pos = pos;
+    g.hrows = pos > 0 ? d.hrows : nullptr;
     d.pos = pos;
     {
       ProfileScope ps(kClsDraftGemm, s);

@@ -349,6 +349,12 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
 #undef DSPARK_VMCNT
 }
 
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_c() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
 constexpr int kRing = 4;  // W2 tiles in flight: the fill of tile i+3 overlaps tiles i and i+1
 
 template <typename TL, bool RESIDUAL, int R>
@@ -705,61 +711,81 @@ __global__ __launch_bounds__(256) void draft_select_kernel(DraftSelectArgs a) {
       a.logq[(size_t)b * gamma + pos] = Tf > 0.0f ? (float)(sx - lse) : 0.0f;
       a.lse[(size_t)b * gamma + pos] = Tf > 0.0f ? lse : sx;
     }
+    // U[x] for the next position's contraction (bf16 factors, 16 bytes a lane)
+    if (a.hrows && pos + 1 < gamma) {
+      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const TF*>(a.U) + (size_t)x * r);
+      uint4* dst = reinterpret_cast<uint4*>(static_cast<TF*>(a.hrows) + (size_t)b * r);
+      for (int i = lane; i * 8 < r; i += 64) dst[i] = src[i];
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Coalesced draft kernel for bf16 logits (V a multiple of 8) and bf16 factors.
-// A workgroup of 8 wavefronts owns 256 slots (32 per wavefront, the MFMA B
-// operand columns, with their U rows held in registers) and walks the tiles
-// t = blockIdx.x, + gridDim.x, ...  Both streams of a tile, the W2 rows and the
-// backbone logits of the 256 slots, reach LDS by direct loads of whole rows
-// into two-slot rings (layouts below); one barrier per tile.
+// Streaming draft kernel for bf16 logits (V a multiple of 8) and bf16 factors,
+// R in {128, 256}.  A workgroup of 8 wavefronts owns 256 slots (32 per
+// wavefront: the MFMA B operand columns, whose gathered rows U[prev] stay in
+// registers) and walks the 64-column tiles t = blockIdx.x + j * gridDim.x, each
+// as two 32-column stages (half-tiles).
+//
+//  * Column order.  MFMA row i of a stage stands for column perm(i) of its 32,
+//    perm(8 g + 4 h + q) = 16 h + 4 g + q, so the 16 accumulator elements a
+//    lane holds for its slot are 16 consecutive columns.
+//  * Both streams reach LDS by direct loads into four-stage rings, three
+//    stages ahead: the stage's W2 rows (shared by the workgroup, stored in MFMA
+//    row order with the bank-spreading layout WLayout) and each wavefront's own
+//    32 backbone-logit rows (64 bytes each, private to the wavefront).  No
+//    register is ever the target of an outstanding load inside the loop, and
+//    every wait is explicit.
+//  * The backbone logits seed the accumulator, so the MFMA chain yields
+//    t = (x - ref) + bias directly, ref being the slot's logit at the tile's
+//    first column (an exact input value).
+//  * Iteration u seeds and issues the MFMAs of stage u+1 interleaved with the
+//    statistics of stage u; the two stages of a tile are merged into one
+//    record; the wait at the end covers only the loads of stage u+2.
 // ---------------------------------------------------------------------------
 // Reductions with the partner lane (lane ^ 32), identical in both lanes.
 __device__ __forceinline__ float pair_max(float v) { return reduce_pair32(v, OpMax{}); }
 __device__ __forceinline__ float pair_sum(float v) { return reduce_pair32(v, OpSum{}); }
 
-// LDS layouts of the streamed tiles.  Every direct load writes one contiguous
-// 1 KB block from whole rows; inside a block the 16-byte chunks are ordered
-// chunk-major, and the blocks are spaced so that the operand reads of 16
-// consecutive lanes fall in distinct bank groups while every lane's address for
-// chunk c is its own base plus a constant (an instruction immediate).
-//   W2 tile (64 rows x R bf16): RB = 1024 / (2R) rows per block, row rho's
-//   chunk c at byte 16 (RB c + rho) of block b = row / RB, blocks 1024 + 16 RB
-//   bytes apart.
-//   logit tile (slots x 64 bf16): 8 slots per block, slot rho's chunk c at byte
-//   16 (8 c + rho); block b starts at 1024 b + 8 (b % 2) + 128 ((b / 2) % 2)
-//   + 256 (b / 4), so that 32 lanes' 8-byte reads of one chunk are disjoint.
-template <int R>
+// LDS layout of a streamed block of W2 rows (ROWS rows x R bf16).  Every direct
+// load writes one contiguous 1 KB block from whole rows; inside a block the
+// 16-byte chunks are ordered chunk-major, and the blocks are spaced so that the
+// operand reads of 16 consecutive lanes fall in distinct bank groups while every
+// lane's address for chunk c is its own base plus a constant (an instruction
+// immediate): RB = 1024 / (2R) rows per block, row s's chunk c at byte
+// 16 (RB c + s % RB) of block s / RB, blocks 1024 + 16 RB bytes apart.
+template <int R, int ROWS = kTile>
 struct WLayout {
   static constexpr int RB = 1024 / (2 * R);
-  static constexpr int NB = kTile / RB;
+  static constexpr int NB = ROWS / RB;
   static constexpr int STRIDE = 1024 + 16 * RB;
   static constexpr int BYTES = NB * STRIDE;
   __device__ static int block(int b) { return b * STRIDE; }
-  // byte offset of row v, chunk c
-  __device__ static int at(int v, int c) { return (v / RB) * STRIDE + 16 * (RB * c + v % RB); }
-};
-struct XLayout {
-  __device__ static int block(int b) { return b * 1024 + 8 * (b & 1) + 128 * ((b >> 1) & 1) + 256 * (b >> 2); }
-  static constexpr int bytes(int slots) { return (slots / 8) * 1024 + 136 + 256 * (slots / 32); }
-  __device__ static int at(int s, int c) { return block(s >> 3) + 16 * (8 * c + (s & 7)); }
+  // byte offset of row s, chunk c
+  __device__ static int at(int s, int c) { return (s / RB) * STRIDE + 16 * (RB * c + s % RB); }
 };
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Column (within a 32-column stage) of MFMA row i.
+__device__ __forceinline__ int col_of_row(int i) { return ((i >> 2) & 1) * 16 + (i >> 3) * 4 + (i & 3); }
+
+// Workgroup barrier without a memory fence (the waits before it are explicit).
+__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
+
+constexpr int kStages = 4;      // ring depth (stages of 32 columns)
+constexpr int kStageCols = 32;
+constexpr int kXStageBytes = 32 * kStageCols * 2;  // one wavefront's logits of a stage: 2 KB
 
 template <int R>
-__global__ __launch_bounds__(512, 1) void gemm_draft_coalesced(GemmArgs a) {
-  using WL = WLayout<R>;
-  constexpr int W_SLOT = (WL::BYTES + 1023) / 1024 * 1024;
-  constexpr int X_SLOT = (XLayout::bytes(kSlotsPerGroup) + 1023) / 1024 * 1024;
-  constexpr int KS = R / 16;                     // MFMA k-steps per tile
-  constexpr int W_DMA = WL::NB / 8;              // direct loads per wave per tile: W2
-  constexpr int X_DMA = kSlotsPerGroup / 64;     // and backbone logits
+__global__ __launch_bounds__(512, 1) void gemm_draft_stream(GemmArgs a) {
+  using WL = WLayout<R, kStageCols>;
+  constexpr int KS = R / 16;                  // MFMA k-steps per stage
+  constexpr int W_DMA = WL::NB / 8;           // direct loads per wave per stage: W2
+  constexpr int X_DMA = kXStageBytes / 1024;  // and this wave's backbone logits
+  constexpr int W_RING = kStages * WL::BYTES;
   extern __shared__ __attribute__((aligned(1024))) char lds[];
-  char* const wring = lds;                        // 2 x W_SLOT
-  char* const xring = lds + 2 * W_SLOT;           // 2 x X_SLOT
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, l32 = lane & 31;
   const int nslots = a.B;
@@ -767,198 +793,209 @@ __global__ __launch_bounds__(512, 1) void gemm_draft_coalesced(GemmArgs a) {
   const int nt = a.n_tiles, G = gridDim.x;
   if (sg0 >= nslots || (int)blockIdx.x >= nt) return;  // uniform across the workgroup
   const int V = a.V;
+  char* const xring = lds + W_RING + wave * (kStages * kXStageBytes);  // this wave's logit ring
   // byte offsets from uniform bases are 32-bit (the launcher checks the sizes)
   const char* const Wb = static_cast<const char*>(a.Wt);
   const char* const Xb = static_cast<const char*>(a.base);
 
-  // direct load k of this wave for the W2 tile `tile` into ring slot buf
-  auto dma_w = [&](int k, int tile, int buf) {
-    const int f = wave + 8 * k;
-    const int rho = lane % WL::RB, c = lane / WL::RB;
-    const int v = min(tile * kTile + f * WL::RB + rho, V - 1);  // rows beyond V only feed masked columns
-    __builtin_amdgcn_global_load_lds(Wb + ((uint32_t)v * (R * 2) + c * 16),
-                                     (lds_ptr_t)(wring + buf * W_SLOT + WL::block(f)), 16, 0, 0);
+  // Stage u of this workgroup: tile blockIdx.x + (u / 2) G, columns 32 (u % 2)
+  // onwards; stages past the last one repeat it (their loads hit L2 and their
+  // results are never used), so every iteration issues the same loads.
+  const int n_stage = 2 * ((nt - 1 - (int)blockIdx.x) / G + 1);
+  auto stage_col = [&](int u) {
+    u = min(u, n_stage - 1);
+    return ((int)blockIdx.x + (u >> 1) * G) * kTile + (u & 1) * kStageCols;
   };
-  // W2 needs nothing from the slots: the first two tiles start loading at once
-  int t = blockIdx.x;
+  auto dma_w = [&](int u, int slot) {
+    const int c0 = stage_col(u);
 #pragma unroll
-  for (int k = 0; k < W_DMA; ++k) dma_w(k, t, 0);
-  if (t + G < nt) {
-#pragma unroll
-    for (int k = 0; k < W_DMA; ++k) dma_w(k, t + G, 1);
-  }
-
-  // this wave's 32 slots (MFMA B operand columns)
-  const bool active = sg0 + wave * 32 < nslots;
-  int rq, pos, prev;
-  bool valid;
-  slot_info<false>(a, sg0 + wave * 32 + l32, nslots, rq, pos, prev, valid);
-  // backbone-logit rows this lane loads: slot 8 f + lane % 8 of the direct loads
-  // f = wave + 8 k
-  uint32_t xoff[X_DMA];  // element offset of the row in the backbone logits [B * gamma, V]
-#pragma unroll
-  for (int k = 0; k < X_DMA; ++k) {
-    const int sx = (wave + 8 * k) * 8 + (lane & 7);
-    int b2, p2, pr2;
-    bool v2;
-    slot_info<false>(a, sg0 + sx, nslots, b2, p2, pr2, v2);
-    xoff[k] = (uint32_t)(b2 * a.gamma + p2) * (uint32_t)V;
-  }
-  auto dma_x = [&](int k, int tile, int buf) {
-    const int f = wave + 8 * k;
-    const int col = min(tile * kTile + ((lane >> 3) << 3), V - 8);  // the ragged tile is masked later
-    __builtin_amdgcn_global_load_lds(Xb + (xoff[k] + col) * 2,
-                                     (lds_ptr_t)(xring + buf * X_SLOT + XLayout::block(f)), 16, 0, 0);
+    for (int k = 0; k < W_DMA; ++k) {
+      const int f = wave + 8 * k;
+      const int s = f * WL::RB + lane % WL::RB, c = lane / WL::RB;
+      const int v = min(c0 + col_of_row(s), V - 1);  // rows >= V feed masked columns
+      __builtin_amdgcn_global_load_lds(Wb + ((uint32_t)v * (R * 2) + c * 16),
+                                       (lds_ptr_t)(lds + slot * WL::BYTES + WL::block(f)), 16, 0, 0);
+    }
   };
+  // this wave's 32 slots (request = slot, row = block position a.pos); lanes
+  // without a valid slot work on row 0 and write their records to the spare row B
+  const int slot = sg0 + wave * 32 + l32;
+  const bool valid = slot < nslots;
+  const int rq = valid ? slot : 0;
+  const uint32_t xrow = (uint32_t)(rq * a.gamma + a.pos) * (uint32_t)V;  // element offset of the slot's row
+  // Backbone logits: direct load k, lane L fetches chunk 2k + L / 32 (8 columns)
+  // of slot L % 32's row, so lane (half, l32) later reads its 32 bytes (columns
+  // 16 half .. + 15) as chunks at k = half, L = l32 and L = 32 + l32.
+  auto dma_x = [&](int u, int slot) {
+    const int c0 = stage_col(u);
 #pragma unroll
-  for (int k = 0; k < X_DMA; ++k) dma_x(k, t, 0);
+    for (int k = 0; k < X_DMA; ++k) {
+      const int col = min(c0 + (2 * k + half) * 8, V - 8);  // the ragged stage is masked later
+      __builtin_amdgcn_global_load_lds(Xb + (xrow + (uint32_t)col) * 2u,
+                                       (lds_ptr_t)(xring + slot * kXStageBytes + k * 1024), 16, 0, 0);
+    }
+  };
+  const uint32_t st_spare = (uint32_t)nslots * (uint32_t)nt;
+  const uint32_t st_base = valid ? (uint32_t)rq * (uint32_t)nt : st_spare;
+  auto store_rec = [&](uint32_t at, float ref, float mx, float sum) {
+    const f32x4 rec = {ref, mx, sum, 0.0f};
+    __builtin_nontemporal_store(rec, reinterpret_cast<f32x4*>(reinterpret_cast<char*>(a.tstat) + at * 16u));
+  };
 
-  const float T = valid ? effective_temp(a.temperature[rq]) : 1.0f;
-  const float cT = T > 0.0f ? kLog2e / T : 0.0f;
+  // The temperature and the U rows of the previous tokens (from the table the
+  // previous draw filled, or gathered through prev0 at position 0) are loaded
+  // and waited for before any stream load: the compiler's wait for a register
+  // load issued before pending direct-to-LDS loads drains those too.  Then
+  // the stream loads, in the order (vmcnt counts in issue order)
+  //   W(0), X(0), W(1), X(1), W(2), X(2), W(3), X(3) | W(4), X(4) |
+  //   W(5), X(5), record | W(6), X(6) | ...
+  const float T_raw = a.temperature[rq];
   bf16x8 H[KS];
   {
-    const uint16_t* h = static_cast<const uint16_t*>(a.U) + (size_t)prev * R + half * 8;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 zero = {};
-      H[ks] = valid ? *reinterpret_cast<const bf16x8*>(h + ks * 16) : zero;
+    const uint16_t* h;
+    if (a.hrows) {
+      h = static_cast<const uint16_t*>(a.hrows) + (size_t)rq * R;
+    } else {
+      const int p0 = a.prev0[rq];
+      h = static_cast<const uint16_t*>(a.U) + (size_t)(valid ? checked_token(p0, V, a.status, kBadPrev) : 0) * R;
     }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) H[ks] = *reinterpret_cast<const bf16x8*>(h + half * 8 + ks * 16);
   }
-  // operand bases: W2 row l32 (column block 0) with chunk half; logits of this
-  // lane's slot, 8-byte half
-  const int wbase = WL::at(l32, half);
-  const int xbase = XLayout::at(wave * 32 + l32, 0) + 8 * half;
-  const uint32_t st_base = (uint32_t)rq * (uint32_t)nt;
+  __builtin_amdgcn_s_waitcnt(0x0070 | (0xF << 8));  // vmcnt(0): T and the U rows have landed
+  const float T = valid ? effective_temp(T_raw) : 1.0f;
+  const float cT = T > 0.0f ? kLog2e / T : 0.0f;
+  __builtin_amdgcn_sched_barrier(0);
+  dma_w(0, 0);
+  dma_x(0, 0);
+  dma_w(1, 1);
+  dma_x(1, 1);
+  dma_w(2, 2);
+  dma_x(2, 2);
+  dma_w(3, 3);
+  dma_x(3, 3);
 
-  auto read_x = [&](int buf, TileBuf<uint16_t>& x) {
-    const char* p = xring + buf * X_SLOT + xbase;
+  const int wbase = WL::at(l32, half);          // operand base: storage row l32, chunk half
+  const int xbase = half * 1024 + l32 * 16;     // this lane's first logit chunk in a stage
+
+  // accumulator seed x - ref from the logits of stage slot `slot`; the first
+  // stage of a tile also sets ref (its column 0, held by lane l32 of half 0)
+  auto seed = [&](int slot, bool first, f32x16& acc, float& ref) {
+    const u32x4 w0 = *reinterpret_cast<const u32x4*>(xring + slot * kXStageBytes + xbase);
+    const u32x4 w1 = *reinterpret_cast<const u32x4*>(xring + slot * kXStageBytes + xbase + 512);
+    if (first) {
+      float even, odd;
+      row_pair<32>(__uint_as_float(w0[0] << 16), even, odd);
+      ref = even;
+    }
 #pragma unroll
-    for (int vb = 0; vb < 2; ++vb)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const uint2 u = *reinterpret_cast<const uint2*>(p + 128 * (vb * 4 + g));
-        x.w[vb][2 * g] = u.x, x.w[vb][2 * g + 1] = u.y;
-      }
+    for (int e = 0; e < 16; ++e) {
+      const uint32_t w = e < 8 ? w0[(e & 7) >> 1] : w1[(e & 7) >> 1];
+      const float xv = (e & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
+      acc[e] = xv - ref;
+    }
   };
-  // streaming store of a tile record (nothing reads it before the next launch)
-  auto put = [&](int tile, const TileStat& st) {
-    const f32x4 v = {st.ref, st.mx, st.sum, 0.0f};
-    __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(reinterpret_cast<char*>(a.tstat) +
-                                                            (st_base + (uint32_t)tile) * 16u));
+  // operand of k-step ks: storage row l32, chunk 2 ks + half of the W2 stage in ring slot `slot`
+  auto rd = [&](int slot, int ks) {
+    return *reinterpret_cast<const bf16x8*>(lds + slot * WL::BYTES + wbase + 32 * WL::RB * ks);
   };
-  // MFMAs of the next tile (W2 slot wb) interleaved by hand with the statistics
-  // of the current one: k-step ks reads the operands of step ks + 1, issues its
-  // two MFMAs and one slice of the epilogue, fenced so that the MFMA pipe and
-  // the VALU work side by side within the wave.  The epilogue's phases (unpack
-  // and tile max of the logits; t = (x - ref) + bias and its max; exp2 sum)
-  // take the first, second and last two quarters of the k-steps.
-  auto fused = [&](auto masked, int wb, int tile, const f32x16 (&cur)[2], f32x16 (&next)[2],
-                   const TileBuf<uint16_t>& x, TileStat& st) {
-    constexpr bool MASK = decltype(masked)::value;
-    const char* base = wring + wb * W_SLOT + wbase;
-    auto rd = [&](int ks, int vb) {  // rows vb * 32 + l32, chunk 2 ks + half
-      return *reinterpret_cast<const bf16x8*>(base + 32 * WL::RB * ks + (32 / WL::RB) * WL::STRIDE * vb);
-    };
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) next[i][e] = 0.0f;
-    float xv[32];  // element j = 16 vb + e; becomes t in place
-    float ref = -INFINITY, tmax = -INFINITY, mc = 0.0f, sum = 0.0f;
-    bf16x8 A[2][2];
-    A[0][0] = rd(0, 0), A[0][1] = rd(0, 1);
+  // MFMAs of the next stage (ring slot `slot`, accumulator `next`, already
+  // seeded) interleaved with the statistics of the current stage (`cur` holds
+  // t): max over the first quarter of the k-steps, exp2-sum over the next half.
+  auto fused = [&](int slot, const f32x16& cur, f32x16& next, float& tmax, float& sum) {
+    tmax = -INFINITY, sum = 0.0f;
+    float mc = 0.0f;
+    bf16x8 A[2];
+    A[0] = rd(slot, 0);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const int cb = ks & 1;
-      if (ks + 1 < KS) A[cb ^ 1][0] = rd(ks + 1, 0), A[cb ^ 1][1] = rd(ks + 1, 1);
-      next[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[cb][0], H[ks], next[0], 0, 0, 0);
-      next[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[cb][1], H[ks], next[1], 0, 0, 0);
-      constexpr int PA = KS / 4, PB = KS / 2;  // phase boundaries
+      if (ks + 1 < KS) A[(ks + 1) & 1] = rd(slot, ks + 1);
+      next = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[ks & 1], H[ks], next, 0, 0, 0);
+      constexpr int PA = KS / 4, PB = PA + KS / 2;  // phase boundaries
       if (ks < PA) {
-        constexpr int n = 32 / PA;
+        constexpr int n = 16 / PA;
 #pragma unroll
-        for (int j = ks * n; j < ks * n + n; ++j) {
-          const int vb = j >> 4, e = j & 15;
-          xv[j] = x.get(vb, e);
-          if (MASK && acc_col(tile * kTile, vb, e, half) >= V) xv[j] = -INFINITY;
-          ref = fmaxf(ref, xv[j]);
-        }
-        asm volatile("" : "+v"(ref));  // keeps this slice in its k-step
-      } else if (ks < PB) {
-        if (ks == PA) ref = pair_max(ref);
-        constexpr int n = 32 / (PB - PA);
-#pragma unroll
-        for (int j = (ks - PA) * n; j < (ks - PA) * n + n; ++j) {
-          xv[j] = (xv[j] - ref) + cur[j >> 4][j & 15];
-          tmax = fmaxf(tmax, xv[j]);
-        }
+        for (int j = ks * n; j < ks * n + n; ++j) tmax = fmaxf(tmax, cur[j]);
         asm volatile("" : "+v"(tmax));  // keeps this slice in its k-step
-      } else {
-        if (ks == PB) tmax = pair_max(tmax), mc = tmax * cT;
-        constexpr int n = 32 / (KS - PB);
+      } else if (ks < PB) {
+        if (ks == PA) tmax = pair_max(tmax), mc = tmax * cT;
+        constexpr int n = 16 / (PB - PA);
 #pragma unroll
-        for (int j = (ks - PB) * n; j < (ks - PB) * n + n; ++j) sum += __builtin_amdgcn_exp2f(fmaf(xv[j], cT, -mc));
+        for (int j = (ks - PA) * n; j < (ks - PA) * n + n; ++j)
+          sum += __builtin_amdgcn_exp2f(fmaf(cur[j], cT, -mc));
         asm volatile("" : "+v"(sum));  // keeps this slice in its k-step
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    st.ref = ref, st.mx = tmax, st.sum = pair_sum(sum), st.pad = 0.0f;
+    sum = pair_sum(sum);
   };
 
-  f32x16 acc0[2] = {}, acc1[2] = {};
-  TileStat st;
-  int st_tile = -1;
-  wait_vmcnt(0);
-  __syncthreads();
-  if (active) {
-    TileBuf<uint16_t> none = {};
-    fused(std::false_type{}, 0, t, acc1, acc0, none, st);  // MFMAs of the first tile only
-  }
-  __syncthreads();
-  // Ring discipline: in iteration i (tile t_i) W2 slot i%2, last read by the
-  // MFMAs of t_i, receives W2 of t_{i+2}; logit slot (i+1)%2, emptied at the top
-  // of iteration i-1, receives the logits of t_{i+1}.  The logits of t_i leave
-  // LDS and the record of t_{i-1} goes out before any load is issued.
-  auto step = [&](int c0, const f32x16 (&cur)[2], f32x16 (&next)[2]) {
-    const int c1 = c0 ^ 1;
-    TileBuf<uint16_t> x;
-    if (active) {
-      read_x(c0, x);
-      if (st_tile >= 0 && half == 0 && valid) put(st_tile, st);
-    }
-    if (t + 2 * G < nt) {
+  // Iteration u (stage u in ring slot S = u % 4 has its t values in `cur`;
+  // stage u+1 in slot S+1 has landed):
+  //   seed `next` from stage u+1's logits; issue stage u+4 into slot S; run the
+  //   MFMAs of stage u+1 with the statistics of stage u; on a tile's second
+  //   stage (odd u) merge with the first and store the record; wait for stage
+  //   u+2, issued in iteration u-2 (or in the prologue), barrier.  The loads
+  //   of iterations u-1 and u (2 (W_DMA + X_DMA)) are younger than X(u+2) and
+  //   may stay in flight.  Record stores are not counted: a store may complete
+  //   before older loads, so counting it could let the wait pass early, while
+  //   leaving it out only ever waits longer.
+  int tile = blockIdx.x;
+  float ref0 = 0.0f, ref1 = 0.0f, mx_first = 0.0f, sum_first = 0.0f;
+  auto step = [&](auto S_, f32x16& cur, f32x16& next, int u) {
+    constexpr int S = decltype(S_)::value;
+    constexpr bool second = S & 1;  // stage u is the second half of its tile
+    if (second) seed((S + 1) % kStages, true, next, ref0);   // next tile's first stage sets its ref
+    else seed((S + 1) % kStages, false, next, ref0);         // same tile, same ref
+    dma_w(u + 4, S);
+    dma_x(u + 4, S);
+    const int c0 = tile * kTile + (second ? kStageCols : 0);
+    if (c0 + kStageCols > V) {  // a ragged stage: columns >= V do not exist
 #pragma unroll
-      for (int k = 0; k < W_DMA; ++k) dma_w(k, t + 2 * G, c0);
+      for (int e = 0; e < 16; ++e)
+        if (c0 + half * 16 + e >= V) cur[e] = -INFINITY;
     }
-    if (t + G < nt) {
-#pragma unroll
-      for (int k = 0; k < X_DMA; ++k) dma_x(k, t + G, c1);
+    float mx, sum;
+    fused((S + 1) % kStages, cur, next, mx, sum);
+    if (second) {
+      // merge the tile's two stages (a stage wholly beyond V has sum 0)
+      const float m = fmaxf(mx_first, mx);
+      float s = sum_first * __builtin_amdgcn_exp2f((mx_first - m) * cT);
+      if (sum > 0.0f) s += sum * __builtin_amdgcn_exp2f((mx - m) * cT);
+      store_rec(st_base + (uint32_t)tile, ref1, m, s);
+      tile += G;
+      ref1 = ref0;
+    } else {
+      mx_first = mx, sum_first = sum;
     }
-    if (active) {
-      // the MFMAs of the last tile's successor read a stale slot and are discarded
-      if ((t + 1) * kTile <= V) fused(std::false_type{}, c1, t, cur, next, x, st);
-      else fused(std::true_type{}, c1, t, cur, next, x, st);
-      st_tile = t;
-    }
-    wait_vmcnt(0);
-    __syncthreads();
-    t += G;
+    wait_vmcnt_c<2 * (W_DMA + X_DMA)>();
+    barrier_only();
   };
-  for (;;) {
-    step(0, acc0, acc1);
-    if (t >= nt) break;
-    step(1, acc1, acc0);
-    if (t >= nt) break;
+
+  f32x16 acc0, acc1;
+  // prologue: stage 0 landed (the loads of stages 1 to 3 may be pending)
+  wait_vmcnt_c<3 * (W_DMA + X_DMA)>();
+  barrier_only();
+  seed(0, true, acc0, ref0);
+  ref1 = ref0;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd(0, ks), H[ks], acc0, 0, 0, 0);
+  wait_vmcnt_c<2 * (W_DMA + X_DMA)>();  // stage 1 landed
+  barrier_only();  // ... in every wave, and every wave is done with ring slot 0
+  // steady state, unrolled four times so that ring slots are immediates
+  for (int u = 0;; u += 4) {
+    step(std::integral_constant<int, 0>{}, acc0, acc1, u + 0); if (u + 1 >= n_stage) break;
+    step(std::integral_constant<int, 1>{}, acc1, acc0, u + 1); if (u + 2 >= n_stage) break;
+    step(std::integral_constant<int, 2>{}, acc0, acc1, u + 2); if (u + 3 >= n_stage) break;
+    step(std::integral_constant<int, 3>{}, acc1, acc0, u + 3); if (u + 4 >= n_stage) break;
   }
-  if (active && st_tile >= 0 && half == 0 && valid) put(st_tile, st);
 }
 
 template <int R>
-hipError_t launch_coalesced(const GemmArgs& a, hipStream_t s) {
+hipError_t launch_draft_stream(const GemmArgs& a, hipStream_t s) {
   static int max_wg = 0;
-  const size_t lds = (size_t)2 * ((WLayout<R>::BYTES + 1023) / 1024 * 1024) +
-                     (size_t)2 * ((XLayout::bytes(kSlotsPerGroup) + 1023) / 1024 * 1024);
-  const void* fn = reinterpret_cast<const void*>(&gemm_draft_coalesced<R>);
+  const size_t lds = (size_t)kStages * (WLayout<R, kStageCols>::BYTES + 8 * kXStageBytes);
+  const void* fn = reinterpret_cast<const void*>(&gemm_draft_stream<R>);
   if (!max_wg) {
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
@@ -972,7 +1009,7 @@ hipError_t launch_coalesced(const GemmArgs& a, hipStream_t s) {
   }
   const int groups = (a.B + kSlotsPerGroup - 1) / kSlotsPerGroup;
   const int wg_x = max(1, min(a.n_tiles, max_wg / groups));
-  gemm_draft_coalesced<R><<<dim3(wg_x, groups), 512, lds, s>>>(a);
+  gemm_draft_stream<R><<<dim3(wg_x, groups), 512, lds, s>>>(a);
   return hipGetLastError();
 }
 
@@ -1234,14 +1271,14 @@ hipError_t gemm_dispatch(const GemmArgs& a, int factor_dtype, bool vec, hipStrea
   if constexpr (sizeof(TL) == 2) {
     // the coalesced kernels address their inputs with 32-bit byte offsets
     const bool fits = (size_t)a.B * (a.gamma + 1) * a.V * 2 < (1ull << 32) &&
-                      (size_t)a.V * a.r * 2 < (1ull << 32) && (size_t)a.B * a.n_tiles * 16 < (1ull << 32);
+                      (size_t)a.V * a.r * 2 < (1ull << 32) && (size_t)(a.B + 1) * a.n_tiles * 16 < (1ull << 32);
     if (factor_dtype == DSPARK_BF16 && a.V % 8 == 0 && a.V >= 64 && (a.r == 128 || a.r == 256) && fits) {
       if constexpr (RESIDUAL) {
         if (a.r == 256) return launch_residual_coalesced<256>(a, s);
         return launch_residual_coalesced<128>(a, s);
       } else {
-        if (a.r == 256) return launch_coalesced<256>(a, s);
-        return launch_coalesced<128>(a, s);
+        if (a.r == 256) return launch_draft_stream<256>(a, s);
+        return launch_draft_stream<128>(a, s);
       }
     }
   }

@@ -36,6 +36,7 @@ struct GemmArgs {
   const int32_t* draft;      // [B, gamma]
   const float* temperature;  // [B]
   const double* draft_lse;   // [B, gamma]             (residual mode)
+  const void* hrows;         // [B, r] U rows of the previous tokens, or NULL (draft mode)
   const ReqState* req;       // [B]                    (residual mode)
   const int32_t* slot_req;   // [B]                    (residual mode)
   const uint32_t* slot_count;//                        (residual mode)
@@ -61,6 +62,7 @@ struct DraftSelectArgs {
   int32_t* draft;
   float* logq;
   double* lse;
+  void* hrows;               // [B, r] or NULL: receives U[x] of the token drawn
   uint32_t* status;
 };
 
