@@ -222,7 +222,6 @@ int dspark_verify(const void* target_logits, const void* base_logits, int logits
   a.debug_logp_logq = debug_logp_logq, a.debug_residual = debug_residual;
   a.status = at<uint32_t>(workspace, L.header);
 
-  DSPARK_TRY(launch_verify_prep(a, s));
   {
     ProfileScope ps(kClsRowStats, s);
     DSPARK_TRY(launch_row_stats(a, logits_dtype, s));

@@ -720,6 +720,167 @@ __global__ __launch_bounds__(256) void draft_select_kernel(DraftSelectArgs a) {
   }
 }
 
+// Draw of block position `pos` for request b = blockIdx.x when the row has at
+// most 64 blocks (V <= 262144): the same three-level draw and fp64 recompute
+// as draft_select_kernel with three memory round trips on the critical path.
+//   1. The tile records, the temperature and the previous token are requested
+//      together; meanwhile waves 0, 1 and 2 compute the block-, tile- and
+//      column-level Gumbel values of this draw (they depend on no data).
+//   2. Records go to LDS; 16-lane groups reduce each block; wave 0 draws the
+//      block and the row's log-sum-exp, then the tile from the LDS copy.
+//   3. The chosen tile is recomputed in fp64 (rank split over the four
+//      wavefronts), the column drawn, and U[x] copied for the next position.
+// The arithmetic of every value that decides a draw is that of
+// draft_select_kernel.
+template <typename TL, typename TF>
+__global__ __launch_bounds__(256) void draft_select_fast(DraftSelectArgs a) {
+  constexpr int kMaxTiles = kTilesPerBlock * 64;
+  __shared__ double s_d[kMaxTiles];     // ref + mx of every tile
+  __shared__ float s_sum[kMaxTiles];    // exp-sum of every tile
+  __shared__ double s_g[3][64];         // Gumbel values: block, tile, column level
+  __shared__ double s_bm[64], s_part[4][64];
+  __shared__ float s_be[64];
+  __shared__ double s_val[4], s_lse;
+  __shared__ int s_idx[4], s_tile;
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int V = a.V, r = a.r, gamma = a.gamma, nt = a.n_tiles, pos = a.pos;
+  const int nblk = (nt + kTilesPerBlock - 1) / kTilesPerBlock;
+  const TileStat* ts = a.tstat + (size_t)b * nt;
+
+  // 1. every load of the draw's first phase at once
+  const float T_raw = a.temperature[b];
+  const int prev_raw = pos == 0 ? a.prev0[b] : a.draft[(size_t)b * gamma + pos - 1];
+  const uint32_t off = a.pos_offset ? (uint32_t)a.pos_offset[b] : 0u;
+  float4 rec[4][4];  // tiles 1024 q + 4 tid + k (unconditional loads, so that they all go out at once)
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) rec[q][k] = *reinterpret_cast<const float4*>(ts + min(1024 * q + 4 * tid + k, nt - 1));
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (1024 * q + 4 * tid + k >= nt) rec[q][k] = make_float4(0.0f, -INFINITY, 0.0f, 0.0f);
+  const uint32_t rpos = (uint32_t)(pos + 1) + off;
+  if (wave < 3 && (wave != 0 || lane < nblk)) s_g[wave][lane] = gumbel(a.seed, kDraftTop + wave, b, rpos, lane);
+  const float Tf = checked_temp(T_raw, a.status);
+  const int prev = checked_token(prev_raw, V, a.status, pos == 0 ? kBadPrev : kBadDraft);
+
+  // 2. records to LDS; block statistics over 16-lane groups
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int t = 1024 * q + 4 * tid + k;
+      if (t < nt) s_d[t] = (double)rec[q][k].x + (double)rec[q][k].y, s_sum[t] = rec[q][k].z;
+    }
+  int tile;
+  double lse = 0.0;
+  if (Tf > 0.0f) {
+    const double invT = 1.0 / (double)Tf;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      double d[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) d[k] = (double)rec[q][k].x + (double)rec[q][k].y;
+      double m = fmax(fmax(d[0], d[1]), fmax(d[2], d[3]));
+      m = group16_max(m);
+      float e = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (rec[q][k].z > 0.0f) e += rec[q][k].z * expf((float)((d[k] - m) * invT));
+      e = group16_sum(e);
+      const int j = 16 * q + 4 * wave + (lane >> 4);
+      if ((lane & 15) == 0 && j < nblk) s_bm[j] = m, s_be[j] = e;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const double mref = s_d[0];
+      // block (lane j) and the row's log-sum-exp
+      double val = -INFINITY, m = -INFINITY, e = 0.0;
+      int idx = 0x7fffffff;
+      if (lane < nblk) {
+        m = s_bm[lane], e = (double)s_be[lane];
+        val = (m - mref) * invT + log(e) + s_g[0][lane];
+        idx = lane;
+      }
+      wave_argmax(val, idx);
+      const double gm = wave_max(m);
+      const double gs = wave_sum(e > 0.0 ? e * exp((m - gm) * invT) : 0.0);
+      // tile inside the chosen block
+      const int blk = index_or(idx, nblk, 0);
+      const int t0 = blk * kTilesPerBlock, t1 = min(t0 + kTilesPerBlock, nt);
+      double tv = -INFINITY;
+      int ti = 0x7fffffff;
+      if (t0 + lane < t1) {
+        tv = (s_d[t0 + lane] - mref) * invT + log((double)s_sum[t0 + lane]) + s_g[1][lane];
+        ti = t0 + lane;
+      }
+      wave_argmax(tv, ti);
+      if (lane == 0) s_tile = index_or(ti, t1, t0), s_lse = gm * invT + log(gs);
+    }
+    __syncthreads();
+    tile = s_tile, lse = s_lse;
+  } else {
+    // greedy: the tile with the largest logit (lowest index on ties)
+    double best = -INFINITY;
+    int bt = 0x7fffffff;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int t = 1024 * q + 4 * tid + k;
+        const double d = (double)rec[q][k].x + (double)rec[q][k].y;
+        if (t < nt && d > best) best = d, bt = t;
+      }
+    wave_argmax(best, bt);
+    if (lane == 0) s_val[wave] = best, s_idx[wave] = bt;
+    __syncthreads();
+    best = -INFINITY, bt = 0x7fffffff;
+    for (int w = 0; w < 4; ++w)
+      if (s_val[w] > best || (s_val[w] == best && s_idx[w] < bt)) best = s_val[w], bt = s_idx[w];
+    tile = index_or(bt, nt, 0);
+  }
+
+  // 3. fp64 recompute of the chosen tile (rank split over the wavefronts)
+  const TL* brow = static_cast<const TL*>(a.base) + ((size_t)b * gamma + pos) * V;
+  const TF* h = static_cast<const TF*>(a.U) + (size_t)prev * r;
+  const int v = tile * kTile + lane;
+  const float xb = load_logit(brow + min(v, V - 1));  // unconditional: issued with the factor rows
+  const int kq = (r + 3) / 4, k0 = min(wave * kq, r), k1 = min(k0 + kq, r);
+  s_part[wave][lane] = v < V ? dot_part<TF>(h, static_cast<const TF*>(a.Wt) + (size_t)v * r, k0, k1) : 0.0;
+  __syncthreads();
+  if (wave == 0) {
+    double lv = -INFINITY, sv = -INFINITY;
+    int vi = 0x7fffffff;
+    if (v < V) {
+      const double d = (double)xb + ((s_part[0][lane] + s_part[1][lane]) + (s_part[2][lane] + s_part[3][lane]));
+      if (Tf > 0.0f) {
+        sv = d / (double)Tf;
+        lv = sv + s_g[2][lane];
+      } else {
+        sv = d;
+        lv = d;
+      }
+      vi = v;
+    }
+    wave_argmax(lv, vi);
+    const int x = index_or(vi, min(V, (tile + 1) * kTile), tile * kTile);
+    const double sx = __shfl(sv, x - tile * kTile);
+    if (lane == 0) {
+      a.draft[(size_t)b * gamma + pos] = x;
+      a.logq[(size_t)b * gamma + pos] = Tf > 0.0f ? (float)(sx - lse) : 0.0f;
+      a.lse[(size_t)b * gamma + pos] = Tf > 0.0f ? lse : sx;
+    }
+    // U[x] for the next position's contraction (bf16 factors, 16 bytes a lane)
+    if (a.hrows && pos + 1 < gamma) {
+      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const TF*>(a.U) + (size_t)x * r);
+      uint4* dst = reinterpret_cast<uint4*>(static_cast<TF*>(a.hrows) + (size_t)b * r);
+      for (int i = lane; i * 8 < r; i += 64) dst[i] = src[i];
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Streaming draft kernel for bf16 logits (V a multiple of 8) and bf16 factors,
 // R in {128, 256}.  A workgroup of 8 wavefronts owns 256 slots (32 per
@@ -1314,6 +1475,16 @@ hipError_t launch_gemm_stats(const GemmArgs& a, int logits_dtype, int factor_dty
 hipError_t launch_draft_select(const DraftSelectArgs& a, int logits_dtype, int factor_dtype,
                                hipStream_t s) {
   const dim3 grid(a.B);
+  if (a.n_tiles <= kTilesPerBlock * 64) {
+    if (logits_dtype == DSPARK_BF16) {
+      if (factor_dtype == DSPARK_BF16) draft_select_fast<uint16_t, uint16_t><<<grid, 256, 0, s>>>(a);
+      else draft_select_fast<uint16_t, float><<<grid, 256, 0, s>>>(a);
+    } else {
+      if (factor_dtype == DSPARK_BF16) draft_select_fast<float, uint16_t><<<grid, 256, 0, s>>>(a);
+      else draft_select_fast<float, float><<<grid, 256, 0, s>>>(a);
+    }
+    return hipGetLastError();
+  }
   if (logits_dtype == DSPARK_BF16) {
     if (factor_dtype == DSPARK_BF16) draft_select_kernel<uint16_t, uint16_t><<<grid, 256, 0, s>>>(a);
     else draft_select_kernel<uint16_t, float><<<grid, 256, 0, s>>>(a);

@@ -96,7 +96,6 @@ struct VerifyArgs {
   uint32_t* status;
 };
 
-hipError_t launch_verify_prep(const VerifyArgs& a, hipStream_t s);
 hipError_t launch_row_stats(const VerifyArgs& a, int logits_dtype, hipStream_t s);
 hipError_t launch_accept(const VerifyArgs& a, int logits_dtype, hipStream_t s);
 hipError_t launch_residual_select(const VerifyArgs& a, int logits_dtype, int factor_dtype,

@@ -8,11 +8,12 @@
 // The residual is max(0, p - q) normalised.
 //
 // Kernels, in launch order:
-//   verify_prep       clear the residual work list, check budgets
 //   row_stats         one wavefront per (target row, 4096-column block): max,
-//                     exp-sum relative to the max, argmax      [HBM-bound pass]
-//   accept            one wavefront per request: accept tests, bonus draw or
-//                     greedy argmax, queue of requests that rejected
+//                     exp-sum relative to the max, argmax      [HBM-bound pass];
+//                     its first wavefront also empties the residual work list
+//   accept            one wavefront per request: budget check, accept tests,
+//                     bonus draw or greedy argmax, queue of requests that
+//                     rejected
 //   (gemm_stats)      residual mass of every tile of the rejected rows
 //   residual_select   one wavefront per rejected request: draw from the residual
 //   residual_debug    optional: the normalised residual row
@@ -32,14 +33,6 @@ __device__ __forceinline__ int budget_of(const VerifyArgs& a, int b) {
   return L < 0 ? 0 : (L > a.gamma ? a.gamma : L);
 }
 
-__global__ void verify_prep_kernel(VerifyArgs a) {
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b == 0) *a.slot_count = 0u;
-  if (b < a.B) {
-    a.req[b].pending = 0;
-    if (a.budget && (a.budget[b] < 0 || a.budget[b] > a.gamma)) flag_status(a.status, kBadBudget);
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Target row statistics.  A lane holds 64 logits of the block in registers:
@@ -51,6 +44,8 @@ template <typename TL, bool VEC>
 __global__ __launch_bounds__(64) void row_stats_kernel(VerifyArgs a) {
   const int blk = blockIdx.x, row = blockIdx.y, lane = threadIdx.x;
   const int gamma = a.gamma, V = a.V;
+  // the accept pass appends to the residual work list after this kernel
+  if (blk == 0 && row == 0 && lane == 0) *a.slot_count = 0u;
   const int b = row / (gamma + 1), j = row - b * (gamma + 1);
   if (j > budget_of(a, b)) return;
   const float T = effective_temp(a.temperature[b]);
@@ -225,6 +220,7 @@ __global__ __launch_bounds__(256) void accept_kernel(VerifyArgs a) {
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int gamma = a.gamma, V = a.V, nb = a.n_blk;
   const int L = budget_of(a, b);
+  if (tid == 0 && a.budget && (a.budget[b] < 0 || a.budget[b] > gamma)) flag_status(a.status, kBadBudget);
   const float Tf = checked_temp(a.temperature[b], a.status);
   const bool greedy = !(Tf > 0.0f);
   const double invT = greedy ? 0.0 : 1.0 / (double)Tf;
@@ -276,6 +272,7 @@ __global__ __launch_bounds__(256) void accept_kernel(VerifyArgs a) {
     a.req[b] = st;
     a.slot_req[atomicAdd(a.slot_count, 1u)] = b;
   }
+  if (tid == 0 && (greedy || n == L)) a.req[b].pending = 0;  // no residual draw for this request
   if (wave == 0) {
     for (int i = lane; i <= gamma; i += 64) {
       int t = -1;
@@ -437,11 +434,6 @@ __global__ __launch_bounds__(64) void residual_debug_kernel(VerifyArgs a) {
 }
 
 }  // namespace
-
-hipError_t launch_verify_prep(const VerifyArgs& a, hipStream_t s) {
-  verify_prep_kernel<<<(a.B + 255) / 256, 256, 0, s>>>(a);
-  return hipGetLastError();
-}
 
 hipError_t launch_row_stats(const VerifyArgs& a, int logits_dtype, hipStream_t s) {
   const dim3 grid(a.n_blk, a.B * (a.gamma + 1));
