@@ -39,7 +39,40 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="only run a plain device copy of known size (counter calibration) and exit")
     return p.parse_args()
+
+
+def calibrate_copy():
+    """A plain device-to-device copy of counters.COPY_BYTES, COPY_REPS times:
+    the reference that scales the FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+
+    from lossless_rejection_sampling_amd import counters
+
+    n = counters.COPY_BYTES // 4
+    src = torch.arange(n, device="cuda", dtype=torch.int32)
+    dst = torch.empty_like(src)
+    for _ in range(counters.COPY_REPS):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    assert torch.equal(dst, src)
+    print(json.dumps({"calibration_copy_bytes": counters.COPY_BYTES, "reps": counters.COPY_REPS}))
+
+
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "draft_gemm_B256_traffic.md")
+
+
+def measured_traffic(kernel_name):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, or None when there is none or the kernel source has changed since."""
+    from lossless_rejection_sampling_amd import counters
+
+    rec = counters.read_summary(TRAFFIC_SUMMARY)
+    if rec is None or rec["kernel"] != kernel_name or rec["source"] != counters.source_hash():
+        return None
+    return rec["bytes"]
 
 
 def algorithmic(rnd, budgets):
@@ -62,6 +95,9 @@ def algorithmic(rnd, budgets):
 
 def main():
     args = parse()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU layout is "
               "a design note, not part of this build", file=sys.stderr)
@@ -153,7 +189,7 @@ def main():
         a = alg.get(dominant, dict(bytes=0.0))
         roof = dict(bound="hbm", achieved=a["bytes"] / dom_avg_s / 1e9, peak=HBM_PEAK_GBS, unit="GB/s")
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(dominant)
     roof["kernel"] = dominant
     roof["avg_us"] = dom_avg_s * 1e6
 

@@ -1,0 +1,145 @@
+"""Summaries of rocprofv3 hardware-counter runs (measurement support).
+
+HBM traffic of a kernel comes from two `rocprofv3 --pmc` runs of the same
+command, one collecting FETCH_SIZE and one WRITE_SIZE (KiB per dispatch, read
+at the L2/memory boundary).  Each counter is scaled by what it reads for a
+plain device copy of known size (`bench.py --calibrate-copy`), so that the
+result is in bytes.  The summary records a hash of the kernel's source file;
+bench.py reports the traffic only while that hash still matches.
+
+  python3 -m lossless_rejection_sampling_amd.counters summarize CSV KERNEL COUNTER
+  python3 -m lossless_rejection_sampling_amd.counters report BENCH_FETCH BENCH_WRITE COPY_FETCH COPY_WRITE KERNEL CLASS
+  python3 -m lossless_rejection_sampling_amd.counters source-hash
+"""
+
+from __future__ import annotations
+
+import csv
+import hashlib
+import os
+import re
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+# files whose content decides the kernels the traffic figures belong to
+SOURCES = ("csrc/draft.hip", "csrc/device.hpp", "csrc/kernels.hpp")
+COPY_BYTES = 256 << 20   # bytes one calibration copy reads (and writes)
+COPY_REPS = 5
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in SOURCES:
+        with open(os.path.join(PKG, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def per_dispatch(path: str, kernel: str, counter: str):
+    """Values of `counter` for every dispatch whose kernel name contains `kernel`."""
+    out = []
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            if kernel in row.get("Kernel_Name", "") and row.get("Counter_Name") == counter:
+                out.append(float(row["Counter_Value"]))
+    return out
+
+
+def summarize(path: str, kernel: str, counter: str) -> dict:
+    vals = per_dispatch(path, kernel, counter)
+    if not vals:
+        raise SystemExit(f"no {counter} rows for kernel '{kernel}' in {path}")
+    vals.sort()
+    return dict(kernel=kernel, counter=counter, dispatches=len(vals),
+                mean_kib=sum(vals) / len(vals), median_kib=vals[len(vals) // 2])
+
+
+def read_summary(md_path: str):
+    """The machine-readable line of a traffic summary:
+    `traffic: kernel=<k> bytes_per_launch=<n> source=<hash>`."""
+    if not os.path.exists(md_path):
+        return None
+    for line in open(md_path):
+        m = re.match(r"\s*traffic:\s+kernel=(\S+)\s+bytes_per_launch=([0-9.e+]+)\s+source=(\w+)", line)
+        if m:
+            return dict(kernel=m.group(1), bytes=float(m.group(2)), source=m.group(3))
+    return None
+
+
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def calibration(path: str, counter: str) -> float:
+    """Bytes per KiB-unit of `counter`: the known copy size over the median
+    reading of the large copy dispatches of `bench.py --calibrate-copy`."""
+    vals = []
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row.get("Kernel_Name") == COPY_KERNEL and row.get("Counter_Name") == counter:
+                vals.append(float(row["Counter_Value"]))
+    vals = sorted(v for v in vals if v > 0.25 * COPY_BYTES / 1024)  # the 256 MiB copies only
+    if len(vals) < COPY_REPS:
+        raise SystemExit(f"expected {COPY_REPS} calibration copies in {path}, found {len(vals)}")
+    return COPY_BYTES / vals[len(vals) // 2]
+
+
+def report(bench_fetch, bench_write, copy_fetch, copy_write, kernel, cls, command_note=""):
+    """Markdown summary with the machine-readable `traffic:` line bench.py reads."""
+    f = summarize(bench_fetch, kernel, "FETCH_SIZE")
+    w = summarize(bench_write, kernel, "WRITE_SIZE")
+    kf = calibration(copy_fetch, "FETCH_SIZE")
+    kw = calibration(copy_write, "WRITE_SIZE")
+    fetch_b, write_b = f["mean_kib"] * kf, w["mean_kib"] * kw
+    lines = [
+        f"# HBM traffic of `{kernel}` (class `{cls}`), DSpark-5 round B=256 gamma=5 V=151936 r=256 (bf16)",
+        "",
+        "Counters read at the L2 / memory boundary, one `rocprofv3 --pmc` run per counter "
+        "(run from /tmp with TMPDIR=/tmp, repository at /root/repo):",
+        "",
+        "```",
+        "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc/bench_fetch -o run --output-format csv -- "
+        "python3 /root/repo/bench.py --steps 2 --warmup 1 --no-cpu-baseline",
+        "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc/bench_write -o run --output-format csv -- "
+        "python3 /root/repo/bench.py --steps 2 --warmup 1 --no-cpu-baseline",
+        "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc/copy_fetch -o run --output-format csv -- "
+        "python3 /root/repo/bench.py --calibrate-copy",
+        "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc/copy_write -o run --output-format csv -- "
+        "python3 /root/repo/bench.py --calibrate-copy",
+        "python3 -m lossless_rejection_sampling_amd.counters report gpurun_out/pmc/bench_fetch/run_counter_collection.csv "
+        "gpurun_out/pmc/bench_write/run_counter_collection.csv gpurun_out/pmc/copy_fetch/run_counter_collection.csv "
+        f"gpurun_out/pmc/copy_write/run_counter_collection.csv {kernel} {cls}",
+        "```",
+        "",
+        f"Calibration: a {COPY_BYTES >> 20} MiB ({COPY_BYTES >> 10} KiB) device copy (`{COPY_KERNEL}`, median of "
+        f"{COPY_REPS}) reads {COPY_BYTES / kf:.1f} KiB of FETCH_SIZE and {COPY_BYTES / kw:.1f} KiB of WRITE_SIZE: "
+        f"the counters are scaled by {kf / 1024:.4f} (FETCH) and {kw / 1024:.4f} (WRITE).",
+        "",
+        "| counter | dispatches | mean KiB | scaled MB per launch |",
+        "|---|---:|---:|---:|",
+        f"| FETCH_SIZE | {f['dispatches']} | {f['mean_kib']:.1f} | {fetch_b / 1e6:.2f} |",
+        f"| WRITE_SIZE | {w['dispatches']} | {w['mean_kib']:.1f} | {write_b / 1e6:.2f} |",
+        f"| total | | | {(fetch_b + write_b) / 1e6:.2f} |",
+        "",
+    ]
+    if command_note:
+        lines += [command_note, ""]
+    lines += [f"traffic: kernel={cls} bytes_per_launch={fetch_b + write_b:.0f} source={source_hash()}", ""]
+    return "\n".join(lines)
+
+
+def main(argv):
+    if len(argv) == 7 and argv[0] == "report":
+        print(report(*argv[1:]), end="")
+        return
+    if len(argv) >= 1 and argv[0] == "source-hash":
+        print(source_hash())
+        return
+    if len(argv) == 4 and argv[0] == "summarize":
+        s = summarize(argv[1], argv[2], argv[3])
+        print(" ".join(f"{k}={v}" for k, v in s.items()))
+        return
+    raise SystemExit(__doc__)
+
+
+if __name__ == "__main__":
+    main(sys.argv[1:])

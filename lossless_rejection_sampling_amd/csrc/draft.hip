@@ -980,6 +980,7 @@ __global__ __launch_bounds__(512, 1) void gemm_draft_stream(GemmArgs a) {
   };
   // this wave's 32 slots (request = slot, row = block position a.pos); lanes
   // without a valid slot work on row 0 and write their records to the spare row B
+  // (any number of lanes may write it: its contents are never read)
   const int slot = sg0 + wave * 32 + l32;
   const bool valid = slot < nslots;
   const int rq = valid ? slot : 0;
@@ -1123,7 +1124,7 @@ __global__ __launch_bounds__(512, 1) void gemm_draft_stream(GemmArgs a) {
       const float m = fmaxf(mx_first, mx);
       float s = sum_first * __builtin_amdgcn_exp2f((mx_first - m) * cT);
       if (sum > 0.0f) s += sum * __builtin_amdgcn_exp2f((mx - m) * cT);
-      store_rec(st_base + (uint32_t)tile, ref1, m, s);
+      if (half == 0) store_rec(st_base + (uint32_t)tile, ref1, m, s);  // both halves hold the same values
       tile += G;
       ref1 = ref0;
     } else {
