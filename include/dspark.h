@@ -18,6 +18,12 @@
  *        the residual distribution.
  *   [P4] "DeepSeek发布DSpark" (learnblockchain.cn), section "DSpark 是什么？":
  *        a bonus token after a fully accepted block.
+ *   [P5] "DSpark, la bozza ..." (paithon.it), section "Che cosa resta da
+ *        verificare", and "DSpark : le pari de DeepSeek ..." (aitalk.it),
+ *        section "Vérifier seulement ce qui compte": in production the cut is
+ *        estimated from confidences two steps old and the early stop is
+ *        removed; scores are recalibrated position by position, left to right
+ *        (Sequential Temperature Scaling), keeping their order.
  *
  * Conventions for every call:
  *   - Tensor arguments are DEVICE pointers owned by the caller; the library
@@ -54,7 +60,7 @@
 extern "C" {
 #endif
 
-#define DSPARK_ABI_VERSION 2
+#define DSPARK_ABI_VERSION 3
 
 enum dspark_status_code {
   DSPARK_OK = 0,
@@ -66,6 +72,14 @@ enum dspark_status_code {
 enum dspark_dtype {
   DSPARK_BF16 = 0, /* bfloat16 */
   DSPARK_F32 = 1   /* IEEE float32 */
+};
+
+/* Verify-budget rules of dspark_schedule_ex. */
+enum dspark_schedule_rule {
+  DSPARK_SCHED_EARLY_STOP = 0, /* the greedy prefix scheduler with its early stop ([P2]) */
+  DSPARK_SCHED_ARGMAX = 1,     /* the production rule: best cut, no early stop ([P5]) */
+  DSPARK_SCHED_FIXED = 2,      /* baseline: every request verifies min(param, gamma) tokens */
+  DSPARK_SCHED_THRESHOLD = 3   /* baseline: verify while the score exceeds param */
 };
 
 /* Version of this ABI (DSPARK_ABI_VERSION of the built library). */
@@ -144,6 +158,34 @@ int dspark_schedule(const float* conf, const double* sps_B, const double* sps_va
                     void* workspace, void* stream);
 
 /*
+ * dspark_schedule_ex -- dspark_schedule with Sequential Temperature Scaling and
+ * a choice of rule ([P2], [P5]).
+ *
+ *   tau      [gamma] float32 or NULL: when given, every score is first
+ *            rescaled to c' = 1 / (1 + exp(-z / tau[j])), z = ln c - ln(1 - c),
+ *            evaluated in float64 and rounded once to float32 (kept inside
+ *            (0, 1)); tau > 0.  The rules below then use c'.
+ *   rule     DSPARK_SCHED_EARLY_STOP: exactly dspark_schedule.
+ *            DSPARK_SCHED_ARGMAX: candidates in the same order; the number m
+ *              admitted maximises Theta_m = tau_m / t(N_m) over m = 0..B*gamma
+ *              (tau_m = B 2^32 + the first m values Q, N_m = B + m, one
+ *              float64 division), the smallest such m on ties.  The production
+ *              scheduler applies this rule to confidence scores two rounds old:
+ *              the caller passes those.
+ *            DSPARK_SCHED_FIXED: budget[b] = min(max(param, 0), gamma) (MTP-k).
+ *            DSPARK_SCHED_THRESHOLD: budget[b] = number of leading positions j
+ *              with c'[b, j] > (float)param.
+ *   sps_B, sps_val, n_points: as for dspark_schedule; only read by the first
+ *            two rules (may be NULL for the others).
+ * Workspace: dspark_schedule_workspace_bytes(B, gamma).  Errors: an unknown
+ * rule or a NaN param returns DSPARK_EINVAL; a non-positive tau gives NaN or
+ * extreme scores that are clamped.
+ */
+int dspark_schedule_ex(const float* conf, const float* tau, const double* sps_B, const double* sps_val,
+                       int n_points, int B, int gamma, int rule, double param, int32_t* budget,
+                       void* workspace, void* stream);
+
+/*
  * dspark_verify -- [P3] lossless verification with the [P4] bonus token.
  *
  * For request b with budget L = budget[b] (NULL: L = gamma), target row j of
@@ -182,6 +224,34 @@ int dspark_verify(const void* target_logits, const void* base_logits, int logits
                   float* debug_logp_logq, float* debug_residual,
                   void* workspace, void* stream);
 
+/*
+ * dspark_acceptance -- the analytic acceptance rate of every drafted position
+ * ("DSpark, la bozza ...", section "Verificare meglio, non di più", eq. c*_k:
+ * one minus the total-variation distance between the draft and target
+ * distributions, the label the confidence head is trained on).
+ *
+ *   c_star[b, k-1] = sum_v min(p_k(v), q_k(v)),   k = 1..gamma
+ * with p_k = softmax(target_logits[b, k-1] / T_b) and q_k the draft
+ * distribution of position k rebuilt from base_logits, U, W and the drafted
+ * prefix (x_0 = prev0[b], x_j = draft_tokens[b, j-1]) and normalised by
+ * draft_lse[b, k-1] -- i.e. the probability that the accept test of position k
+ * passes given that x_1..x_{k-1} were accepted.  Greedy requests (T_b = 0):
+ * 1 if draft_tokens[b, k-1] is the target row's lowest-index maximum, else 0.
+ *
+ *   target_logits [B, gamma+1, V], base_logits [B, gamma, V], U, W, prev0,
+ *   temperature: as for dspark_verify; draft_tokens, draft_lse: the outputs of
+ *   dspark_draft_round for the same inputs.
+ *   c_star        [B, gamma] float64 out.
+ * Reads every target and backbone row once plus W2 per group of 128 positions;
+ * tile masses are fp32, their sum fp64.  Shares the workspace of the other
+ * calls (ordered on one stream: it empties the residual work list).
+ */
+int dspark_acceptance(const void* target_logits, const void* base_logits, int logits_dtype,
+                      const void* U, const void* W, int factor_dtype,
+                      const int32_t* prev0, const int32_t* draft_tokens, const double* draft_lse,
+                      const float* temperature, int B, int gamma, int V, int r,
+                      double* c_star, void* workspace, void* stream);
+
 /* Synchronises `stream`, returns DSPARK_EDATA if any call on this workspace
  * found bad data since the last dspark_status() (and clears the word), else
  * DSPARK_OK; DSPARK_EHIP if the stream reports an error. */
@@ -193,7 +263,7 @@ int dspark_status(void* workspace, void* stream);
  * the number of bracketed launches and their summed duration in ms, then
  * clears the record.  Classes: 0 draft GEMM + softmax statistics, 1 draft
  * sample, 2 target row statistics, 3 accept / bonus, 4 residual statistics,
- * 5 residual sample, 6 scheduler. */
+ * 5 residual sample, 6 scheduler, 7 acceptance-pass GEMM. */
 int dspark_profile_enable(int kernel_class, int enabled);
 int dspark_profile_read(int kernel_class, int* launches, double* total_ms);
 

@@ -16,12 +16,13 @@ constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // Workspace: [header | scheduler ranks | tile stats (B + 1 rows) | block stats | request state | slot list |
-// residual tile mass | U rows of the last drawn tokens].  Header words: 0 status, 1 residual slot count, 2 scheduler
+// residual tile mass | U rows of the last drawn tokens | acceptance pass: row
+// statistics, row argmax, tile masses].  Header words: 0 status, 1 residual slot count, 2 scheduler
 // ticket, 3 scheduler first failure.  The header and the scheduler ranks are all
 // that dspark_schedule touches, at offsets that do not depend on V and r.
 constexpr size_t kHeaderBytes = 256;
 struct Layout {
-  size_t header, sched, tstat, bstat, req, slots, rsum, hrows, total;
+  size_t header, sched, tstat, bstat, req, slots, rsum, hrows, rowinfo, rowarg, tmass, total;
   int n_tiles, n_blk;
 };
 
@@ -41,8 +42,9 @@ Layout layout(int B, int gamma, int V, int r) {
   size_t off = 0;
   L.header = off;
   off = align_up(off + kHeaderBytes);
-  L.sched = off;
+  L.sched = off;  // candidate ranks, then Theta of every cut (best-cut rule)
   off = align_up(off + (size_t)B * gamma * sizeof(int32_t));
+  off = align_up(off + ((size_t)B * gamma + 1) * sizeof(double));
   L.tstat = off;  // one spare row (B) takes the records of padding slots
   off = align_up(off + (size_t)(B + 1) * L.n_tiles * sizeof(TileStat));
   L.bstat = off;
@@ -55,6 +57,13 @@ Layout layout(int B, int gamma, int V, int r) {
   off = align_up(off + (size_t)B * L.n_tiles * sizeof(float));
   L.hrows = off;  // U rows of the tokens drawn at the previous block position
   off = align_up(off + (size_t)B * r * sizeof(uint16_t));
+  // acceptance pass: target row statistics and the tile masses of every position
+  L.rowinfo = off;
+  off = align_up(off + (size_t)B * gamma * 2 * sizeof(double));
+  L.rowarg = off;
+  off = align_up(off + (size_t)B * gamma * sizeof(int32_t));
+  L.tmass = off;
+  off = align_up(off + (size_t)B * gamma * L.n_tiles * sizeof(float));
   L.total = off;
   return L;
 }
@@ -126,7 +135,8 @@ size_t dspark_workspace_bytes(int B, int gamma, int V, int r) {
 
 size_t dspark_schedule_workspace_bytes(int B, int gamma) {
   if (!schedule_sizes_ok(B, gamma)) return 0;
-  return align_up(kHeaderBytes) + align_up((size_t)B * gamma * sizeof(int32_t));
+  return align_up(kHeaderBytes) + align_up((size_t)B * gamma * sizeof(int32_t)) +
+         align_up(((size_t)B * gamma + 1) * sizeof(double));
 }
 
 int dspark_draft_round(const void* base_logits, int logits_dtype, const void* U, const void* W,
@@ -176,22 +186,33 @@ int dspark_draft_round(const void* base_logits, int logits_dtype, const void* U,
   return DSPARK_OK;
 }
 
-int dspark_schedule(const float* conf, const double* sps_B, const double* sps_val, int n_points,
-                    int B, int gamma, int32_t* budget, void* workspace, void* stream) {
+int dspark_schedule_ex(const float* conf, const float* tau, const double* sps_B, const double* sps_val,
+                       int n_points, int B, int gamma, int rule, double param, int32_t* budget,
+                       void* workspace, void* stream) {
   if (!schedule_sizes_ok(B, gamma)) return DSPARK_EINVAL;
-  if (n_points < 2 || n_points > 1024) return DSPARK_EINVAL;
-  if (!conf || !sps_B || !sps_val || !budget || !workspace) return DSPARK_EINVAL;
+  if (rule < DSPARK_SCHED_EARLY_STOP || rule > DSPARK_SCHED_THRESHOLD) return DSPARK_EINVAL;
+  const bool table = rule == DSPARK_SCHED_EARLY_STOP || rule == DSPARK_SCHED_ARGMAX;
+  if (table && (n_points < 2 || n_points > 1024 || !sps_B || !sps_val)) return DSPARK_EINVAL;
+  if (!(param == param)) return DSPARK_EINVAL;  // NaN
+  if (!conf || !budget || !workspace) return DSPARK_EINVAL;
   if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return DSPARK_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   ScheduleArgs a{};
-  a.conf = conf, a.sps_B = sps_B, a.sps_val = sps_val, a.n_points = n_points;
-  a.B = B, a.gamma = gamma, a.budget = budget;
+  a.conf = conf, a.tau = tau, a.sps_B = sps_B, a.sps_val = sps_val, a.n_points = table ? n_points : 0;
+  a.B = B, a.gamma = gamma, a.rule = rule, a.param = param, a.budget = budget;
   a.status = at<uint32_t>(workspace, 0);
   a.ticket = a.status + 2, a.stop_enc = a.status + 3;
   a.rank = at<int32_t>(workspace, align_up(kHeaderBytes));
+  a.theta = at<double>(workspace, align_up(kHeaderBytes) + align_up((size_t)B * gamma * sizeof(int32_t)));
   ProfileScope ps(kClsSchedule, s);
   DSPARK_TRY(launch_schedule(a, s));
   return DSPARK_OK;
+}
+
+int dspark_schedule(const float* conf, const double* sps_B, const double* sps_val, int n_points,
+                    int B, int gamma, int32_t* budget, void* workspace, void* stream) {
+  return dspark_schedule_ex(conf, nullptr, sps_B, sps_val, n_points, B, gamma, DSPARK_SCHED_EARLY_STOP, 0.0,
+                            budget, workspace, stream);
 }
 
 int dspark_verify(const void* target_logits, const void* base_logits, int logits_dtype, const void* U,
@@ -245,6 +266,52 @@ int dspark_verify(const void* target_logits, const void* base_logits, int logits
     DSPARK_TRY(launch_residual_select(a, logits_dtype, factor_dtype, s));
   }
   if (debug_residual) DSPARK_TRY(launch_residual_debug(a, logits_dtype, factor_dtype, s));
+  return DSPARK_OK;
+}
+
+int dspark_acceptance(const void* target_logits, const void* base_logits, int logits_dtype, const void* U,
+                      const void* W, int factor_dtype, const int32_t* prev0, const int32_t* draft_tokens,
+                      const double* draft_lse, const float* temperature, int B, int gamma, int V, int r,
+                      double* c_star, void* workspace, void* stream) {
+  if (!sizes_ok(B, gamma, V, r) || !dtype_ok(logits_dtype) || !dtype_ok(factor_dtype)) return DSPARK_EINVAL;
+  if (!target_logits || !base_logits || !U || !W || !prev0 || !draft_tokens || !draft_lse || !temperature ||
+      !c_star || !workspace)
+    return DSPARK_EINVAL;
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return DSPARK_EINVAL;
+  const Layout L = layout(B, gamma, V, r);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  // block statistics of target rows 0..gamma (all of them)
+  VerifyArgs v{};
+  v.target = target_logits, v.temperature = temperature, v.budget = nullptr;
+  v.B = B, v.gamma = gamma, v.V = V, v.r = r, v.n_blk = L.n_blk, v.n_tiles = L.n_tiles;
+  v.bstat = at<BlockStat>(workspace, L.bstat);
+  v.slot_count = at<uint32_t>(workspace, L.header) + 1;
+  v.status = at<uint32_t>(workspace, L.header);
+  DSPARK_TRY(launch_row_stats(v, logits_dtype, s));
+
+  AcceptanceArgs c{};
+  c.bstat = v.bstat, c.temperature = temperature, c.draft = draft_tokens;
+  c.tile_mass = at<float>(workspace, L.tmass);
+  c.rowinfo = at<double2>(workspace, L.rowinfo);
+  c.rowarg = at<int32_t>(workspace, L.rowarg);
+  c.c_star = c_star;
+  c.B = B, c.gamma = gamma, c.V = V, c.n_blk = L.n_blk, c.n_tiles = L.n_tiles;
+  c.status = v.status;
+  DSPARK_TRY(launch_row_info(c, s));
+
+  // tile masses of min(p, q) for every (request, row): the residual-mode pass
+  GemmArgs g{};
+  g.base = base_logits, g.target = target_logits, g.U = U, g.Wt = W, g.prev0 = prev0;
+  g.draft = draft_tokens, g.temperature = temperature, g.draft_lse = draft_lse;
+  g.tv = 1, g.rowinfo = c.rowinfo;
+  g.B = B, g.gamma = gamma, g.V = V, g.r = r, g.n_tiles = L.n_tiles;
+  g.rsum = at<float>(workspace, L.tmass), g.status = v.status;
+  {
+    ProfileScope ps(kClsAcceptance, s);
+    DSPARK_TRY(launch_gemm_stats(g, logits_dtype, factor_dtype, true, s));
+  }
+  DSPARK_TRY(launch_acceptance_finish(c, s));
   return DSPARK_OK;
 }
 

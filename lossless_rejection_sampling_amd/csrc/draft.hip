@@ -24,14 +24,46 @@ typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Residual-mode passes serve two calls.  The residual draw: slots are the
+// requests queued in slot_req[0..*slot_count), each at its rejected row, with the
+// statistics of that target row in req[b]; a tile's value is the mass of
+// max(0, p - q).  The acceptance pass (tv set): slot s is (request s / gamma,
+// row s % gamma) for all B gamma of them, row statistics in rowinfo[s]; a tile's
+// value is the mass of min(p, q).  Outputs go to rsum[(b or s) * n_tiles + tile].
+__device__ __forceinline__ int residual_slots(const GemmArgs& a) {
+  return a.tv ? a.B * a.gamma : (int)*a.slot_count;
+}
+__device__ __forceinline__ void residual_rowstats(const GemmArgs& a, int b, int pos, double& mx, double& lsum) {
+  if (a.tv) {
+    const double2 r = a.rowinfo[(size_t)b * a.gamma + pos];
+    mx = r.x, lsum = r.y;
+  } else {
+    mx = a.req[b].row_max, lsum = a.req[b].row_logsum;
+  }
+}
+__device__ __forceinline__ float residual_mass(const GemmArgs& a, float p, float q) {
+  return a.tv ? fminf(p, q) : fmaxf(p - q, 0.0f);
+}
+__device__ __forceinline__ size_t residual_out(const GemmArgs& a, int b, int pos, int tile) {
+  return (a.tv ? (size_t)b * a.gamma + pos : (size_t)b) * a.n_tiles + tile;
+}
+
+// Largest number of slots a launch must cover (host side).
+inline int max_slots(const GemmArgs& a, bool residual) { return residual && a.tv ? a.B * a.gamma : a.B; }
+
 // Which request, base row and previous token a GEMM slot stands for.
 template <bool RESIDUAL>
 __device__ __forceinline__ void slot_info(const GemmArgs& a, int s, int nslots, int& b, int& pos,
                                           int& prev, bool& valid) {
   valid = s < nslots;
   if (RESIDUAL) {
-    b = valid ? a.slot_req[s] : 0;
-    pos = valid ? a.req[b].n : 0;
+    if (a.tv) {
+      b = valid ? s / a.gamma : 0;
+      pos = valid ? s - b * a.gamma : 0;
+    } else {
+      b = valid ? a.slot_req[s] : 0;
+      pos = valid ? a.req[b].n : 0;
+    }
   } else {
     b = valid ? s : 0;
     pos = a.pos;
@@ -73,7 +105,7 @@ __global__ __launch_bounds__(256) void gemm_stats_mfma(GemmArgs a) {
   const int tile = blockIdx.x;
   const int lane = threadIdx.x & 63;
   const int slot0 = (blockIdx.y * 4 + (threadIdx.x >> 6)) * 64;
-  const int nslots = RESIDUAL ? (int)*a.slot_count : a.B;
+  const int nslots = RESIDUAL ? residual_slots(a) : a.B;
   if (slot0 >= nslots) return;  // uniform across the wavefront
   const int half = lane >> 5, l32 = lane & 31;
   const int V = a.V, r = a.r;
@@ -166,9 +198,10 @@ __global__ __launch_bounds__(256) void gemm_stats_mfma(GemmArgs a) {
       // the draft statistics of the same position.
       float rs = 0.0f;
       if (valid[bb]) {
-        const ReqState st = a.req[rq];
+        double rmax, rlsum;
+        residual_rowstats(a, rq, pos[bb], rmax, rlsum);
         const float invT = 1.0f / T;
-        const float mp = (float)st.row_max, lsp = (float)st.row_logsum;
+        const float mp = (float)rmax, lsp = (float)rlsum;
         const double lse_q = a.draft_lse[(size_t)rq * a.gamma + pos[bb]];
         const float cq = (float)(lse_q - (double)ref / (double)T);
         const TL* trow = static_cast<const TL*>(a.target) + ((size_t)rq * (a.gamma + 1) + pos[bb]) * V;
@@ -182,12 +215,12 @@ __global__ __launch_bounds__(256) void gemm_stats_mfma(GemmArgs a) {
             for (int e = 0; e < 4; ++e) {
               const float p = expf((z[e] - mp) * invT - lsp);
               const float q = expf(x[vb][g * 4 + e] * invT - cq);
-              rs += fmaxf(p - q, 0.0f);
+              rs += residual_mass(a, p, q);
             }
           }
       }
       rs += __shfl_xor(rs, 32);
-      if (half == 0 && valid[bb]) a.rsum[(size_t)rq * a.n_tiles + tile] = rs;
+      if (half == 0 && valid[bb]) a.rsum[residual_out(a, rq, pos[bb], tile)] = rs;
     }
   }
 }
@@ -311,9 +344,10 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const f32x16 (&
     load_tile<TL>(trow, tile * kTile, half, a.V, z);
     float rs = 0.0f;
     if (valid) {
-      const ReqState st = a.req[rq];
+      double rmax, rlsum;
+      residual_rowstats(a, rq, pos, rmax, rlsum);
       const float c = kLog2e / T;
-      const float kp = (float)(((double)st.row_max / (double)T + st.row_logsum) * 1.4426950408889634);
+      const float kp = (float)((rmax / (double)T + rlsum) * 1.4426950408889634);
       const double lse_q = a.draft_lse[(size_t)rq * a.gamma + pos];
       const float kq = (float)((lse_q - (double)ref / (double)T) * 1.4426950408889634);
 #pragma unroll
@@ -323,11 +357,11 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const f32x16 (&
           const float zv = (full || acc_col(tile * kTile, vb, e, half) < a.V) ? z.get(vb, e) : -INFINITY;
           const float p = __builtin_amdgcn_exp2f(fmaf(zv, c, -kp));
           const float q = __builtin_amdgcn_exp2f(fmaf(t[vb][e], c, -kq));
-          rs += fmaxf(p - q, 0.0f);
+          rs += residual_mass(a, p, q);
         }
     }
     rs += __shfl_xor(rs, 32);
-    if (half == 0 && valid) a.rsum[(size_t)rq * a.n_tiles + tile] = rs;
+    if (half == 0 && valid) a.rsum[residual_out(a, rq, pos, tile)] = rs;
   }
 }
 
@@ -363,7 +397,7 @@ __global__ __launch_bounds__(512, 1) void gemm_stats_lds(GemmArgs a) {
   extern __shared__ __attribute__((aligned(1024))) char lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nwaves = blockDim.x >> 6;
   const int half = lane >> 5, l32 = lane & 31;
-  const int nslots = RESIDUAL ? (int)*a.slot_count : a.B;
+  const int nslots = RESIDUAL ? residual_slots(a) : a.B;
   const int sg0 = blockIdx.y * kSlotsPerGroup;
   const int nt = a.n_tiles, G = gridDim.x;
   if (sg0 >= nslots || (int)blockIdx.x >= nt) return;  // uniform across the workgroup
@@ -484,7 +518,7 @@ __global__ __launch_bounds__(512, 1) void gemm_stats_lds(GemmArgs a) {
 template <typename TL, typename TF, bool RESIDUAL>
 __global__ __launch_bounds__(64) void gemm_stats_valu(GemmArgs a) {
   const int tile = blockIdx.x, s = blockIdx.y, lane = threadIdx.x;
-  const int nslots = RESIDUAL ? (int)*a.slot_count : a.B;
+  const int nslots = RESIDUAL ? residual_slots(a) : a.B;
   if (s >= nslots) return;
   int b, pos, prev;
   bool valid;
@@ -511,19 +545,20 @@ __global__ __launch_bounds__(64) void gemm_stats_valu(GemmArgs a) {
       a.tstat[(size_t)b * a.n_tiles + tile] = st;
     }
   } else {
-    const ReqState st = a.req[b];
+    double rmax, rlsum;
+    residual_rowstats(a, b, pos, rmax, rlsum);
     const float invT = 1.0f / T;
     const double lse_q = a.draft_lse[(size_t)b * a.gamma + pos];
     const float cq = (float)(lse_q - (double)ref / (double)T);
     float rv = 0.0f;
     if (ok) {
       const TL* trow = static_cast<const TL*>(a.target) + ((size_t)b * (a.gamma + 1) + pos) * V;
-      const float p = expf((load_logit(trow + v) - (float)st.row_max) * invT - (float)st.row_logsum);
+      const float p = expf((load_logit(trow + v) - (float)rmax) * invT - (float)rlsum);
       const float q = expf(t * invT - cq);
-      rv = fmaxf(p - q, 0.0f);
+      rv = residual_mass(a, p, q);
     }
     const float sum = wave_sum(rv);
-    if (lane == 0) a.rsum[(size_t)b * a.n_tiles + tile] = sum;
+    if (lane == 0) a.rsum[residual_out(a, b, pos, tile)] = sum;
   }
 }
 
@@ -1206,7 +1241,7 @@ __global__ __launch_bounds__(512, 1) void gemm_residual_coalesced(GemmArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, l32 = lane & 31;
   const int vb = wave >> 2, sl = (wave & 3) * 32 + l32;  // column block, slot in the group
-  const int nslots = (int)*a.slot_count;
+  const int nslots = residual_slots(a);
   if (nslots <= 0) return;
   const int ngroups = (nslots + kResSlots - 1) / kResSlots;
   // walkers per slot group, a multiple of 8 so that the workgroups of one tile
@@ -1228,11 +1263,12 @@ __global__ __launch_bounds__(512, 1) void gemm_residual_coalesced(GemmArgs a) {
   double lse_q = 0.0;
   if (valid) {
     T = effective_temp(a.temperature[rq]);
-    const ReqState st = a.req[rq];
-    kp = (float)(((double)st.row_max / (double)T + st.row_logsum) * 1.4426950408889634);
+    double rmax, rlsum;
+    residual_rowstats(a, rq, pos, rmax, rlsum);
+    kp = (float)((rmax / (double)T + rlsum) * 1.4426950408889634);
     lse_q = a.draft_lse[(size_t)rq * a.gamma + pos];
   }
-  if (!(T > 0.0f)) T = 1.0f;  // greedy rows never hold a residual draw
+  if (!(T > 0.0f)) T = 1.0f;  // greedy rows: no residual draw; the acceptance pass ignores their masses
   const float c = kLog2e / T;
   bf16x8 H[R / 16];
   {
@@ -1338,7 +1374,7 @@ __global__ __launch_bounds__(512, 1) void gemm_residual_coalesced(GemmArgs a) {
     for (int e = 0; e < 16; ++e) {
       const float p = __builtin_amdgcn_exp2f(fmaf(zv[e], c, -kp));
       const float q = __builtin_amdgcn_exp2f(fmaf((xv[e] - ref) + acc[e], c, -kq));
-      rs += fmaxf(p - q, 0.0f);
+      rs += residual_mass(a, p, q);
     }
     return reduce_pair32(rs, OpSum{});
   };
@@ -1370,7 +1406,7 @@ __global__ __launch_bounds__(512, 1) void gemm_residual_coalesced(GemmArgs a) {
     }
     wait_vmcnt(0);
     __syncthreads();
-    if (vb == 0 && half == 0 && valid) a.rsum[(size_t)rq * nt + t] = rs + part[c0][sl];
+    if (vb == 0 && half == 0 && valid) a.rsum[residual_out(a, rq, pos, t)] = rs + part[c0][sl];
     t += G;
   };
   for (;;) {
@@ -1399,7 +1435,7 @@ hipError_t launch_residual_coalesced(const GemmArgs& a, hipStream_t s) {
   }
   // enough workgroups to give every CU one, and at least one per tile of every
   // possible slot group when the batch is small
-  const int groups = (a.B + kResSlots - 1) / kResSlots;
+  const int groups = (max_slots(a, true) + kResSlots - 1) / kResSlots;
   const int grid = max(8, min(max_wg, groups * a.n_tiles));
   gemm_residual_coalesced<R><<<grid, 512, lds, s>>>(a);
   return hipGetLastError();
@@ -1421,8 +1457,8 @@ hipError_t launch_pipelined(const GemmArgs& a, hipStream_t s) {
       per_cu = 1;
     max_wg = cus * per_cu;
   }
-  const int groups = (a.B + kSlotsPerGroup - 1) / kSlotsPerGroup;
-  const int threads = 64 * min(kLdsWaves, (a.B + 31) / 32);
+  const int groups = (max_slots(a, RESIDUAL) + kSlotsPerGroup - 1) / kSlotsPerGroup;
+  const int threads = 64 * min(kLdsWaves, (max_slots(a, RESIDUAL) + 31) / 32);
   const int wg_x = max(1, min(a.n_tiles, max_wg / groups));
   gemm_stats_lds<TL, RESIDUAL, R><<<dim3(wg_x, groups), threads, lds, s>>>(a);
   return hipGetLastError();
@@ -1450,11 +1486,11 @@ hipError_t gemm_dispatch(const GemmArgs& a, int factor_dtype, bool vec, hipStrea
     return launch_pipelined<TL, RESIDUAL, 64>(a, s);
   }
   if (factor_dtype == DSPARK_BF16 && a.r % 16 == 0) {
-    const dim3 grid(a.n_tiles, (a.B + 255) / 256);
+    const dim3 grid(a.n_tiles, (max_slots(a, RESIDUAL) + 255) / 256);
     if (vec) gemm_stats_mfma<TL, RESIDUAL, true><<<grid, 256, 0, s>>>(a);
     else gemm_stats_mfma<TL, RESIDUAL, false><<<grid, 256, 0, s>>>(a);
   } else {
-    const dim3 grid(a.n_tiles, a.B);
+    const dim3 grid(a.n_tiles, max_slots(a, RESIDUAL));
     if (factor_dtype == DSPARK_BF16) gemm_stats_valu<TL, uint16_t, RESIDUAL><<<grid, 64, 0, s>>>(a);
     else gemm_stats_valu<TL, float, RESIDUAL><<<grid, 64, 0, s>>>(a);
   }

@@ -10,7 +10,7 @@ namespace dspark {
 
 enum KernelClass : int {
   kClsDraftGemm = 0, kClsDraftSelect = 1, kClsRowStats = 2, kClsAccept = 3,
-  kClsResidualGemm = 4, kClsResidualSelect = 5, kClsSchedule = 6, kNumClasses = 7,
+  kClsResidualGemm = 4, kClsResidualSelect = 5, kClsSchedule = 6, kClsAcceptance = 7, kNumClasses = 8,
 };
 
 // Event bracketing of kernel launches (measurement support).
@@ -40,6 +40,8 @@ struct GemmArgs {
   const ReqState* req;       // [B]                    (residual mode)
   const int32_t* slot_req;   // [B]                    (residual mode)
   const uint32_t* slot_count;//                        (residual mode)
+  int tv;                    // residual mode as the acceptance pass: every (request, row)
+  const double2* rowinfo;    // [B, gamma] target row max and ln-sum-exp    (acceptance pass)
   int B, gamma, V, r, n_tiles, pos;
   TileStat* tstat;           // draft mode output
   float* rsum;               // residual mode output
@@ -103,16 +105,36 @@ hipError_t launch_residual_select(const VerifyArgs& a, int logits_dtype, int fac
 hipError_t launch_residual_debug(const VerifyArgs& a, int logits_dtype, int factor_dtype,
                                  hipStream_t s);
 
+// Acceptance pass helpers: statistics of target rows 0..gamma-1 from their
+// block statistics, and the per-position sum of the tile masses.
+struct AcceptanceArgs {
+  const BlockStat* bstat;    // [B, gamma+1, n_blk]
+  const float* temperature;
+  const int32_t* draft;      // [B, gamma]
+  const float* tile_mass;    // [B * gamma, n_tiles]
+  double2* rowinfo;          // [B, gamma]
+  int32_t* rowarg;           // [B, gamma] lowest index of the row maximum
+  double* c_star;            // [B, gamma]
+  int B, gamma, V, n_blk, n_tiles;
+  uint32_t* status;
+};
+hipError_t launch_row_info(const AcceptanceArgs& a, hipStream_t s);
+hipError_t launch_acceptance_finish(const AcceptanceArgs& a, hipStream_t s);
+
 struct ScheduleArgs {
   const float* conf;
+  const float* tau;          // [gamma] Sequential Temperature Scaling, or NULL
   const double* sps_B;
   const double* sps_val;
   int n_points, B, gamma;
+  int rule;                  // dspark_schedule_rule
+  double param;              // fixed length or score threshold
   int32_t* budget;
   uint32_t* status;
   int32_t* rank;       // [B * gamma] position of each candidate in the admission order
   uint32_t* ticket;    // workgroups finished (returns to 0)
   uint32_t* stop_enc;  // first failing position m as 0x7fffffff - m, 0 if none (returns to 0)
+  double* theta;       // [B * gamma + 1] Theta after the first m candidates (best-cut rule)
 };
 
 hipError_t launch_schedule(const ScheduleArgs& a, hipStream_t s);

@@ -1,21 +1,27 @@
 // Hardware-aware prefix scheduler ("DSpark, la bozza che sa quando fermarsi",
 // section "Verificare meglio, non di più": a_j = prod_{i<=j} c_i, Theta =
 // tau * SPS(B), candidates admitted in decreasing a while Theta grows, with an
-// early stop at the first candidate that does not raise it).
+// early stop at the first candidate that does not raise it), and its variants:
+// Sequential Temperature Scaling of the scores (same section), the production
+// rule that takes the best cut without the early stop (section "Che cosa resta
+// da verificare"), and the fixed-length and fixed-threshold baselines.
 //
 // The admitted prefix is found without sorting.  The position (rank) m of a
 // candidate in the order (Q desc, request asc, position asc) is the number of
 // keys ordered before it, and tau_m - B 2^32 is the sum of their Q; both come
-// from one pass over all keys, in exact integer arithmetic, so the admission
-// test of every candidate is evaluated independently:
-//   1. every workgroup forms all keys in LDS (a lane per request: fp32 prefix
-//      products left to right, Q = floor(a * 2^32)) and the step-time table;
-//   2. 16 lanes per candidate count and sum the keys before it, the test runs in
-//      fp64 in the stated order, and a failing candidate lowers the device-wide
-//      first failure (an atomic max of kNoFail - m);
+// from one pass over all keys, in exact integer arithmetic, so the test of every
+// candidate is evaluated independently:
+//   1. every workgroup forms all keys in LDS (a lane per request: optional
+//      temperature scaling, fp32 prefix products left to right, Q = floor(a *
+//      2^32)) and the step-time table; the fixed and threshold rules finish here;
+//   2. 16 lanes per candidate count and sum the keys before it; the early-stop
+//      rule runs its test in fp64 in the stated order and a failing candidate
+//      lowers the device-wide first failure (an atomic max of kNoFail - m); the
+//      best-cut rule stores Theta after the candidate, theta[m + 1];
 //   3. ranks go to the workspace; the last workgroup to finish (a ticket
-//      counter) sets budget[b] = number of b's candidates ranked before the
-//      first failure, and resets the counter and the failure word.
+//      counter) finds the cut (first failure, or the first largest Theta), sets
+//      budget[b] = number of b's candidates ranked before it, and resets the
+//      counter and the failure word.
 #include <math.h>
 
 #include "dspark.h"
@@ -48,34 +54,59 @@ __device__ double step_time(double N, const double* Bs, const double* ts, int np
   return ts[lo] + inc;
 }
 
+// Sequential Temperature Scaling of one score: 1 / (1 + exp(-z / tau)),
+// z = ln c - ln(1 - c), in fp64 from the fp32 score, rounded once to fp32 and
+// kept strictly inside (0, 1).
+__device__ float scaled_score(float c, float tau) {
+  const double x = (double)c;
+  const double z = log(x) - log1p(-x);
+  double y = 1.0 / (1.0 + exp(-z / (double)tau));
+  y = fmin(fmax(y, 0x1p-126), 0x1.fffffep-1);
+  return (float)y;
+}
+
 __global__ __launch_bounds__(kThreads) void schedule_kernel(ScheduleArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   __shared__ int s_last;
+  __shared__ double s_best[kThreads / 64];
+  __shared__ int s_bestm[kThreads / 64];
   const int tid = threadIdx.x, B = a.B, gamma = a.gamma, np = a.n_points;
   const int nk = B * gamma;
   uint32_t* const qinv = reinterpret_cast<uint32_t*>(smem);  // 0xFFFFFFFF - Q, candidate b * gamma + j
   double* const tB = reinterpret_cast<double*>(smem + ((nk * 4 + 15) & ~15));
   double* const tT = tB + np;
+  const bool ranked = a.rule == DSPARK_SCHED_EARLY_STOP || a.rule == DSPARK_SCHED_ARGMAX;
 
   for (int i = tid; i < np; i += kThreads) {
     tB[i] = a.sps_B[i];
     tT[i] = 1.0 / a.sps_val[i];
   }
   bool bad = false;
+  const float thr = (float)a.param;
   for (int b = tid; b < B; b += kThreads) {
     float acc = 1.0f;
+    int lead = 0;  // leading positions above the threshold
+    bool run = true;
     for (int j = 0; j < gamma; ++j) {
       float cj = a.conf[(size_t)b * gamma + j];
       if (!(cj > 0.0f && cj < 1.0f)) {
         bad = true;
         cj = cj > 0.0f ? 0x1.fffffep-1f : 0x1p-126f;  // clamp into (0, 1); NaN -> tiny
       }
+      if (a.tau) cj = scaled_score(cj, a.tau[j]);
+      run = run && cj > thr;
+      lead += run ? 1 : 0;
       acc = acc * cj;
       const uint32_t q = (uint32_t)floor((double)acc * 4294967296.0);
       qinv[b * gamma + j] = 0xFFFFFFFFu - q;
     }
+    if (blockIdx.x == 0 && !ranked) {
+      const int fixed = (int)fmin(fmax(a.param, 0.0), (double)gamma);
+      a.budget[b] = a.rule == DSPARK_SCHED_FIXED ? fixed : lead;
+    }
   }
   if (bad && blockIdx.x == 0) flag_status(a.status, kBadConf);
+  if (!ranked) return;  // uniform: the fixed and threshold rules are done
   __syncthreads();
 
   // candidate i: keys before it and the sum of their Q
@@ -98,11 +129,17 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(ScheduleArgs a) {
     const unsigned long long q = 0xFFFFFFFFull - qi;
     const unsigned long long T = ((unsigned long long)B << 32) + tau;
     const double N = (double)(B + (int)cnt);
-    const double lhs = (double)(T + q) * step_time(N, tB, tT, np);
-    const double rhs = (double)T * step_time(N + 1.0, tB, tT, np);
-    if (!(lhs > rhs)) atomicMax(a.stop_enc, kNoFail - cnt);
+    if (a.rule == DSPARK_SCHED_EARLY_STOP) {
+      const double lhs = (double)(T + q) * step_time(N, tB, tT, np);
+      const double rhs = (double)T * step_time(N + 1.0, tB, tT, np);
+      if (!(lhs > rhs)) atomicMax(a.stop_enc, kNoFail - cnt);
+    } else {
+      a.theta[cnt + 1] = (double)(T + q) / step_time(N + 1.0, tB, tT, np);
+    }
     a.rank[i] = (int)cnt;
   }
+  if (a.rule == DSPARK_SCHED_ARGMAX && blockIdx.x == 0 && tid == 0)
+    a.theta[0] = (double)((unsigned long long)B << 32) / step_time((double)B, tB, tT, np);
 
   // the last workgroup to finish turns ranks into budgets
   __threadfence();
@@ -111,8 +148,26 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(ScheduleArgs a) {
   __syncthreads();
   if (!s_last) return;
   __threadfence();
-  const uint32_t enc = __hip_atomic_load(a.stop_enc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const int stop = enc ? (int)(kNoFail - enc) : nk;
+  int stop;
+  if (a.rule == DSPARK_SCHED_EARLY_STOP) {
+    const uint32_t enc = __hip_atomic_load(a.stop_enc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    stop = enc ? (int)(kNoFail - enc) : nk;
+  } else {
+    // the first largest Theta over the cuts m = 0..nk
+    double best = -1.0;
+    int bm = 0x7fffffff;
+    for (int m = tid; m <= nk; m += kThreads) {
+      const double th = __builtin_nontemporal_load(a.theta + m);
+      if (th > best) best = th, bm = m;  // m increases: ties keep the first
+    }
+    wave_argmax(best, bm);
+    if ((tid & 63) == 0) s_best[tid >> 6] = best, s_bestm[tid >> 6] = bm;
+    __syncthreads();
+    best = -1.0, bm = 0x7fffffff;
+    for (int w = 0; w < kThreads / 64; ++w)
+      if (s_best[w] > best || (s_best[w] == best && s_bestm[w] < bm)) best = s_best[w], bm = s_bestm[w];
+    stop = index_or(bm, nk + 1, 0);
+  }
   for (int b = tid; b < B; b += kThreads) {
     int n = 0;
     for (int j = 0; j < gamma; ++j) n += __builtin_nontemporal_load(a.rank + b * gamma + j) < stop ? 1 : 0;
@@ -129,7 +184,8 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(ScheduleArgs a) {
 hipError_t launch_schedule(const ScheduleArgs& a, hipStream_t s) {
   const int nk = a.B * a.gamma;
   const size_t lds = (size_t)((nk * 4 + 15) & ~15) + (size_t)a.n_points * 16;
-  const int groups = (nk + kCandPerGroup - 1) / kCandPerGroup;
+  const bool ranked = a.rule == DSPARK_SCHED_EARLY_STOP || a.rule == DSPARK_SCHED_ARGMAX;
+  const int groups = ranked ? (nk + kCandPerGroup - 1) / kCandPerGroup : 1;
   schedule_kernel<<<groups, kThreads, lds, s>>>(a);
   return hipGetLastError();
 }

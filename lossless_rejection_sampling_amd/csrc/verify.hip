@@ -433,6 +433,43 @@ __global__ __launch_bounds__(64) void residual_debug_kernel(VerifyArgs a) {
   a.debug_residual[(size_t)b * a.V + v] = (float)(st.res_mass > 0.0 ? rv / st.res_mass : p);
 }
 
+// ---------------------------------------------------------------------------
+// Analytic acceptance c*_k = sum_v min(p_k(v), q_k(v)) = 1 - TV(p_k, q_k) at
+// every block position ("DSpark, la bozza ...", section "Verificare meglio, non
+// di più", eq. c*_k): the tile masses come from the residual-mode GEMM pass in
+// its acceptance form; these two kernels prepare the target row statistics and
+// add the tile masses up (one wavefront per (request, row)).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void row_info_kernel(AcceptanceArgs a) {
+  const int s = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (s >= a.B * a.gamma) return;  // uniform across the wavefront
+  const int b = s / a.gamma, j = s - b * a.gamma;
+  const float Tf = checked_temp(a.temperature[b], a.status);
+  const bool greedy = !(Tf > 0.0f);
+  const RowInfo ri = row_info(a.bstat + ((size_t)b * (a.gamma + 1) + j) * a.n_blk, a.n_blk, greedy,
+                              greedy ? 0.0 : 1.0 / (double)Tf, lane);
+  if (lane == 0) {
+    a.rowinfo[s] = make_double2(ri.M, ri.logS);
+    a.rowarg[s] = ri.arg;
+  }
+}
+
+__global__ __launch_bounds__(256) void acceptance_finish_kernel(AcceptanceArgs a) {
+  const int s = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (s >= a.B * a.gamma) return;  // uniform across the wavefront
+  const int b = s / a.gamma;
+  if (!(effective_temp(a.temperature[b]) > 0.0f)) {
+    // greedy: both distributions are one-hot at their lowest-index maximum
+    if (lane == 0) a.c_star[s] = a.draft[s] == a.rowarg[s] ? 1.0 : 0.0;
+    return;
+  }
+  const float* m = a.tile_mass + (size_t)s * a.n_tiles;
+  double acc = 0.0;
+  for (int t = lane; t < a.n_tiles; t += 64) acc += (double)m[t];
+  acc = wave_sum(acc);
+  if (lane == 0) a.c_star[s] = acc;
+}
+
 }  // namespace
 
 hipError_t launch_row_stats(const VerifyArgs& a, int logits_dtype, hipStream_t s) {
@@ -475,6 +512,16 @@ hipError_t launch_residual_debug(const VerifyArgs& a, int logits_dtype, int fact
     if (factor_dtype == DSPARK_BF16) residual_debug_kernel<float, uint16_t><<<grid, 64, 0, s>>>(a);
     else residual_debug_kernel<float, float><<<grid, 64, 0, s>>>(a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_row_info(const AcceptanceArgs& a, hipStream_t s) {
+  row_info_kernel<<<(a.B * a.gamma + 3) / 4, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_acceptance_finish(const AcceptanceArgs& a, hipStream_t s) {
+  acceptance_finish_kernel<<<(a.B * a.gamma + 3) / 4, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -22,8 +22,9 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "dspark.h")
 
 DSPARK_BF16, DSPARK_F32 = 0, 1
 DSPARK_OK, DSPARK_EINVAL, DSPARK_EHIP, DSPARK_EDATA = 0, -1, -2, -3
+SCHED_RULES = {"early_stop": 0, "argmax": 1, "fixed": 2, "threshold": 3}
 KERNEL_CLASSES = {"draft_gemm": 0, "draft_select": 1, "row_stats": 2, "accept": 3,
-                  "residual_gemm": 4, "residual_select": 5, "schedule": 6}
+                  "residual_gemm": 4, "residual_select": 5, "schedule": 6, "acceptance": 7}
 
 
 class DsparkError(RuntimeError):
@@ -43,8 +44,10 @@ _SIG = {
     "dspark_draft_round": (_I, [_P, _I, _P, _P, _I, _P, _P, ctypes.c_uint64, _P,
                                 _I, _I, _I, _I, _P, _P, _P, _P, _P]),
     "dspark_schedule": (_I, [_P, _P, _P, _I, _I, _I, _P, _P, _P]),
+    "dspark_schedule_ex": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_double, _P, _P, _P]),
     "dspark_verify": (_I, [_P, _P, _I, _P, _P, _I, _P, _P, _P, _P, _P, _P, ctypes.c_uint64, _P,
                            _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]),
+    "dspark_acceptance": (_I, [_P, _P, _I, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _P]),
     "dspark_status": (_I, [_P, _P]),
     "dspark_profile_enable": (_I, [_I, _I]),
     "dspark_profile_read": (_I, [_I, ctypes.POINTER(_I), ctypes.POINTER(ctypes.c_double)]),
@@ -149,6 +152,20 @@ def dspark_schedule(conf, sps_B, sps_val, budget, workspace, stream=None):
     _check("dspark_schedule", rc)
 
 
+def dspark_schedule_ex(conf, tau, sps_B, sps_val, rule, param, budget, workspace, stream=None):
+    """rule: a key of SCHED_RULES (or its code); tau: [gamma] float32 or None;
+    sps_B / sps_val may be None for the fixed and threshold rules."""
+    B, gamma = conf.shape
+    code = SCHED_RULES[rule] if isinstance(rule, str) else int(rule)
+    n = int(sps_B.numel()) if sps_B is not None else 0
+    rc = lib().dspark_schedule_ex(
+        _dev(conf, "conf", torch.float32), _dev(tau, "tau", torch.float32, optional=True),
+        _dev(sps_B, "sps_B", torch.float64, optional=True), _dev(sps_val, "sps_val", torch.float64, optional=True),
+        n, B, gamma, code, float(param), _dev(budget, "budget", torch.int32),
+        _dev(workspace, "workspace", torch.uint8), _stream(stream))
+    _check("dspark_schedule_ex", rc)
+
+
 def dspark_verify(target_logits, base_logits, U, W, prev0, draft_tokens, draft_logq, draft_lse,
                   budget, temperature, seed, pos_offset, out_tokens, num_accepted, num_emitted,
                   workspace, debug_logp_logq=None, debug_residual=None, stream=None):
@@ -169,6 +186,22 @@ def dspark_verify(target_logits, base_logits, U, W, prev0, draft_tokens, draft_l
         _dev(debug_residual, "debug_residual", torch.float32, optional=True),
         _dev(workspace, "workspace", torch.uint8), _stream(stream))
     _check("dspark_verify", rc)
+
+
+def dspark_acceptance(target_logits, base_logits, U, W, prev0, draft_tokens, draft_lse, temperature,
+                      c_star, workspace, stream=None):
+    """c_star [B, gamma] float64 out: sum_v min(p_k, q_k) of every drafted position."""
+    B, gamma, V = base_logits.shape
+    r = U.shape[1]
+    if tuple(target_logits.shape) != (B, gamma + 1, V) or target_logits.dtype != base_logits.dtype:
+        raise ValueError("target_logits must be [B, gamma+1, V] with the dtype of base_logits")
+    rc = lib().dspark_acceptance(
+        _dev(target_logits, "target_logits"), _dev(base_logits, "base_logits"), _dtype_code(base_logits),
+        _dev(U, "U"), _dev(W, "W"), _dtype_code(U), _dev(prev0, "prev0", torch.int32),
+        _dev(draft_tokens, "draft_tokens", torch.int32), _dev(draft_lse, "draft_lse", torch.float64),
+        _dev(temperature, "temperature", torch.float32), B, gamma, V, r,
+        _dev(c_star, "c_star", torch.float64), _dev(workspace, "workspace", torch.uint8), _stream(stream))
+    _check("dspark_acceptance", rc)
 
 
 def dspark_status(workspace, stream=None) -> int:

@@ -292,6 +292,150 @@ def schedule(conf, sps_B, sps_val) -> ScheduleResult:
     return ScheduleResult(budget, admitted, min_gap)
 
 
+def analytic_acceptance(target, base, U, W, prev0, draft_tokens, temperature) -> np.ndarray:
+    """c*[b, k-1] = sum_v min(p_k(v), q_k(v)) = 1 - (1/2) ||p_k - q_k||_1 for
+    k = 1..gamma ("DSpark, la bozza ...", section "Verificare meglio, non di
+    più", eq. c*_k): the probability that position k's accept test passes
+    given the drafted prefix x_1..x_{k-1} was accepted.  p_k = softmax(target
+    row k-1 / T); q_k = softmax(draft logits of position k with previous token
+    x_{k-1} / T).  Greedy requests: both are one-hot at their lowest-index
+    maximum, so c* is 1 when the draft token is the target argmax, else 0."""
+    target, base = _f64(target), _f64(base)
+    B, gamma, V = base.shape
+    U, W = _f64(U), _f64(W)
+    out = np.zeros((B, gamma))
+    for b in range(B):
+        T = effective_temperature(temperature[b])
+        xs = [int(prev0[b])] + [int(t) for t in draft_tokens[b]]
+        for k in range(1, gamma + 1):
+            z = target[b, k - 1]
+            if T == 0.0:
+                out[b, k - 1] = 1.0 if xs[k] == argmax_first(z) else 0.0
+                continue
+            p = softmax(z / T)
+            q = softmax(draft_logits(base[b, k - 1], U, W, xs[k - 1]) / T)
+            out[b, k - 1] = float(np.minimum(p, q).sum())
+    return out
+
+
+# ----------------------------------------------------------------------------
+# Variants of the verify-budget rule ("DSpark, la bozza ...", sections
+# "Verificare meglio, non di più" and "Che cosa resta da verificare"; "DSpark :
+# le pari de DeepSeek ...", section "Vérifier seulement ce qui compte"):
+#   * Sequential Temperature Scaling rescales each position's score,
+#     c' = sigma(logit(c) / tau_k), before the products;
+#   * the production scheduler takes the cut with the largest Theta over the
+#     whole sorted list (no early stop), on scores two steps old;
+#   * the baselines the pages compare against: a fixed draft length (MTP-1,
+#     MTP-3, MTP-5) and a fixed confidence threshold ("verify while the
+#     confidence exceeds 0.7").
+# ----------------------------------------------------------------------------
+
+RULES = ("early_stop", "argmax", "fixed", "threshold")
+_F32_LO, _F32_HI = float(np.float32(2.0 ** -126)), float(np.nextafter(np.float32(1.0), np.float32(0.0)))
+
+
+def calibrate_scores(conf, tau):
+    """Sequential Temperature Scaling applied to raw scores: for position k,
+    c' = 1 / (1 + exp(-z / tau_k)), z = ln c - ln(1 - c), evaluated in fp64 from
+    the fp32 score and rounded once to fp32, then kept strictly inside (0, 1).
+    Returns (c', near) where `near` marks values whose fp64 result lies within
+    1e-12 (relative) of an fp32 rounding boundary: another correctly rounded
+    evaluation of the same formula may round those the other way."""
+    c = np.asarray(conf, dtype=np.float32)
+    tau = np.asarray(tau, dtype=np.float32)
+    out = np.empty_like(c)
+    near = np.zeros(c.shape, dtype=bool)
+    for b in range(c.shape[0]):
+        for k in range(c.shape[1]):
+            x = float(c[b, k])
+            z = math.log(x) - math.log1p(-x)
+            y = 1.0 / (1.0 + math.exp(-z / float(tau[k])))
+            y = min(max(y, _F32_LO), _F32_HI)
+            f = np.float32(y)
+            out[b, k] = f
+            lo, hi = sorted((float(f), float(np.nextafter(f, np.float32(2.0) if float(f) < y else np.float32(0.0)))))
+            mid = 0.5 * (lo + hi)
+            near[b, k] = abs(y - mid) <= 1e-12 * y
+    return out, near
+
+
+def _sorted_candidates(a):
+    B, gamma = a.shape
+    Q = np.floor(a.astype(np.float64) * 2.0 ** 32).astype(np.int64)
+    return Q, sorted((-int(Q[b, j]), b, j) for b in range(B) for j in range(gamma))
+
+
+def schedule_rule(conf, sps_B, sps_val, rule: str = "early_stop", param: float = 0.0, tau=None) -> ScheduleResult:
+    """Budgets under one of RULES, optionally after Sequential Temperature
+    Scaling with per-position temperatures `tau`.
+      early_stop  the greedy prefix scheduler with its first-failure stop
+      argmax      the cut m* maximising Theta_m = tau_m / t(N_m) over m = 0..B gamma
+                  along the same sorted list (tau_m = B 2^32 + the first m Q,
+                  N_m = B + m; Theta as one correctly rounded fp64 division;
+                  ties go to the smaller m)
+      fixed       L_b = min(param, gamma) for every request
+      threshold   L_b = number of leading positions whose score exceeds param
+    """
+    if rule not in RULES:
+        raise ValueError(f"unknown rule {rule}")
+    c = np.asarray(conf, dtype=np.float32)
+    if tau is not None:
+        c, _ = calibrate_scores(c, tau)
+    B, gamma = c.shape
+    if rule == "early_stop":
+        return schedule(c, sps_B, sps_val)
+    if rule == "fixed":
+        L = int(min(max(int(param), 0), gamma))
+        return ScheduleResult(np.full(B, L, dtype=np.int32), B * L, math.inf)
+    if rule == "threshold":
+        thr = np.float32(param)
+        budget = np.zeros(B, dtype=np.int32)
+        for b in range(B):
+            n = 0
+            while n < gamma and c[b, n] > thr:
+                n += 1
+            budget[b] = n
+        return ScheduleResult(budget, int(budget.sum()), math.inf)
+    # argmax
+    sps_B = [float(v) for v in sps_B]
+    t_tab = [1.0 / float(v) for v in sps_val]
+    a = prefix_survival(c)
+    Q, cand = _sorted_candidates(a)
+    tau_m = B << 32
+    best, best_m = float(tau_m) / step_time(float(B), sps_B, t_tab), 0
+    thetas = [best]
+    for m, (negq, b, j) in enumerate(cand, start=1):
+        tau_m += -negq
+        th = float(tau_m) / step_time(float(B + m), sps_B, t_tab)
+        thetas.append(th)
+        if th > best:
+            best, best_m = th, m
+    budget = np.zeros(B, dtype=np.int32)
+    for negq, b, j in cand[:best_m]:
+        budget[b] = max(budget[b], j + 1)
+    # the closest call: the best Theta against every other cut's
+    others = [t for i, t in enumerate(thetas) if i != best_m]
+    gap = min((abs(best - t) / best for t in others), default=math.inf)
+    return ScheduleResult(budget, best_m, gap)
+
+
+def expected_theta(conf, budget, sps_B, sps_val, tau=None):
+    """Expected tokens per round tau = sum_b (1 + sum_{j <= L_b} a_{b,j}), verify
+    batch N = sum_b (1 + L_b) tokens and Theta = tau / t(N) in fp64: the measure
+    the pages compare schedulers by (Theta = tau SPS(B))."""
+    c = np.asarray(conf, dtype=np.float32)
+    if tau is not None:
+        c, _ = calibrate_scores(c, tau)
+    a = prefix_survival(c).astype(np.float64)
+    budget = np.asarray(budget)
+    B = a.shape[0]
+    tok = float(B) + sum(float(a[b, :int(budget[b])].sum()) for b in range(B))
+    N = float(B + int(budget.sum()))
+    t = step_time(N, [float(v) for v in sps_B], [1.0 / float(v) for v in sps_val])
+    return tok, N, tok / t
+
+
 # ----------------------------------------------------------------------------
 # A whole round and its flags.
 # ----------------------------------------------------------------------------

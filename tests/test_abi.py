@@ -25,7 +25,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_error_strings(lib):
-    assert ds.dspark_abi_version() == 2
+    assert ds.dspark_abi_version() == 3
     assert ds.error_string(0) == "ok"
     assert "argument" in ds.error_string(-1)
     assert "device" in ds.error_string(-3)
@@ -39,9 +39,11 @@ def test_workspace_size_rules(lib):
     assert ds.dspark_workspace_bytes(4, 5, 0, 8) == 0
     small = ds.dspark_workspace_bytes(4, 4, 1024, 16)
     assert small % 256 == 0 and small < ds.dspark_workspace_bytes(8, 4, 1024, 16)
-    # the scheduler's own part: header + one int per candidate, within the full workspace
-    assert ds.dspark_schedule_workspace_bytes(256, 5) == 256 + 256 * 5 * 4
-    assert ds.dspark_schedule_workspace_bytes(1024, 8) == 256 + 1024 * 8 * 4
+    # the scheduler's own part: header + one int per candidate + one float64 per
+    # cut (each part 256-byte aligned), within the full workspace
+    up = lambda x: (x + 255) // 256 * 256
+    assert ds.dspark_schedule_workspace_bytes(256, 5) == 256 + up(256 * 5 * 4) + up((256 * 5 + 1) * 8)
+    assert ds.dspark_schedule_workspace_bytes(1024, 8) == 256 + up(1024 * 8 * 4) + up((1024 * 8 + 1) * 8)
     assert ds.dspark_schedule_workspace_bytes(1024, 9) == 0      # B * gamma > 8192
     assert ds.dspark_schedule_workspace_bytes(0, 4) == 0
     for B, g, V, r in [(1, 1, 8, 1), (7, 16, 65, 20), (256, 5, 151936, 256)]:
@@ -71,5 +73,10 @@ def test_host_argument_checks_return_einval(lib):
     # scheduler limits: too many candidates, too few table points
     assert lib.dspark_schedule(fake, fake, fake, 16, 1025, 8, fake, fake, nul) == ds.DSPARK_EINVAL
     assert lib.dspark_schedule(fake, fake, fake, 1, 4, 4, fake, fake, nul) == ds.DSPARK_EINVAL
+    # unknown rule, NaN parameter, missing table for a rule that reads it
+    ex = lib.dspark_schedule_ex
+    assert ex(fake, nul, fake, fake, 16, 4, 4, 9, 0.0, fake, fake, nul) == ds.DSPARK_EINVAL
+    assert ex(fake, nul, nul, nul, 0, 4, 4, 2, float("nan"), fake, fake, nul) == ds.DSPARK_EINVAL
+    assert ex(fake, nul, nul, nul, 0, 4, 4, 1, 0.0, fake, fake, nul) == ds.DSPARK_EINVAL
     assert lib.dspark_status(nul, nul) == ds.DSPARK_EINVAL
     assert lib.dspark_profile_enable(99, 1) == ds.DSPARK_EINVAL

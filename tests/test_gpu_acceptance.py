@@ -1,0 +1,91 @@
+"""Analytic acceptance pass (dspark_acceptance through the C ABI) against the
+oracle's sum_v min(p_k, q_k): each side drafts on its own from the same seeded
+inputs, and for every request whose drafted block the two agree on (all of
+them outside oracle-flagged requests) every position's c* must agree within
+1e-6 absolute + 1e-4 relative.  Small rounds span several tiles and a ragged
+tail; the full-size workloads run the whole batch on the GPU and check a
+sample of requests."""
+
+import numpy as np
+import pytest
+import torch
+
+from lossless_rejection_sampling_amd import dspark as ds
+from lossless_rejection_sampling_amd import round as rd
+from lossless_rejection_sampling_amd import workloads as wl
+from oracle import dspark as od
+
+from parity import ATOL_P, RTOL_P, say
+
+pytestmark = [
+    pytest.mark.gpu,
+    pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU"),
+]
+
+DEV = "cuda"
+
+
+def _gpu(rnd):
+    buf = rd.allocate(rnd)
+    rd.draft(rnd, buf)
+    c = torch.full((rnd.B, rnd.gamma), float("nan"), dtype=torch.float64, device=DEV)
+    ds.dspark_acceptance(rnd.target, rnd.base, rnd.U, rnd.Wt, rnd.prev0, buf.draft_tokens, buf.draft_lse,
+                         rnd.temperature, c, buf.workspace)
+    torch.cuda.synchronize()
+    assert ds.dspark_status(buf.workspace) == ds.DSPARK_OK
+    return buf.draft_tokens.cpu().numpy(), c.cpu().numpy()
+
+
+def _check(rnd, idx, name):
+    say(f"[{name}] B={rnd.B} gamma={rnd.gamma} V={rnd.V} r={rnd.r} dtype={rnd.base.dtype} sample={len(idx)}")
+    g_draft, g_c = _gpu(rnd)
+    h = wl.to_host
+    t = torch.as_tensor(idx, dtype=torch.long, device=rnd.base.device)
+    pick = lambda x: None if x is None else h(x.index_select(0, t))
+    base, target = pick(rnd.base), pick(rnd.target)
+    prev0, T, off = pick(rnd.prev0), pick(rnd.temperature), pick(rnd.pos_offset)
+    U, W = h(rnd.U), h(rnd.W)
+    dr = od.draft_round(base, U, W, prev0, T, rnd.seed, off, req_ids=idx)
+    ref = od.analytic_acceptance(target, base, U, W, prev0, dr.tokens, T)
+    flagged = dr.margin.min(axis=1) < od.MARGIN_FLAG
+    same = np.all(g_draft[idx] == dr.tokens, axis=1)
+    assert np.all(same | flagged), f"{name}: drafts differ on unflagged requests"
+    ok = same & ~flagged
+    assert ok.sum() >= 0.9 * len(idx)
+    got = g_c[idx][ok]
+    want = ref[ok]
+    err = np.abs(got - want)
+    assert np.all(np.isfinite(got)) and np.all((got >= -1e-6) & (got <= 1 + 1e-6))
+    assert np.all(err <= ATOL_P + RTOL_P * np.abs(want)), f"{name}: max err {err.max():.3g}"
+    return g_c
+
+
+@pytest.mark.parametrize("case", [
+    dict(B=24, gamma=5, V=1000, r=32, dtype=torch.float32, fdt=torch.bfloat16, temps=(1.0, 0.7, 1.5, 0.0)),
+    dict(B=24, gamma=4, V=1000, r=32, dtype=torch.bfloat16, fdt=torch.bfloat16, temps=(1.0, 0.0)),
+    dict(B=16, gamma=4, V=9000, r=16, dtype=torch.float32, fdt=torch.float32, temps=(1.0, 0.8)),
+    dict(B=8, gamma=6, V=65, r=20, dtype=torch.float32, fdt=torch.bfloat16, temps=(0.9,)),
+    dict(B=70, gamma=3, V=9000, r=256, dtype=torch.bfloat16, fdt=torch.bfloat16, temps=(1.0, 0.0)),
+    dict(B=300, gamma=2, V=3001, r=128, dtype=torch.bfloat16, fdt=torch.bfloat16, temps=(1.0, 1.2)),
+    dict(B=130, gamma=3, V=5000, r=128, dtype=torch.bfloat16, fdt=torch.bfloat16, temps=(1.0,)),
+])
+def test_small_rounds(case):
+    rnd = wl.small_random(case["B"], case["gamma"], case["V"], case["r"], device=DEV, seed=case["B"] + 7 * case["V"],
+                          dtype=case["dtype"], factor_dtype=case["fdt"], temps=case["temps"])
+    _check(rnd, np.arange(rnd.B), f"acceptance_{case['B']}x{case['gamma']}x{case['V']}_r{case['r']}")
+
+
+def test_identical_draft_gives_one():
+    rnd = wl.small_random(32, 4, 3000, 16, device=DEV, seed=3, temps=(1.0, 0.6))
+    rnd.base = rnd.target[:, :4].contiguous()
+    rnd.Wt = torch.zeros_like(rnd.Wt)
+    _, c = _gpu(rnd)
+    assert np.allclose(c, 1.0, atol=1e-5)
+
+
+def test_headline_b256_sample():
+    _check(wl.headline(device=DEV), np.array([0, 37, 101, 255]), "acceptance_headline_B256")
+
+
+def test_block_length_g8_sample():
+    _check(wl.block_length(8, device=DEV), np.array([3, 128, 254]), "acceptance_block_length_g8")
