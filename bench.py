@@ -193,6 +193,8 @@ def main():
     roof["kernel"] = dominant
     roof["avg_us"] = dom_avg_s * 1e6
 
+    extras = measure_extras(rounds[0], bufs[0])
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(base_round, budgets, args.cpu_seconds)
@@ -218,8 +220,77 @@ def main():
         "roofline": roof,
         "kernels": kernels,
         "cpu_baseline": cpu,
+        "extras": extras,
     }
     print(json.dumps(line), flush=True)
+
+
+def measure_extras(rnd, buf, reps=5):
+    """Outside the timed round: (1) the analytic-acceptance pass (c*_k of every
+    drafted position) on the same inputs, its GEMM launch timed with HIP events
+    and priced against HBM; (2) Theta = tau SPS(B) of the verify budgets each
+    scheduler rule grants for the round's scores (budgets computed on the GPU);
+    (3) Sequential Temperature Scaling on synthetic overconfident scores whose
+    labels are the acceptance pass's c*: ECE before and after, temperatures
+    fitted on half of the requests and scored on the other half."""
+    import numpy as np
+    import torch
+
+    from lossless_rejection_sampling_amd import analysis, calibration
+    from lossless_rejection_sampling_amd import dspark as ds
+
+    B, g, V, r = rnd.B, rnd.gamma, rnd.V, rnd.r
+    c = torch.empty((B, g), dtype=torch.float64, device="cuda")
+    run = lambda: ds.dspark_acceptance(rnd.target, rnd.base, rnd.U, rnd.Wt, rnd.prev0, buf.draft_tokens,
+                                       buf.draft_lse, rnd.temperature, c, buf.workspace)
+    run()
+    torch.cuda.synchronize()
+    cls = ds.KERNEL_CLASSES["acceptance"]
+    ds.dspark_profile_enable(cls, True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    n, ms = ds.dspark_profile_read(cls)
+    ds.dspark_profile_enable(cls, False)
+    es = rnd.base.element_size()
+    n_tiles = -(-V // 64)
+    # target rows 0..gamma-1 and backbone rows once, W2 once, tile masses written
+    alg = 2 * B * g * V * es + V * r * rnd.U.element_size() + B * g * n_tiles * 4
+    gemm_us = 1e3 * ms / max(n, 1)
+    acc = {"call_us": 1e3 * e0.elapsed_time(e1) / reps, "gemm_us": gemm_us,
+           "gemm_algorithmic_bytes": alg, "gemm_GB_s": alg / gemm_us / 1e3,
+           "gemm_frac_hbm": alg / gemm_us / 1e3 / HBM_PEAK_GBS,
+           "mean_c_star": float(c.mean().item())}
+
+    conf = rnd.conf
+    tB = torch.as_tensor(rnd.sps_B, dtype=torch.float64, device="cuda")
+    tS = torch.as_tensor(rnd.sps_val, dtype=torch.float64, device="cuda")
+    ws = torch.zeros(ds.dspark_schedule_workspace_bytes(B, g), dtype=torch.uint8, device="cuda")
+    budget = torch.empty(B, dtype=torch.int32, device="cuda")
+    sched = {}
+    for name, rule, p in [("dspark_early_stop", "early_stop", 0), ("production_best_cut", "argmax", 0),
+                          ("mtp1", "fixed", 1), ("mtp3", "fixed", 3), ("mtp5", "fixed", 5),
+                          ("threshold_0.7", "threshold", 0.7)]:
+        ds.dspark_schedule_ex(conf, None, tB, tS, rule, p, budget, ws)
+        L = budget.cpu().numpy()
+        tau, N, theta = analysis.expected_theta(conf.cpu().numpy(), L, rnd.sps_B, rnd.sps_val)
+        sched[name] = {"verified_per_round": int(L.sum()), "expected_tokens": tau, "batch_tokens": N,
+                       "theta_tokens_per_s": theta}
+
+    cs = c.cpu().numpy()
+    rng = np.random.default_rng(17)
+    z = np.log(np.clip(cs, 1e-9, 1 - 1e-9)) - np.log1p(-np.clip(cs, 1e-9, 1 - 1e-9))
+    raw = 1 / (1 + np.exp(-(2.5 * z + rng.normal(0, 0.3, size=z.shape))))
+    half = B // 2
+    tau_k = calibration.fit_sts(raw[:half], cs[:half])
+    sts = {"temperatures": [float(t) for t in tau_k],
+           "ece_before": calibration.sequential_ece(raw[half:], cs[half:]),
+           "ece_after": calibration.sequential_ece(calibration.scale_scores(raw[half:], tau_k), cs[half:]),
+           "scores": "sigmoid(2.5 logit(c*) + N(0, 0.3^2)), c* from the acceptance pass"}
+    return {"acceptance_pass": acc, "schedulers": sched, "sequential_temperature_scaling": sts}
 
 
 def cpu_baseline(rnd, budgets, seconds):
