@@ -309,7 +309,7 @@ int dspark_acceptance(const void* target_logits, const void* base_logits, int lo
   g.rsum = at<float>(workspace, L.tmass), g.status = v.status;
   {
     ProfileScope ps(kClsAcceptance, s);
-    DSPARK_TRY(launch_gemm_stats(g, logits_dtype, factor_dtype, true, s));
+    DSPARK_TRY(launch_gemm_stats(g, logits_dtype, factor_dtype, true, s, &c.n_parts));
   }
   DSPARK_TRY(launch_acceptance_finish(c, s));
   return DSPARK_OK;

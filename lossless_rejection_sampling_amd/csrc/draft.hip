@@ -1241,7 +1241,7 @@ __global__ __launch_bounds__(512, 1) void gemm_residual_coalesced(GemmArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, l32 = lane & 31;
   const int vb = wave >> 2, sl = (wave & 3) * 32 + l32;  // column block, slot in the group
-  const int nslots = residual_slots(a);
+  const int nslots = (int)*a.slot_count;
   if (nslots <= 0) return;
   const int ngroups = (nslots + kResSlots - 1) / kResSlots;
   // walkers per slot group, a multiple of 8 so that the workgroups of one tile
@@ -1263,12 +1263,11 @@ __global__ __launch_bounds__(512, 1) void gemm_residual_coalesced(GemmArgs a) {
   double lse_q = 0.0;
   if (valid) {
     T = effective_temp(a.temperature[rq]);
-    double rmax, rlsum;
-    residual_rowstats(a, rq, pos, rmax, rlsum);
-    kp = (float)((rmax / (double)T + rlsum) * 1.4426950408889634);
+    const ReqState st = a.req[rq];
+    kp = (float)(((double)st.row_max / (double)T + st.row_logsum) * 1.4426950408889634);
     lse_q = a.draft_lse[(size_t)rq * a.gamma + pos];
   }
-  if (!(T > 0.0f)) T = 1.0f;  // greedy rows: no residual draw; the acceptance pass ignores their masses
+  if (!(T > 0.0f)) T = 1.0f;  // greedy rows never hold a residual draw
   const float c = kLog2e / T;
   bf16x8 H[R / 16];
   {
@@ -1374,7 +1373,7 @@ __global__ __launch_bounds__(512, 1) void gemm_residual_coalesced(GemmArgs a) {
     for (int e = 0; e < 16; ++e) {
       const float p = __builtin_amdgcn_exp2f(fmaf(zv[e], c, -kp));
       const float q = __builtin_amdgcn_exp2f(fmaf((xv[e] - ref) + acc[e], c, -kq));
-      rs += residual_mass(a, p, q);
+      rs += fmaxf(p - q, 0.0f);
     }
     return reduce_pair32(rs, OpSum{});
   };
@@ -1406,7 +1405,7 @@ __global__ __launch_bounds__(512, 1) void gemm_residual_coalesced(GemmArgs a) {
     }
     wait_vmcnt(0);
     __syncthreads();
-    if (vb == 0 && half == 0 && valid) a.rsum[residual_out(a, rq, pos, t)] = rs + part[c0][sl];
+    if (vb == 0 && half == 0 && valid) a.rsum[(size_t)rq * nt + t] = rs + part[c0][sl];
     t += G;
   };
   for (;;) {
@@ -1415,6 +1414,252 @@ __global__ __launch_bounds__(512, 1) void gemm_residual_coalesced(GemmArgs a) {
     step(1, acc1, acc0);
     if (t >= nt) break;
   }
+}
+
+// ---------------------------------------------------------------------------
+// Streaming residual-mode pass (bf16 logits with V a multiple of 8, bf16
+// factors, R in {128, 256}): the draft kernel's design with a third stream.
+// A workgroup of 8 wavefronts owns 256 slots and walks 64-column tiles as two
+// 32-column stages; W2 rows (shared) and each wavefront's backbone and target
+// rows (private) reach LDS by direct loads into three-stage rings, two stages
+// ahead.  Iteration u seeds and issues the MFMAs of stage u+1 (so t = (x -
+// ref) + bias comes out of the accumulator) with the masses of stage u: per
+// column p = exp(z / T - ln Z_p), q = exp((ref + t) / T - lse_q) and
+// max(0, p - q) (the residual draw) or min(p, q) (the acceptance pass).  The
+// residual draw needs each tile's mass; the acceptance pass only the total, so
+// a slot's masses are summed in fp64 across the workgroup's tiles and written
+// once per workgroup (column blockIdx.x of the slot's row of partial sums).
+// ---------------------------------------------------------------------------
+constexpr int kRStages = 3;
+
+template <int R, bool TV>
+__global__ __launch_bounds__(512, 1) void gemm_residual_stream(GemmArgs a) {
+  using WL = WLayout<R, kStageCols>;
+  constexpr int KS = R / 16;
+  constexpr int W_DMA = WL::NB / 8;
+  constexpr int X_DMA = kXStageBytes / 1024;
+  constexpr int W_RING = kRStages * WL::BYTES;
+  constexpr int SLOT_BYTES = 2 * kXStageBytes;  // backbone then target logits of one stage
+  extern __shared__ __attribute__((aligned(1024))) char lds[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int nslots = residual_slots(a);
+  const int sg0 = blockIdx.y * kSlotsPerGroup;
+  const int nt = a.n_tiles, G = gridDim.x;
+  if (sg0 >= nslots || (int)blockIdx.x >= nt) return;  // uniform across the workgroup
+  const int V = a.V;
+  char* const ring = lds + W_RING + wave * (kRStages * SLOT_BYTES);  // this wave's logit ring
+  const char* const Wb = static_cast<const char*>(a.Wt);
+  const char* const Xb = static_cast<const char*>(a.base);
+  const char* const Zb = static_cast<const char*>(a.target);
+
+  const int n_stage = 2 * ((nt - 1 - (int)blockIdx.x) / G + 1);
+  auto stage_col = [&](int u) {
+    u = min(u, n_stage - 1);
+    return ((int)blockIdx.x + (u >> 1) * G) * kTile + (u & 1) * kStageCols;
+  };
+  auto dma_w = [&](int u, int slot) {
+    const int c0 = stage_col(u);
+#pragma unroll
+    for (int k = 0; k < W_DMA; ++k) {
+      const int f = wave + 8 * k;
+      const int s = f * WL::RB + lane % WL::RB, c = lane / WL::RB;
+      const int v = min(c0 + col_of_row(s), V - 1);
+      __builtin_amdgcn_global_load_lds(Wb + ((uint32_t)v * (R * 2) + c * 16),
+                                       (lds_ptr_t)(lds + slot * WL::BYTES + WL::block(f)), 16, 0, 0);
+    }
+  };
+
+  // this wave's 32 slots (compiler-visible loads, all waited for before the
+  // first stream load is issued)
+  int rq, pos, prev;
+  bool valid;
+  slot_info<true>(a, sg0 + wave * 32 + l32, nslots, rq, pos, prev, valid);
+  float T = valid ? effective_temp(a.temperature[rq]) : 1.0f;
+  if (!(T > 0.0f)) T = 1.0f;  // greedy rows: no residual draw; the acceptance pass ignores their masses
+  double rmax = 0.0, rlsum = 0.0, lse_q = 0.0;
+  if (valid) {
+    residual_rowstats(a, rq, pos, rmax, rlsum);
+    lse_q = a.draft_lse[(size_t)rq * a.gamma + pos];
+  }
+  bf16x8 H[KS];
+  {
+    const uint16_t* h = static_cast<const uint16_t*>(a.U) + (size_t)prev * R + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) H[ks] = *reinterpret_cast<const bf16x8*>(h + ks * 16);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0070 | (0xF << 8));  // vmcnt(0)
+  const double invT = 1.0 / (double)T;
+  const float cT = kLog2e / T;
+  const float kp = (float)((rmax * invT + rlsum) * 1.4426950408889634);
+  asm volatile("" : "+v"(lse_q));  // every register load is consumed here, before the streams start
+  __builtin_amdgcn_sched_barrier(0);
+
+  const uint32_t xrow = (uint32_t)(rq * a.gamma + pos) * (uint32_t)V;
+  const uint32_t zrow = (uint32_t)(rq * (a.gamma + 1) + pos) * (uint32_t)V;
+  // lane L of direct load k fetches chunk 2k + L / 32 of slot L % 32's row
+  auto dma_xz = [&](int u, int slot) {
+    const int c0 = stage_col(u);
+#pragma unroll
+    for (int k = 0; k < X_DMA; ++k) {
+      const int col = min(c0 + (2 * k + half) * 8, V - 8);
+      __builtin_amdgcn_global_load_lds(Xb + (xrow + (uint32_t)col) * 2u,
+                                       (lds_ptr_t)(ring + slot * SLOT_BYTES + k * 1024), 16, 0, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < X_DMA; ++k) {
+      const int col = min(c0 + (2 * k + half) * 8, V - 8);
+      __builtin_amdgcn_global_load_lds(Zb + (zrow + (uint32_t)col) * 2u,
+                                       (lds_ptr_t)(ring + slot * SLOT_BYTES + kXStageBytes + k * 1024), 16, 0, 0);
+    }
+  };
+  constexpr int STAGE_LOADS = W_DMA + 2 * X_DMA;
+  dma_w(0, 0);
+  dma_xz(0, 0);
+  dma_w(1, 1);
+  dma_xz(1, 1);
+  dma_w(2, 2);
+  dma_xz(2, 2);
+
+  const int wbase = WL::at(l32, half);
+  const int xbase = half * 1024 + l32 * 16;
+  auto read16 = [&](int slot, int off, u32x4& w0, u32x4& w1) {
+    w0 = *reinterpret_cast<const u32x4*>(ring + slot * SLOT_BYTES + off + xbase);
+    w1 = *reinterpret_cast<const u32x4*>(ring + slot * SLOT_BYTES + off + xbase + 512);
+  };
+  auto unpack = [](const u32x4& w0, const u32x4& w1, int e) {
+    const uint32_t w = e < 8 ? w0[(e & 7) >> 1] : w1[(e & 7) >> 1];
+    return (e & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
+  };
+  auto seed = [&](int slot, bool first, f32x16& acc, float& ref) {
+    u32x4 w0, w1;
+    read16(slot, 0, w0, w1);
+    if (first) {
+      float even, odd;
+      row_pair<32>(__uint_as_float(w0[0] << 16), even, odd);
+      ref = even;
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = unpack(w0, w1, e) - ref;
+  };
+  auto rd = [&](int slot, int ks) {
+    return *reinterpret_cast<const bf16x8*>(lds + slot * WL::BYTES + wbase + 32 * WL::RB * ks);
+  };
+  // MFMAs of the next stage interleaved with the masses of the current one
+  auto fused = [&](int slot, const f32x16& cur, const float (&z)[16], float kq, f32x16& next) {
+    float m = 0.0f;
+    bf16x8 A[2];
+    A[0] = rd(slot, 0);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + 1 < KS) A[(ks + 1) & 1] = rd(slot, ks + 1);
+      next = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[ks & 1], H[ks], next, 0, 0, 0);
+      constexpr int n = 16 / KS > 0 ? 16 / KS : 1;  // columns of the current stage per k-step
+      if (ks * n < 16) {
+#pragma unroll
+        for (int j = ks * n; j < ks * n + n; ++j) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(z[j], cT, -kp));
+          const float q = __builtin_amdgcn_exp2f(fmaf(cur[j], cT, -kq));
+          m += TV ? fminf(p, q) : fmaxf(p - q, 0.0f);
+        }
+        asm volatile("" : "+v"(m));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return pair_sum(m);
+  };
+
+  f32x16 acc0, acc1;
+  float ref0 = 0.0f, ref1 = 0.0f, tile_mass = 0.0f;
+  double total = 0.0;  // acceptance pass: this slot's masses over the workgroup's tiles
+  int tile = blockIdx.x;
+  wait_vmcnt_c<2 * STAGE_LOADS>();  // stage 0 landed
+  barrier_only();
+  seed(0, true, acc0, ref0);
+  ref1 = ref0;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd(0, ks), H[ks], acc0, 0, 0, 0);
+  wait_vmcnt_c<STAGE_LOADS>();  // stage 1 landed
+  barrier_only();
+
+  // Iteration u (stage u in ring slot S = u % 3, its t values in `cur`):
+  //   seed `next` from stage u+1's backbone logits, take stage u's target
+  //   logits into registers, issue stage u+3 into slot S, run stage u+1's
+  //   MFMAs with stage u's masses, on a tile's second stage store the tile's
+  //   mass (residual draw), wait for stage u+2 (issued in iteration u-1, or
+  //   the prologue), barrier.
+  auto step = [&](auto S_, auto second_, f32x16& cur, f32x16& next, int u) {
+    constexpr int S = decltype(S_)::value;
+    constexpr bool second = decltype(second_)::value;
+    seed((S + 1) % kRStages, second, next, ref0);
+    u32x4 zw0, zw1;
+    read16(S, kXStageBytes, zw0, zw1);
+    float z[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) z[e] = unpack(zw0, zw1, e);  // waits for the LDS reads: slot S is free
+    dma_w(u + 3, S);
+    dma_xz(u + 3, S);
+    const int c0 = tile * kTile + (second ? kStageCols : 0);
+    if (c0 + kStageCols > V) {  // a ragged stage: columns >= V do not exist
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (c0 + half * 16 + e >= V) cur[e] = -INFINITY, z[e] = -INFINITY;
+    }
+    const float kq = (float)((lse_q - (double)ref1 * invT) * 1.4426950408889634);
+    const float m = fused((S + 1) % kRStages, cur, z, kq, next);
+    tile_mass += m;
+    if (second) {
+      if (TV) total += (double)tile_mass;
+      else if (half == 0 && valid) a.rsum[residual_out(a, rq, pos, tile)] = tile_mass;
+      tile_mass = 0.0f;
+      tile += G;
+      ref1 = ref0;
+    }
+    wait_vmcnt_c<STAGE_LOADS>();
+    barrier_only();
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using F = std::false_type;
+  using Tt = std::true_type;
+  for (int u = 0;; u += 6) {
+    step(I0{}, F{}, acc0, acc1, u + 0); if (u + 1 >= n_stage) break;
+    step(I1{}, Tt{}, acc1, acc0, u + 1); if (u + 2 >= n_stage) break;
+    step(I2{}, F{}, acc0, acc1, u + 2); if (u + 3 >= n_stage) break;
+    step(I0{}, Tt{}, acc1, acc0, u + 3); if (u + 4 >= n_stage) break;
+    step(I1{}, F{}, acc0, acc1, u + 4); if (u + 5 >= n_stage) break;
+    step(I2{}, Tt{}, acc1, acc0, u + 5); if (u + 6 >= n_stage) break;
+  }
+  if (TV && half == 0 && valid)
+    a.rsum[((size_t)rq * a.gamma + pos) * a.n_tiles + blockIdx.x] = (float)total;
+}
+
+template <int R>
+hipError_t launch_residual_stream(const GemmArgs& a, hipStream_t s, int* parts) {
+  static int max_wg[2] = {0, 0};
+  const size_t lds = (size_t)kRStages * (WLayout<R, kStageCols>::BYTES + 8 * 2 * kXStageBytes);
+  const void* fn = a.tv ? reinterpret_cast<const void*>(&gemm_residual_stream<R, true>)
+                       : reinterpret_cast<const void*>(&gemm_residual_stream<R, false>);
+  int& mw = max_wg[a.tv ? 1 : 0];
+  if (!mw) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return hipErrorUnknown;
+    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+      return hipErrorUnknown;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 512, lds) != hipSuccess || per_cu < 1)
+      per_cu = 1;
+    mw = cus * per_cu;
+  }
+  // the residual draw may need every request; the acceptance pass has B gamma slots
+  const int groups = (max_slots(a, true) + kSlotsPerGroup - 1) / kSlotsPerGroup;
+  const int wg_x = max(1, min(a.n_tiles, mw / groups));
+  if (parts) *parts = wg_x;
+  if (a.tv) gemm_residual_stream<R, true><<<dim3(wg_x, groups), 512, lds, s>>>(a);
+  else gemm_residual_stream<R, false><<<dim3(wg_x, groups), 512, lds, s>>>(a);
+  return hipGetLastError();
 }
 
 template <int R>
@@ -1465,15 +1710,19 @@ hipError_t launch_pipelined(const GemmArgs& a, hipStream_t s) {
 }
 
 template <typename TL, bool RESIDUAL>
-hipError_t gemm_dispatch(const GemmArgs& a, int factor_dtype, bool vec, hipStream_t s) {
+hipError_t gemm_dispatch(const GemmArgs& a, int factor_dtype, bool vec, hipStream_t s, int* parts) {
+  if (parts) *parts = a.n_tiles;  // one partial per tile unless the streaming pass says otherwise
   if constexpr (sizeof(TL) == 2) {
     // the coalesced kernels address their inputs with 32-bit byte offsets
     const bool fits = (size_t)a.B * (a.gamma + 1) * a.V * 2 < (1ull << 32) &&
                       (size_t)a.V * a.r * 2 < (1ull << 32) && (size_t)(a.B + 1) * a.n_tiles * 16 < (1ull << 32);
     if (factor_dtype == DSPARK_BF16 && a.V % 8 == 0 && a.V >= 64 && (a.r == 128 || a.r == 256) && fits) {
       if constexpr (RESIDUAL) {
-        if (a.r == 256) return launch_residual_coalesced<256>(a, s);
-        return launch_residual_coalesced<128>(a, s);
+        // the residual draw (at most B rows): the coalesced kernel; the acceptance
+        // pass (B gamma rows): the streaming one
+        if (!a.tv) return a.r == 256 ? launch_residual_coalesced<256>(a, s) : launch_residual_coalesced<128>(a, s);
+        if (a.r == 256) return launch_residual_stream<256>(a, s, parts);
+        return launch_residual_stream<128>(a, s, parts);
       } else {
         if (a.r == 256) return launch_draft_stream<256>(a, s);
         return launch_draft_stream<128>(a, s);
@@ -1500,13 +1749,13 @@ hipError_t gemm_dispatch(const GemmArgs& a, int factor_dtype, bool vec, hipStrea
 }  // namespace
 
 hipError_t launch_gemm_stats(const GemmArgs& a, int logits_dtype, int factor_dtype, bool residual,
-                             hipStream_t s) {
+                             hipStream_t s, int* parts) {
   const bool vec = a.V % 4 == 0;
   if (logits_dtype == DSPARK_BF16)
-    return residual ? gemm_dispatch<uint16_t, true>(a, factor_dtype, vec, s)
-                    : gemm_dispatch<uint16_t, false>(a, factor_dtype, vec, s);
-  return residual ? gemm_dispatch<float, true>(a, factor_dtype, vec, s)
-                  : gemm_dispatch<float, false>(a, factor_dtype, vec, s);
+    return residual ? gemm_dispatch<uint16_t, true>(a, factor_dtype, vec, s, parts)
+                    : gemm_dispatch<uint16_t, false>(a, factor_dtype, vec, s, parts);
+  return residual ? gemm_dispatch<float, true>(a, factor_dtype, vec, s, parts)
+                  : gemm_dispatch<float, false>(a, factor_dtype, vec, s, parts);
 }
 
 hipError_t launch_draft_select(const DraftSelectArgs& a, int logits_dtype, int factor_dtype,

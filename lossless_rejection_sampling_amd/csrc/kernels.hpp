@@ -48,8 +48,10 @@ struct GemmArgs {
   uint32_t* status;
 };
 
+// `parts` (acceptance pass, may be NULL) receives the number of partial sums
+// written per slot row of rsum: n_tiles, or one per workgroup of the streaming pass.
 hipError_t launch_gemm_stats(const GemmArgs& a, int logits_dtype, int factor_dtype, bool residual,
-                             hipStream_t s);
+                             hipStream_t s, int* parts = nullptr);
 
 struct DraftSelectArgs {
   const void* base;
@@ -116,6 +118,7 @@ struct AcceptanceArgs {
   int32_t* rowarg;           // [B, gamma] lowest index of the row maximum
   double* c_star;            // [B, gamma]
   int B, gamma, V, n_blk, n_tiles;
+  int n_parts;               // partial sums per position in tile_mass
   uint32_t* status;
 };
 hipError_t launch_row_info(const AcceptanceArgs& a, hipStream_t s);

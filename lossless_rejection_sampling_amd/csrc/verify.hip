@@ -463,9 +463,9 @@ __global__ __launch_bounds__(256) void acceptance_finish_kernel(AcceptanceArgs a
     if (lane == 0) a.c_star[s] = a.draft[s] == a.rowarg[s] ? 1.0 : 0.0;
     return;
   }
-  const float* m = a.tile_mass + (size_t)s * a.n_tiles;
+  const float* m = a.tile_mass + (size_t)s * a.n_tiles;  // rows of n_tiles, the first n_parts used
   double acc = 0.0;
-  for (int t = lane; t < a.n_tiles; t += 64) acc += (double)m[t];
+  for (int t = lane; t < a.n_parts; t += 64) acc += (double)m[t];
   acc = wave_sum(acc);
   if (lane == 0) a.c_star[s] = acc;
 }
