@@ -258,10 +258,11 @@ int dspark_acceptance(const void* target_logits, const void* base_logits, int lo
 int dspark_status(void* workspace, void* stream);
 
 /* Timing of individual kernels (measurement support).  While enabled, every
- * launch of the kernel class `kernel_class` is bracketed by HIP events on the
- * caller's stream.  dspark_profile_read() synchronises the stream and returns
- * the number of bracketed launches and their summed duration in ms, then
- * clears the record.  Classes: 0 draft GEMM + softmax statistics, 1 draft
+ * launch of the kernel class `kernel_class` carries a pair of HIP events in its
+ * dispatch (hipExtLaunchKernel), which take the kernel's own start and end
+ * times on the caller's stream.  dspark_profile_read() waits for the recorded
+ * events and returns the number of timed launches and their summed duration in
+ * ms, then clears the record.  Classes: 0 draft GEMM + softmax statistics, 1 draft
  * sample, 2 target row statistics, 3 accept / bonus, 4 residual statistics,
  * 5 residual sample, 6 scheduler, 7 acceptance-pass GEMM. */
 int dspark_profile_enable(int kernel_class, int enabled);

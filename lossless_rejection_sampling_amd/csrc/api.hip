@@ -89,20 +89,38 @@ ProfState& prof() {
 
 }  // namespace
 
-ProfileScope::ProfileScope(int c, hipStream_t s) : cls(c), stream(s), ev0(nullptr), ev1(nullptr), on(false) {
-  ProfState& p = prof();
-  std::lock_guard<std::mutex> g(p.mu);
-  if (!p.on[cls]) return;
-  if (hipEventCreate(&ev0) != hipSuccess || hipEventCreate(&ev1) != hipSuccess) return;
-  on = hipEventRecord(ev0, stream) == hipSuccess;
+namespace {
+thread_local KernelEvents* t_events = nullptr;
+}
+
+KernelEvents* kernel_events() { return t_events; }
+
+ProfileScope::ProfileScope(int c, hipStream_t) : cls(c), ev{nullptr, nullptr, 0}, outer(t_events), on(false) {
+  {
+    ProfState& p = prof();
+    std::lock_guard<std::mutex> g(p.mu);
+    if (!p.on[cls]) return;
+  }
+  if (hipEventCreate(&ev.start) != hipSuccess) return;
+  if (hipEventCreate(&ev.stop) != hipSuccess) {
+    (void)hipEventDestroy(ev.start);
+    return;
+  }
+  on = true;
+  t_events = &ev;
 }
 
 ProfileScope::~ProfileScope() {
   if (!on) return;
-  if (hipEventRecord(ev1, stream) != hipSuccess) return;
+  t_events = outer;
+  if (ev.launches == 0) {  // nothing was launched: nothing to time
+    (void)hipEventDestroy(ev.start);
+    (void)hipEventDestroy(ev.stop);
+    return;
+  }
   ProfState& p = prof();
   std::lock_guard<std::mutex> g(p.mu);
-  p.ev[cls].emplace_back(ev0, ev1);
+  p.ev[cls].emplace_back(ev.start, ev.stop);
 }
 
 }  // namespace dspark

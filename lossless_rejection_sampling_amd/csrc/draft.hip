@@ -994,13 +994,26 @@ __global__ __launch_bounds__(512, 1) void gemm_draft_stream(GemmArgs a) {
   const char* const Wb = static_cast<const char*>(a.Wt);
   const char* const Xb = static_cast<const char*>(a.base);
 
-  // Stage u of this workgroup: tile blockIdx.x + (u / 2) G, columns 32 (u % 2)
-  // onwards; stages past the last one repeat it (their loads hit L2 and their
-  // results are never used), so every iteration issues the same loads.
-  const int n_stage = 2 * ((nt - 1 - (int)blockIdx.x) / G + 1);
+  // Tiles of this workgroup.  Workgroups are dealt to the 8 XCDs round robin
+  // (blockIdx.x % 8), each XCD with its own L2.  In the nt / G full rounds the
+  // G tiles of a round are split into 8 runs of G / 8 adjacent tiles, one per
+  // XCD, so the 16-byte records of neighbouring tiles of a row meet in one L2
+  // and leave it as whole lines.  The nt % G leftover tiles go to the workgroups
+  // of even XCDs first (odd XCDs stream measurably slower in this kernel).
+  // Without a multiple of 8 workgroups the order is plain: tile bx + j G.
+  const int bx = blockIdx.x, full = nt / G, rem = nt - full * G;
+  const bool xcd_order = (G & 7) == 0;
+  const int run_pos = xcd_order ? (bx & 7) * (G >> 3) + (bx >> 3) : bx;
+  const int tail_rank = xcd_order ? (bx & 1) * (G >> 1) + (bx >> 1) : bx;
+  auto tile_of = [&](int j) { return j < full ? j * G + run_pos : full * G + tail_rank; };
+  // Stage u: tile tile_of(u / 2), columns 32 (u % 2) onwards; stages past the
+  // last one repeat it (their loads hit L2 and their results are never used), so
+  // every iteration issues the same loads.
+  const int n_stage = 2 * (full + (tail_rank < rem ? 1 : 0));
+  if (n_stage == 0) return;  // no tile (only with more workgroups than tiles)
   auto stage_col = [&](int u) {
     u = min(u, n_stage - 1);
-    return ((int)blockIdx.x + (u >> 1) * G) * kTile + (u & 1) * kStageCols;
+    return tile_of(u >> 1) * kTile + (u & 1) * kStageCols;
   };
   auto dma_w = [&](int u, int slot) {
     const int c0 = stage_col(u);
@@ -1036,7 +1049,9 @@ __global__ __launch_bounds__(512, 1) void gemm_draft_stream(GemmArgs a) {
   const uint32_t st_base = valid ? (uint32_t)rq * (uint32_t)nt : st_spare;
   auto store_rec = [&](uint32_t at, float ref, float mx, float sum) {
     const f32x4 rec = {ref, mx, sum, 0.0f};
-    __builtin_nontemporal_store(rec, reinterpret_cast<f32x4*>(reinterpret_cast<char*>(a.tstat) + at * 16u));
+    // an ordinary store: the line stays in L2 until the neighbouring records
+    // of the same XCD's run have joined it, and leaves as a whole line
+    *reinterpret_cast<f32x4*>(reinterpret_cast<char*>(a.tstat) + at * 16u) = rec;
   };
 
   // The temperature and the U rows of the previous tokens (from the table the
@@ -1137,7 +1152,7 @@ __global__ __launch_bounds__(512, 1) void gemm_draft_stream(GemmArgs a) {
   //   may stay in flight.  Record stores are not counted: a store may complete
   //   before older loads, so counting it could let the wait pass early, while
   //   leaving it out only ever waits longer.
-  int tile = blockIdx.x;
+  int jt = 0, tile = tile_of(0);
   float ref0 = 0.0f, ref1 = 0.0f, mx_first = 0.0f, sum_first = 0.0f;
   auto step = [&](auto S_, f32x16& cur, f32x16& next, int u) {
     constexpr int S = decltype(S_)::value;
@@ -1160,7 +1175,7 @@ __global__ __launch_bounds__(512, 1) void gemm_draft_stream(GemmArgs a) {
       float s = sum_first * __builtin_amdgcn_exp2f((mx_first - m) * cT);
       if (sum > 0.0f) s += sum * __builtin_amdgcn_exp2f((mx - m) * cT);
       if (half == 0) store_rec(st_base + (uint32_t)tile, ref1, m, s);  // both halves hold the same values
-      tile += G;
+      tile = tile_of(++jt);
       ref1 = ref0;
     } else {
       mx_first = mx, sum_first = sum;
@@ -1206,7 +1221,7 @@ hipError_t launch_draft_stream(const GemmArgs& a, hipStream_t s) {
   }
   const int groups = (a.B + kSlotsPerGroup - 1) / kSlotsPerGroup;
   const int wg_x = max(1, min(a.n_tiles, max_wg / groups));
-  gemm_draft_stream<R><<<dim3(wg_x, groups), 512, lds, s>>>(a);
+  launch(&gemm_draft_stream<R>, dim3(wg_x, groups), 512, lds, s, a);
   return hipGetLastError();
 }
 
@@ -1657,8 +1672,8 @@ hipError_t launch_residual_stream(const GemmArgs& a, hipStream_t s, int* parts) 
   const int groups = (max_slots(a, true) + kSlotsPerGroup - 1) / kSlotsPerGroup;
   const int wg_x = max(1, min(a.n_tiles, mw / groups));
   if (parts) *parts = wg_x;
-  if (a.tv) gemm_residual_stream<R, true><<<dim3(wg_x, groups), 512, lds, s>>>(a);
-  else gemm_residual_stream<R, false><<<dim3(wg_x, groups), 512, lds, s>>>(a);
+  if (a.tv) launch(&gemm_residual_stream<R, true>, dim3(wg_x, groups), 512, lds, s, a);
+  else launch(&gemm_residual_stream<R, false>, dim3(wg_x, groups), 512, lds, s, a);
   return hipGetLastError();
 }
 
@@ -1682,7 +1697,7 @@ hipError_t launch_residual_coalesced(const GemmArgs& a, hipStream_t s) {
   // possible slot group when the batch is small
   const int groups = (max_slots(a, true) + kResSlots - 1) / kResSlots;
   const int grid = max(8, min(max_wg, groups * a.n_tiles));
-  gemm_residual_coalesced<R><<<grid, 512, lds, s>>>(a);
+  launch(&gemm_residual_coalesced<R>, grid, 512, lds, s, a);
   return hipGetLastError();
 }
 
@@ -1705,7 +1720,7 @@ hipError_t launch_pipelined(const GemmArgs& a, hipStream_t s) {
   const int groups = (max_slots(a, RESIDUAL) + kSlotsPerGroup - 1) / kSlotsPerGroup;
   const int threads = 64 * min(kLdsWaves, (max_slots(a, RESIDUAL) + 31) / 32);
   const int wg_x = max(1, min(a.n_tiles, max_wg / groups));
-  gemm_stats_lds<TL, RESIDUAL, R><<<dim3(wg_x, groups), threads, lds, s>>>(a);
+  launch(&gemm_stats_lds<TL, RESIDUAL, R>, dim3(wg_x, groups), threads, lds, s, a);
   return hipGetLastError();
 }
 
@@ -1736,12 +1751,12 @@ hipError_t gemm_dispatch(const GemmArgs& a, int factor_dtype, bool vec, hipStrea
   }
   if (factor_dtype == DSPARK_BF16 && a.r % 16 == 0) {
     const dim3 grid(a.n_tiles, (max_slots(a, RESIDUAL) + 255) / 256);
-    if (vec) gemm_stats_mfma<TL, RESIDUAL, true><<<grid, 256, 0, s>>>(a);
-    else gemm_stats_mfma<TL, RESIDUAL, false><<<grid, 256, 0, s>>>(a);
+    if (vec) launch(&gemm_stats_mfma<TL, RESIDUAL, true>, grid, 256, 0, s, a);
+    else launch(&gemm_stats_mfma<TL, RESIDUAL, false>, grid, 256, 0, s, a);
   } else {
     const dim3 grid(a.n_tiles, max_slots(a, RESIDUAL));
-    if (factor_dtype == DSPARK_BF16) gemm_stats_valu<TL, uint16_t, RESIDUAL><<<grid, 64, 0, s>>>(a);
-    else gemm_stats_valu<TL, float, RESIDUAL><<<grid, 64, 0, s>>>(a);
+    if (factor_dtype == DSPARK_BF16) launch(&gemm_stats_valu<TL, uint16_t, RESIDUAL>, grid, 64, 0, s, a);
+    else launch(&gemm_stats_valu<TL, float, RESIDUAL>, grid, 64, 0, s, a);
   }
   return hipGetLastError();
 }
@@ -1763,20 +1778,20 @@ hipError_t launch_draft_select(const DraftSelectArgs& a, int logits_dtype, int f
   const dim3 grid(a.B);
   if (a.n_tiles <= kTilesPerBlock * 64) {
     if (logits_dtype == DSPARK_BF16) {
-      if (factor_dtype == DSPARK_BF16) draft_select_fast<uint16_t, uint16_t><<<grid, 256, 0, s>>>(a);
-      else draft_select_fast<uint16_t, float><<<grid, 256, 0, s>>>(a);
+      if (factor_dtype == DSPARK_BF16) launch(&draft_select_fast<uint16_t, uint16_t>, grid, 256, 0, s, a);
+      else launch(&draft_select_fast<uint16_t, float>, grid, 256, 0, s, a);
     } else {
-      if (factor_dtype == DSPARK_BF16) draft_select_fast<float, uint16_t><<<grid, 256, 0, s>>>(a);
-      else draft_select_fast<float, float><<<grid, 256, 0, s>>>(a);
+      if (factor_dtype == DSPARK_BF16) launch(&draft_select_fast<float, uint16_t>, grid, 256, 0, s, a);
+      else launch(&draft_select_fast<float, float>, grid, 256, 0, s, a);
     }
     return hipGetLastError();
   }
   if (logits_dtype == DSPARK_BF16) {
-    if (factor_dtype == DSPARK_BF16) draft_select_kernel<uint16_t, uint16_t><<<grid, 256, 0, s>>>(a);
-    else draft_select_kernel<uint16_t, float><<<grid, 256, 0, s>>>(a);
+    if (factor_dtype == DSPARK_BF16) launch(&draft_select_kernel<uint16_t, uint16_t>, grid, 256, 0, s, a);
+    else launch(&draft_select_kernel<uint16_t, float>, grid, 256, 0, s, a);
   } else {
-    if (factor_dtype == DSPARK_BF16) draft_select_kernel<float, uint16_t><<<grid, 256, 0, s>>>(a);
-    else draft_select_kernel<float, float><<<grid, 256, 0, s>>>(a);
+    if (factor_dtype == DSPARK_BF16) launch(&draft_select_kernel<float, uint16_t>, grid, 256, 0, s, a);
+    else launch(&draft_select_kernel<float, float>, grid, 256, 0, s, a);
   }
   return hipGetLastError();
 }

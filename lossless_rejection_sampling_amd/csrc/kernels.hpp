@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 
 #include "device.hpp"
@@ -13,15 +14,41 @@ enum KernelClass : int {
   kClsResidualGemm = 4, kClsResidualSelect = 5, kClsSchedule = 6, kClsAcceptance = 7, kNumClasses = 8,
 };
 
-// Event bracketing of kernel launches (measurement support).
+// Kernel timing (measurement support).  While a ProfileScope of an enabled
+// class is open, the launches inside it carry its two events in their dispatch:
+// `start` takes the first kernel's start time and `stop` each kernel's end time,
+// so the interval covers kernel execution and the gaps between the scope's own
+// kernels, not the dispatch of the first one.
+struct KernelEvents {
+  hipEvent_t start, stop;
+  int launches;
+};
+KernelEvents* kernel_events();  // the innermost open scope's events, or NULL
+
 struct ProfileScope {
   ProfileScope(int cls, hipStream_t s);
   ~ProfileScope();
   int cls;
-  hipStream_t stream;
-  hipEvent_t ev0, ev1;
+  KernelEvents ev;
+  KernelEvents* outer;
   bool on;
 };
+
+// Launch of a kernel taking one argument struct, timed by the open ProfileScope.
+// Errors are left for hipGetLastError(), as with the <<<>>> launch.
+template <typename Arg, typename A>
+void launch(void (*k)(Arg), dim3 grid, dim3 block, size_t lds, hipStream_t s, const A& a) {
+  KernelEvents* e = kernel_events();
+  if (!e) {
+    k<<<grid, block, lds, s>>>(a);
+    return;
+  }
+  Arg arg = a;
+  void* args[] = {&arg};
+  if (hipExtLaunchKernel(reinterpret_cast<const void*>(k), grid, block, args, lds, s,
+                         e->launches == 0 ? e->start : nullptr, e->stop, 0) == hipSuccess)
+    ++e->launches;
+}
 
 // Arguments of the fused Markov-bias GEMM with its softmax-statistics epilogue.
 // Draft mode: one slot per request, base row `pos`; writes TileStat [B][n_tiles].

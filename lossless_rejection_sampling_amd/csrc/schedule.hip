@@ -186,7 +186,7 @@ hipError_t launch_schedule(const ScheduleArgs& a, hipStream_t s) {
   const size_t lds = (size_t)((nk * 4 + 15) & ~15) + (size_t)a.n_points * 16;
   const bool ranked = a.rule == DSPARK_SCHED_EARLY_STOP || a.rule == DSPARK_SCHED_ARGMAX;
   const int groups = ranked ? (nk + kCandPerGroup - 1) / kCandPerGroup : 1;
-  schedule_kernel<<<groups, kThreads, lds, s>>>(a);
+  launch(&schedule_kernel, groups, kThreads, lds, s, a);
   return hipGetLastError();
 }
 

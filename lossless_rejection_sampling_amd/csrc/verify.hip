@@ -475,29 +475,29 @@ __global__ __launch_bounds__(256) void acceptance_finish_kernel(AcceptanceArgs a
 hipError_t launch_row_stats(const VerifyArgs& a, int logits_dtype, hipStream_t s) {
   const dim3 grid(a.n_blk, a.B * (a.gamma + 1));
   if (logits_dtype == DSPARK_BF16) {
-    if (a.V % 8 == 0) row_stats_kernel<uint16_t, true><<<grid, 64, 0, s>>>(a);
-    else row_stats_kernel<uint16_t, false><<<grid, 64, 0, s>>>(a);
+    if (a.V % 8 == 0) launch(&row_stats_kernel<uint16_t, true>, grid, 64, 0, s, a);
+    else launch(&row_stats_kernel<uint16_t, false>, grid, 64, 0, s, a);
   } else {
-    if (a.V % 4 == 0) row_stats_kernel<float, true><<<grid, 64, 0, s>>>(a);
-    else row_stats_kernel<float, false><<<grid, 64, 0, s>>>(a);
+    if (a.V % 4 == 0) launch(&row_stats_kernel<float, true>, grid, 64, 0, s, a);
+    else launch(&row_stats_kernel<float, false>, grid, 64, 0, s, a);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_accept(const VerifyArgs& a, int logits_dtype, hipStream_t s) {
-  if (logits_dtype == DSPARK_BF16) accept_kernel<uint16_t><<<a.B, 256, 0, s>>>(a);
-  else accept_kernel<float><<<a.B, 256, 0, s>>>(a);
+  if (logits_dtype == DSPARK_BF16) launch(&accept_kernel<uint16_t>, a.B, 256, 0, s, a);
+  else launch(&accept_kernel<float>, a.B, 256, 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_residual_select(const VerifyArgs& a, int logits_dtype, int factor_dtype,
                                   hipStream_t s) {
   if (logits_dtype == DSPARK_BF16) {
-    if (factor_dtype == DSPARK_BF16) residual_select_kernel<uint16_t, uint16_t><<<a.B, 256, 0, s>>>(a);
-    else residual_select_kernel<uint16_t, float><<<a.B, 256, 0, s>>>(a);
+    if (factor_dtype == DSPARK_BF16) launch(&residual_select_kernel<uint16_t, uint16_t>, a.B, 256, 0, s, a);
+    else launch(&residual_select_kernel<uint16_t, float>, a.B, 256, 0, s, a);
   } else {
-    if (factor_dtype == DSPARK_BF16) residual_select_kernel<float, uint16_t><<<a.B, 256, 0, s>>>(a);
-    else residual_select_kernel<float, float><<<a.B, 256, 0, s>>>(a);
+    if (factor_dtype == DSPARK_BF16) launch(&residual_select_kernel<float, uint16_t>, a.B, 256, 0, s, a);
+    else launch(&residual_select_kernel<float, float>, a.B, 256, 0, s, a);
   }
   return hipGetLastError();
 }
@@ -506,22 +506,22 @@ hipError_t launch_residual_debug(const VerifyArgs& a, int logits_dtype, int fact
                                  hipStream_t s) {
   const dim3 grid(a.n_tiles, a.B);
   if (logits_dtype == DSPARK_BF16) {
-    if (factor_dtype == DSPARK_BF16) residual_debug_kernel<uint16_t, uint16_t><<<grid, 64, 0, s>>>(a);
-    else residual_debug_kernel<uint16_t, float><<<grid, 64, 0, s>>>(a);
+    if (factor_dtype == DSPARK_BF16) launch(&residual_debug_kernel<uint16_t, uint16_t>, grid, 64, 0, s, a);
+    else launch(&residual_debug_kernel<uint16_t, float>, grid, 64, 0, s, a);
   } else {
-    if (factor_dtype == DSPARK_BF16) residual_debug_kernel<float, uint16_t><<<grid, 64, 0, s>>>(a);
-    else residual_debug_kernel<float, float><<<grid, 64, 0, s>>>(a);
+    if (factor_dtype == DSPARK_BF16) launch(&residual_debug_kernel<float, uint16_t>, grid, 64, 0, s, a);
+    else launch(&residual_debug_kernel<float, float>, grid, 64, 0, s, a);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_row_info(const AcceptanceArgs& a, hipStream_t s) {
-  row_info_kernel<<<(a.B * a.gamma + 3) / 4, 256, 0, s>>>(a);
+  launch(&row_info_kernel, (a.B * a.gamma + 3) / 4, 256, 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_acceptance_finish(const AcceptanceArgs& a, hipStream_t s) {
-  acceptance_finish_kernel<<<(a.B * a.gamma + 3) / 4, 256, 0, s>>>(a);
+  launch(&acceptance_finish_kernel, (a.B * a.gamma + 3) / 4, 256, 0, s, a);
   return hipGetLastError();
 }
 
