@@ -192,6 +192,11 @@ def main():
     roof["traffic"] = measured_traffic(dominant)
     roof["kernel"] = dominant
     roof["avg_us"] = dom_avg_s * 1e6
+    # the same achieved rate against what this device reaches in plain kernels
+    peaks = measure_peaks()
+    roof["measured_peak"] = peaks
+    roof["frac_of_measured"] = roof["achieved"] / (peaks["stream_read_GB_s"] if roof["unit"] == "GB/s"
+                                                   else peaks["mfma_bf16_TFLOP_s"])
 
     extras = measure_extras(rounds[0], bufs[0])
 
@@ -223,6 +228,39 @@ def main():
         "extras": extras,
     }
     print(json.dumps(line), flush=True)
+
+
+def measure_peaks(reps=3):
+    """Reference rates of this device, timed with events around one kernel each:
+    a streaming read of a 2 GiB buffer (8x the Infinity Cache) and a dense bf16
+    MFMA loop.  Median of `reps`."""
+    import torch
+    from lossless_rejection_sampling_amd import dspark as ds
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    buf = torch.ones(2 << 30, dtype=torch.uint8, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        out = []
+        for _ in range(reps):
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            out.append(e0.elapsed_time(e1) * 1e-3)
+        return sorted(out)[len(out) // 2]
+
+    t_read = timed(lambda: ds.dspark_peak_stream_read(buf, sink))
+    del buf
+    blocks, iters = 1024, 4096
+    t_mfma = timed(lambda: ds.dspark_peak_mfma_bf16(blocks, iters, sink))
+    flops = blocks * 4 * iters * 4 * 32768
+    torch.cuda.empty_cache()
+    return {"stream_read_GB_s": (2 << 30) / t_read / 1e9, "mfma_bf16_TFLOP_s": flops / t_mfma / 1e12,
+            "how": "streaming read of 2 GiB (8192 WGs x 256 lanes, 8 x 16-byte loads in flight per lane); "
+                   "1024 WGs x 4 waves x 4096 rounds of 4 independent v_mfma_f32_32x32x16_bf16 chains"}
 
 
 def measure_extras(rnd, buf, reps=5):

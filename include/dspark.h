@@ -268,6 +268,21 @@ int dspark_status(void* workspace, void* stream);
 int dspark_profile_enable(int kernel_class, int enabled);
 int dspark_profile_read(int kernel_class, int* launches, double* total_ms);
 
+/* Reference rates of the device (measurement support, not part of a round:
+ * the roofline of the kernels above is also reported against these).  Both
+ * only enqueue one kernel on `stream`; the caller times it.  `sink` is a
+ * device uint32 that is written only in a case that does not occur (it keeps
+ * the work from being optimised away).
+ *   dspark_peak_stream_read: reads the `bytes` (a positive multiple of 16)
+ *     of the device buffer `buf` once, 8192 workgroups of 256 lanes striding
+ *     over it with 8 loads of 16 bytes in flight per lane.
+ *   dspark_peak_mfma_bf16: `blocks` workgroups of 4 wavefronts, each running
+ *     `iters` rounds of 4 independent v_mfma_f32_32x32x16_bf16 chains:
+ *     blocks * 4 * iters * 4 * 32768 flops.
+ * Errors: DSPARK_EINVAL for a NULL pointer or a size out of range. */
+int dspark_peak_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+int dspark_peak_mfma_bf16(int blocks, int iters, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -51,6 +51,8 @@ _SIG = {
     "dspark_status": (_I, [_P, _P]),
     "dspark_profile_enable": (_I, [_I, _I]),
     "dspark_profile_read": (_I, [_I, ctypes.POINTER(_I), ctypes.POINTER(ctypes.c_double)]),
+    "dspark_peak_stream_read": (_I, [_P, ctypes.c_size_t, _P, _P]),
+    "dspark_peak_mfma_bf16": (_I, [_I, _I, _P, _P]),
 }
 
 
@@ -217,3 +219,15 @@ def dspark_profile_read(kernel_class: int):
     ms = ctypes.c_double(0.0)
     _check("dspark_profile_read", lib().dspark_profile_read(int(kernel_class), ctypes.byref(n), ctypes.byref(ms)))
     return n.value, ms.value
+
+
+def dspark_peak_stream_read(buf, sink, stream=None):
+    """One streaming read of the whole uint8 device tensor `buf` (size a multiple of 16)."""
+    _check("dspark_peak_stream_read", lib().dspark_peak_stream_read(
+        _dev(buf, "buf", torch.uint8), buf.numel(), _dev(sink, "sink", torch.int32), _stream(stream)))
+
+
+def dspark_peak_mfma_bf16(blocks, iters, sink, stream=None):
+    """blocks * 4 * iters * 4 * 32768 flops of dense bf16 MFMA."""
+    _check("dspark_peak_mfma_bf16", lib().dspark_peak_mfma_bf16(
+        int(blocks), int(iters), _dev(sink, "sink", torch.int32), _stream(stream)))
