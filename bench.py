@@ -75,20 +75,22 @@ def measured_traffic(kernel_name):
     return rec["bytes"]
 
 
-def algorithmic(rnd, budgets):
+def algorithmic(rnd, budgets, emitted):
     """Bytes and flops each kernel class must move / perform per launch (what
-    the method needs, not what the kernels happen to do)."""
+    the method needs, not what the kernels happen to do).  Verification needs
+    the target rows up to the first rejection only: rows 0..n_b of request b,
+    sum_b (n_b + 1) = sum of the emitted counts."""
     B, g, V, r = rnd.B, rnd.gamma, rnd.V, rnd.r
     es = rnd.base.element_size()
     fs = rnd.U.element_size()
     n_tiles = -(-V // 64)
-    rows = int(sum(int(L) + 1 for L in budgets))
+    rows = int(sum(int(e) for e in emitted))
     return {
         # one draft step: backbone row of every request, W2 once, U rows gathered,
         # tile statistics written
         "draft_gemm": dict(bytes=B * V * es + V * r * fs + B * r * fs + B * n_tiles * 16,
                            flops=2.0 * B * r * V, per="draft step"),
-        # target rows 0..L_b of every request read once
+        # target rows 0..n_b of every request read once (statistics, tests, final tokens)
         "row_stats": dict(bytes=rows * V * es, flops=0.0, per="verify"),
     }
 
@@ -163,7 +165,7 @@ def main():
     sec_per_step = (t1 - t0) / args.steps
     value = verified / sec_per_step
 
-    alg = algorithmic(base_round, budgets)
+    alg = algorithmic(base_round, budgets, bufs[0].num_emitted.cpu().numpy())
     kernels = {}
     for name, st in per_class.items():
         if st["launches"]:

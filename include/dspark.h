@@ -208,8 +208,8 @@ int dspark_schedule_ex(const float* conf, const float* tau, const double* sps_B,
  *   out_tokens   [B, gamma+1] int32: x_1..x_n, final token, then -1
  *   num_accepted [B] int32 n;  num_emitted [B] int32 n + 1
  *   debug_logp_logq [B, gamma, 2] float32 or NULL: (ln p_k(x_k), ln q_k(x_k))
- *                 at verified positions of sampled requests (untouched
- *                 elsewhere)
+ *                 at the positions k = 1..min(n + 1, L) whose test ran, for
+ *                 sampled requests (untouched elsewhere)
  *   debug_residual  [B, V] float32 or NULL: the normalised residual row of
  *                 requests that rejected (untouched elsewhere)
  */
@@ -263,8 +263,9 @@ int dspark_status(void* workspace, void* stream);
  * times on the caller's stream.  dspark_profile_read() waits for the recorded
  * events and returns the number of timed launches and their summed duration in
  * ms, then clears the record.  Classes: 0 draft GEMM + softmax statistics, 1 draft
- * sample, 2 target row statistics, 3 accept / bonus, 4 residual statistics,
- * 5 residual sample, 6 scheduler, 7 acceptance-pass GEMM. */
+ * sample, 2 verification pass (target row statistics up to the first
+ * rejection, accept tests, bonus and greedy tokens), 3 unused, 4 residual
+ * statistics, 5 residual sample, 6 scheduler, 7 acceptance-pass GEMM. */
 int dspark_profile_enable(int kernel_class, int enabled);
 int dspark_profile_read(int kernel_class, int* launches, double* total_ms);
 

@@ -17,12 +17,12 @@ inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // Workspace: [header | scheduler ranks | tile stats (B + 1 rows) | block stats | request state | slot list |
 // residual tile mass | U rows of the last drawn tokens | acceptance pass: row
-// statistics, row argmax, tile masses].  Header words: 0 status, 1 residual slot count, 2 scheduler
+// statistics, row argmax, tile masses | lazy verification: row counters, request progress].  Header words: 0 status, 1 residual slot count, 2 scheduler
 // ticket, 3 scheduler first failure.  The header and the scheduler ranks are all
 // that dspark_schedule touches, at offsets that do not depend on V and r.
 constexpr size_t kHeaderBytes = 256;
 struct Layout {
-  size_t header, sched, tstat, bstat, req, slots, rsum, hrows, rowinfo, rowarg, tmass, total;
+  size_t header, sched, tstat, bstat, req, slots, rsum, hrows, rowinfo, rowarg, tmass, vsync, total;
   int n_tiles, n_blk;
 };
 
@@ -64,6 +64,8 @@ Layout layout(int B, int gamma, int V, int r) {
   off = align_up(off + (size_t)B * gamma * sizeof(int32_t));
   L.tmass = off;
   off = align_up(off + (size_t)B * gamma * L.n_tiles * sizeof(float));
+  L.vsync = off;  // lazy verification: blocks done per target row, then the decided positions per request
+  off = align_up(off + ((size_t)B * (gamma + 1) + B) * sizeof(uint32_t));
   L.total = off;
   return L;
 }
@@ -253,6 +255,8 @@ int dspark_verify(const void* target_logits, const void* base_logits, int logits
   a.temperature = temperature, a.pos_offset = pos_offset, a.seed = seed;
   a.B = B, a.gamma = gamma, a.V = V, a.r = r, a.n_blk = L.n_blk, a.n_tiles = L.n_tiles;
   a.bstat = at<BlockStat>(workspace, L.bstat);
+  a.rowcnt = at<uint32_t>(workspace, L.vsync);
+  a.vstate = a.rowcnt + (size_t)B * (gamma + 1);
   a.req = at<ReqState>(workspace, L.req);
   a.slot_req = at<int32_t>(workspace, L.slots);
   a.slot_count = at<uint32_t>(workspace, L.header) + 1;
@@ -262,12 +266,9 @@ int dspark_verify(const void* target_logits, const void* base_logits, int logits
   a.status = at<uint32_t>(workspace, L.header);
 
   {
+    // target rows read up to the first rejection; statistics, tests and final tokens in one pass
     ProfileScope ps(kClsRowStats, s);
-    DSPARK_TRY(launch_row_stats(a, logits_dtype, s));
-  }
-  {
-    ProfileScope ps(kClsAccept, s);
-    DSPARK_TRY(launch_accept(a, logits_dtype, s));
+    DSPARK_TRY(launch_verify_lazy(a, logits_dtype, s));
   }
   {
     GemmArgs g{};

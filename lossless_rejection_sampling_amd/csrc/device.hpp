@@ -47,8 +47,9 @@ struct ReqState {
   double row_logsum; // ln sum exp((z - row_max) / T) over target row n
   double res_mass;   // total residual mass of the row (set by the residual draw)
   int n;             // accepted count
-  int pending;       // 1 while the final token still has to be drawn from the residual
+  int pending;       // the final token still to be drawn: kDrawResidual or kDrawBonus, else 0
 };
+enum : int { kDrawResidual = 1, kDrawBonus = 2 };
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 

@@ -115,6 +115,8 @@ struct VerifyArgs {
   uint64_t seed;
   int B, gamma, V, r, n_blk, n_tiles;
   BlockStat* bstat;          // [B, gamma+1, n_blk]
+  uint32_t* rowcnt;          // [B, gamma+1] blocks of each target row done (lazy pass; zeroed by verify_init)
+  uint32_t* vstate;          // [B] progress word of the lazy pass (rows complete, positions accepted, done)
   ReqState* req;             // [B]
   int32_t* slot_req;         // [B]
   uint32_t* slot_count;
@@ -128,7 +130,7 @@ struct VerifyArgs {
 };
 
 hipError_t launch_row_stats(const VerifyArgs& a, int logits_dtype, hipStream_t s);
-hipError_t launch_accept(const VerifyArgs& a, int logits_dtype, hipStream_t s);
+hipError_t launch_verify_lazy(const VerifyArgs& a, int logits_dtype, hipStream_t s);
 hipError_t launch_residual_select(const VerifyArgs& a, int logits_dtype, int factor_dtype,
                                   hipStream_t s);
 hipError_t launch_residual_debug(const VerifyArgs& a, int logits_dtype, int factor_dtype,

@@ -8,15 +8,20 @@
 // The residual is max(0, p - q) normalised.
 //
 // Kernels, in launch order:
-//   row_stats         one wavefront per (target row, 4096-column block): max,
-//                     exp-sum relative to the max, argmax      [HBM-bound pass];
-//                     its first wavefront also empties the residual work list
-//   accept            one wavefront per request: budget check, accept tests,
-//                     bonus draw or greedy argmax, queue of requests that
-//                     rejected
+//   verify_init       zeroes the row counters, request progress and the
+//                     residual work list
+//   verify_lazy       one workgroup per (target row, request, 4 consecutive
+//                     4096-column blocks), position-major: max, exp-sum relative to the
+//                     max, argmax of the rows still needed [HBM-bound pass];
+//                     the accept tests run as rows complete; the wavefront
+//                     that decides a request emits its accepted tokens and
+//                     counts, and its greedy final token
 //   (gemm_stats)      residual mass of every tile of the rejected rows
-//   residual_select   one wavefront per rejected request: draw from the residual
+//   residual_select   one workgroup per request still drawing: a draw from the
+//                     residual of a rejected row, or the bonus from target row L
 //   residual_debug    optional: the normalised residual row
+// row_stats (the same statistics for every row 0..L_b) serves the analytic
+// acceptance pass.
 #include <math.h>
 
 #include "dspark.h"
@@ -41,14 +46,8 @@ __device__ __forceinline__ int budget_of(const VerifyArgs& a, int b) {
 // scalar path: element i*64 + lane.
 // ---------------------------------------------------------------------------
 template <typename TL, bool VEC>
-__global__ __launch_bounds__(64) void row_stats_kernel(VerifyArgs a) {
-  const int blk = blockIdx.x, row = blockIdx.y, lane = threadIdx.x;
-  const int gamma = a.gamma, V = a.V;
-  // the accept pass appends to the residual work list after this kernel
-  if (blk == 0 && row == 0 && lane == 0) *a.slot_count = 0u;
-  const int b = row / (gamma + 1), j = row - b * (gamma + 1);
-  if (j > budget_of(a, b)) return;
-  const float T = effective_temp(a.temperature[b]);
+__device__ __forceinline__ BlockStat block_stats(const VerifyArgs& a, int row, int blk, float T, int lane) {
+  const int V = a.V;
   const int start = blk * kBlock;
   const int len = min(kBlock, V - start);
   const TL* p = static_cast<const TL*>(a.target) + (size_t)row * V + start;
@@ -103,11 +102,41 @@ __global__ __launch_bounds__(64) void row_stats_kernel(VerifyArgs a) {
     }
     arg = wave_min_int(arg);
   }
-  if (lane == 0) {
-    BlockStat st;
-    st.mx = m, st.sum = s, st.arg = arg == 0x7fffffff ? -1 : start + arg, st.pad = 0.0f;
-    a.bstat[(size_t)row * a.n_blk + blk] = st;
-  }
+  BlockStat st;
+  st.mx = m, st.sum = s, st.arg = arg == 0x7fffffff ? -1 : start + arg, st.pad = 0.0f;
+  return st;
+}
+
+template <typename TL, bool VEC>
+__global__ __launch_bounds__(64) void row_stats_kernel(VerifyArgs a) {
+  const int blk = blockIdx.x, row = blockIdx.y, lane = threadIdx.x;
+  const int gamma = a.gamma;
+  // the accept pass appends to the residual work list after this kernel
+  if (blk == 0 && row == 0 && lane == 0) *a.slot_count = 0u;
+  const int b = row / (gamma + 1), j = row - b * (gamma + 1);
+  if (j > budget_of(a, b)) return;
+  const BlockStat st = block_stats<TL, VEC>(a, row, blk, effective_temp(a.temperature[b]), lane);
+  if (lane == 0) a.bstat[(size_t)row * a.n_blk + blk] = st;
+}
+
+// Block statistics exchanged between the workgroups of one pass (lazy
+// verification): written and read as agent-scope atomics (coherent across the
+// XCDs' L2 caches, with no cache-wide writeback or invalidate), 8 bytes at a time.
+__device__ __forceinline__ void store_bstat_coherent(BlockStat* p, const BlockStat& st) {
+  uint64_t w[2];
+  __builtin_memcpy(w, &st, sizeof(w));
+  uint64_t* q = reinterpret_cast<uint64_t*>(p);
+  __hip_atomic_store(q, w[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(q + 1, w[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ BlockStat load_bstat_coherent(const BlockStat* p) {
+  uint64_t w[2];
+  uint64_t* q = reinterpret_cast<uint64_t*>(const_cast<BlockStat*>(p));
+  w[0] = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  w[1] = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  BlockStat st;
+  __builtin_memcpy(&st, w, sizeof(w));
+  return st;
 }
 
 // Statistics of target rows 0..nrows-1 of one request from their block
@@ -123,8 +152,9 @@ __device__ __forceinline__ RowInfo row_info(const BlockStat* bs, int nb, bool gr
   double m = -INFINITY;
   int arg = 0x7fffffff;
   for (int i = lane; i < nb; i += 64) {
-    const double mi = bs[i].mx;
-    if (mi > m || (greedy && mi == m && bs[i].arg < arg)) m = mi, arg = bs[i].arg;
+    const BlockStat st = load_bstat_coherent(bs + i);
+    const double mi = st.mx;
+    if (mi > m || (greedy && mi == m && st.arg < arg)) m = mi, arg = st.arg;
   }
   double mm = m;
   int aa = arg;
@@ -134,7 +164,10 @@ __device__ __forceinline__ RowInfo row_info(const BlockStat* bs, int nb, bool gr
   ri.logS = 0.0;
   if (!greedy) {
     double sum = 0.0;
-    for (int i = lane; i < nb; i += 64) sum += (double)bs[i].sum * exp(((double)bs[i].mx - mm) * invT);
+    for (int i = lane; i < nb; i += 64) {
+      const BlockStat st = load_bstat_coherent(bs + i);
+      sum += (double)st.sum * exp(((double)st.mx - mm) * invT);
+    }
     ri.logS = log(wave_sum(sum));
   }
   return ri;
@@ -146,12 +179,12 @@ __device__ __forceinline__ RowInfo row_info(const BlockStat* bs, int nb, bool gr
 template <typename TL>
 __device__ int sample_row(const TL* row, const BlockStat* bs, int nb, int V, double invT, uint64_t seed,
                           uint32_t req, uint32_t rpos, int lane) {
-  const double mref = bs[0].mx;
+  const double mref = load_bstat_coherent(bs).mx;
   double best = -INFINITY;
   int bi = 0x7fffffff;
   for (int i = lane; i < nb; i += 64) {
-    const double val = ((double)bs[i].mx - mref) * invT + log((double)bs[i].sum) +
-                       gumbel(seed, kFinalTop, req, rpos, i);
+    const BlockStat st = load_bstat_coherent(bs + i);
+    const double val = ((double)st.mx - mref) * invT + log((double)st.sum) + gumbel(seed, kFinalTop, req, rpos, i);
     if (val > best) best = val, bi = i;
   }
   wave_argmax(best, bi);
@@ -212,79 +245,146 @@ __device__ int sample_row(const TL* row, const BlockStat* bs, int nb, int V, dou
   return index_or(vi, min(start + len, tstart + kTile), tstart);
 }
 
-// One workgroup of 4 wavefronts per request.
-template <typename TL>
-__global__ __launch_bounds__(256) void accept_kernel(VerifyArgs a) {
-  __shared__ double s_M[17], s_logS[17];
-  __shared__ int s_arg[17], s_n;
-  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int gamma = a.gamma, V = a.V, nb = a.n_blk;
+// ---------------------------------------------------------------------------
+// Lazy verification: a target row is skipped once its request is known to be
+// decided, so the rows read are 0..n_b plus the few read before the decision
+// was known (instead of 0..L_b).  One workgroup of 4 wavefronts per work item
+// (target row j, request b, 4 consecutive 4096-column blocks, one per
+// wavefront) in position-major order,
+//   item = (j B + b) ceil(n_blk / 4) + chunk,
+// so the rows of early positions, whose tests decide which later rows are
+// needed, are read first.  No item waits for another.
+//
+// Progress of request b, one word changed only by atomic read-modify-writes:
+//   bit j (j <= 16)   target row j has all its block statistics
+//   bits 20..24       m: positions 1..m tested and accepted
+//   bit 31            the final token is decided (no further row is needed)
+// The test of position j + 1 needs row j complete and m = j.  The last block of
+// row j sets bit j and runs the test if it finds m = j; the wavefront that
+// raises m to j runs it if it finds bit j set; each read-modify-write sees the
+// other's, so exactly one of them runs it.  A tester goes on with the next
+// position while the next row is already complete.  The final token: a failed
+// test at position n + 1 (residual work item, or the greedy argmax), or n = L
+// (bonus draw, or the greedy argmax); residual and bonus draws are made by
+// residual_select.  The accept tests are those of the pages in fp64.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kProgOne = 1u << 20;
+constexpr uint32_t kVerifyDone = 0x80000000u;
+__device__ __forceinline__ int prog_of(uint32_t w) { return (int)((w >> 20) & 31u); }
+
+__global__ __launch_bounds__(256) void verify_init_kernel(VerifyArgs a) {
+  const int n = a.B * (a.gamma + 1);
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) a.rowcnt[i] = 0u;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < a.B; i += gridDim.x * blockDim.x) a.vstate[i] = 0u;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *a.slot_count = 0u;
+}
+
+// Lane 0 applies the read-modify-write; every lane gets the previous word.
+__device__ __forceinline__ uint32_t vstate_or(uint32_t* w, uint32_t bits, int lane) {
+  uint32_t old = 0u;
+  if (lane == 0) old = __hip_atomic_fetch_or(w, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __shfl(old, 0);
+}
+__device__ __forceinline__ uint32_t vstate_add(uint32_t* w, uint32_t v, int lane) {
+  uint32_t old = 0u;
+  if (lane == 0) old = __hip_atomic_fetch_add(w, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __shfl(old, 0);
+}
+
+constexpr int kLazyBlocks = 4;  // 4096-column blocks per work item, one per wavefront
+
+template <typename TL, bool VEC>
+__global__ __launch_bounds__(256) void verify_lazy_kernel(VerifyArgs a) {
+  __shared__ uint32_t s_word;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int B = a.B, gamma = a.gamma, V = a.V, nb = a.n_blk;
+  const int nch = (nb + kLazyBlocks - 1) / kLazyBlocks;
+  const int item = blockIdx.x;
+  const int j = item / (B * nch), rest = item - j * (B * nch), b = rest / nch, ch = rest - b * nch;
   const int L = budget_of(a, b);
-  if (tid == 0 && a.budget && (a.budget[b] < 0 || a.budget[b] > gamma)) flag_status(a.status, kBadBudget);
+  if (j > L) return;  // uniform across the workgroup
+  if (j == 0 && ch == 0 && tid == 0 && a.budget && (a.budget[b] < 0 || a.budget[b] > gamma))
+    flag_status(a.status, kBadBudget);
+  uint32_t* const vw = a.vstate + b;
+  if (j > 0) {
+    if (tid == 0) s_word = __hip_atomic_load(vw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (s_word & kVerifyDone) return;  // decided at an earlier position: row j is not needed
+  }
+
+  const int row0 = b * (gamma + 1);
+  const int blk = ch * kLazyBlocks + wave;
+  if (blk < nb) {
+    const BlockStat st = block_stats<TL, VEC>(a, row0 + j, blk, effective_temp(a.temperature[b]), lane);
+    if (lane == 0) {
+      store_bstat_coherent(a.bstat + (size_t)(row0 + j) * nb + blk, st);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // complete at the agent's coherence point
+    }
+  }
+  // count the item once every statistic of it is stored, so the item that finds
+  // the row's count full reads them all with its coherent loads
+  __syncthreads();
+  if (wave != 0) return;
+  uint32_t before = 0u;
+  if (lane == 0) before = __hip_atomic_fetch_add(a.rowcnt + row0 + j, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (__shfl(before, 0) != (uint32_t)(nch - 1)) return;
+  // row j is complete: announce it, and test position j + 1 if its turn has come
+  {
+    const uint32_t old = vstate_or(vw, 1u << j, lane);
+    if ((old & kVerifyDone) || prog_of(old) != j) return;
+  }
+
   const float Tf = checked_temp(a.temperature[b], a.status);
   const bool greedy = !(Tf > 0.0f);
   const double invT = greedy ? 0.0 : 1.0 / (double)Tf;
   const uint32_t off = a.pos_offset ? (uint32_t)a.pos_offset[b] : 0u;
-  const BlockStat* bs = a.bstat + (size_t)b * (gamma + 1) * nb;
-  const TL* trow0 = static_cast<const TL*>(a.target) + (size_t)b * (gamma + 1) * V;
+  const TL* trow0 = static_cast<const TL*>(a.target) + (size_t)row0 * V;
   const int32_t* xs = a.draft + (size_t)b * gamma;
-
-  // statistics of rows 0..L, one wavefront per row
-  for (int j = wave; j <= L; j += 4) {
-    const RowInfo ri = row_info(bs + (size_t)j * nb, nb, greedy, invT, lane);
-    if (lane == 0) s_M[j] = ri.M, s_logS[j] = ri.logS, s_arg[j] = ri.arg;
-  }
-  __syncthreads();
-
-  // every accept test at once (lane k-1 tests position k); n = first failure
-  if (wave == 0) {
-    bool fail = false;
-    if (lane < L) {
-      const int k = lane + 1;
-      const int x = checked_token(xs[lane], V, a.status, kBadDraft);
-      if (greedy) {
-        fail = x != s_arg[lane];
-      } else {
-        const double lp = ((double)load_logit(trow0 + (size_t)lane * V + x) - s_M[lane]) * invT - s_logS[lane];
-        const double lq = (double)a.draft_logq[(size_t)b * gamma + lane];
-        const double lnu = log(uniform_from_word(rng_word(a.seed, kAccept, b, k + off, 0)));
-        fail = !(lnu < lp - lq);  // accept iff u < min(1, p/q), since ln u < 0
-        if (a.debug_logp_logq) {
-          a.debug_logp_logq[((size_t)b * gamma + lane) * 2] = (float)lp;
-          a.debug_logp_logq[((size_t)b * gamma + lane) * 2 + 1] = (float)lq;
-        }
+  int n = j;  // rows 0..n complete, positions 1..n accepted
+  RowInfo ri;
+  for (;;) {
+    ri = row_info(a.bstat + (size_t)(row0 + n) * nb, nb, greedy, invT, lane);
+    if (n == L) break;  // every drafted position accepted
+    const int k = n + 1;
+    const int x = checked_token(xs[n], V, a.status, kBadDraft);
+    bool fail;
+    if (greedy) {
+      fail = x != ri.arg;
+    } else {
+      const double lp = ((double)load_logit(trow0 + (size_t)n * V + x) - ri.M) * invT - ri.logS;
+      const double lq = (double)a.draft_logq[(size_t)b * gamma + n];
+      const double lnu = log(uniform_from_word(rng_word(a.seed, kAccept, b, k + off, 0)));
+      fail = !(lnu < lp - lq);  // accept iff u < min(1, p/q), since ln u < 0
+      if (a.debug_logp_logq && lane == 0) {
+        a.debug_logp_logq[((size_t)b * gamma + n) * 2] = (float)lp;
+        a.debug_logp_logq[((size_t)b * gamma + n) * 2 + 1] = (float)lq;
       }
     }
-    const unsigned long long m = __ballot(fail);
-    if (lane == 0) s_n = m ? __ffsll((long long)m) - 1 : L;
+    if (fail) break;
+    const uint32_t old = vstate_add(vw, kProgOne, lane);  // m: n -> k
+    if (!(old & (1u << k))) return;  // row k not complete yet: its last item tests position k + 1
+    n = k;
   }
-  __syncthreads();
-  const int n = s_n;
-
-  int y = -1;
-  if (greedy) {
-    y = s_arg[n];
-  } else if (n == L) {
-    if (wave == 0) y = sample_row(trow0 + (size_t)n * V, bs + (size_t)n * nb, nb, V, invT, a.seed, b, n + 1 + off, lane);
-  } else if (tid == 0) {
-    ReqState st;
-    st.row_max = s_M[n], st.row_logsum = s_logS[n], st.res_mass = 0.0, st.n = n, st.pending = 1;
-    a.req[b] = st;
-    a.slot_req[atomicAdd(a.slot_count, 1u)] = b;
+  // the final token, n accepted: the greedy argmax here; a bonus or residual
+  // draw in residual_select (after the residual pass)
+  if (lane == 0) {
+    ReqState rs;
+    rs.row_max = ri.M, rs.row_logsum = ri.logS, rs.res_mass = 0.0, rs.n = n;
+    rs.pending = greedy ? 0 : (n < L ? kDrawResidual : kDrawBonus);
+    a.req[b] = rs;
+    if (rs.pending == kDrawResidual) a.slot_req[atomicAdd(a.slot_count, 1u)] = b;
   }
-  if (tid == 0 && (greedy || n == L)) a.req[b].pending = 0;  // no residual draw for this request
-  if (wave == 0) {
-    for (int i = lane; i <= gamma; i += 64) {
-      int t = -1;
-      if (i < n) t = xs[i];
-      else if (i == n) t = y;
-      a.out_tokens[(size_t)b * (gamma + 1) + i] = t;
-    }
-    if (lane == 0) {
-      a.num_accepted[b] = n;
-      a.num_emitted[b] = n + 1;
-    }
+  for (int i = lane; i <= gamma; i += 64) {
+    int t = -1;
+    if (i < n) t = xs[i];
+    else if (i == n && greedy) t = ri.arg;
+    a.out_tokens[(size_t)b * (gamma + 1) + i] = t;
   }
+  if (lane == 0) {
+    a.num_accepted[b] = n;
+    a.num_emitted[b] = n + 1;
+  }
+  vstate_or(vw, kVerifyDone, lane);
 }
 
 template <typename TF>
@@ -338,6 +438,15 @@ __global__ __launch_bounds__(256) void residual_select_kernel(VerifyArgs a) {
   const double invT = 1.0 / (double)a.temperature[b];
   const uint32_t off = a.pos_offset ? (uint32_t)a.pos_offset[b] : 0u;
   const uint32_t rpos = n + 1 + off;
+  if (st.pending == kDrawBonus) {  // every drafted position accepted: the bonus from target row n = L
+    if (wave == 0) {
+      const TL* trow = static_cast<const TL*>(a.target) + ((size_t)b * (gamma + 1) + n) * V;
+      const int y = sample_row(trow, a.bstat + ((size_t)b * (gamma + 1) + n) * a.n_blk, a.n_blk, V, invT, a.seed,
+                               b, rpos, lane);
+      if (lane == 0) a.out_tokens[(size_t)b * (gamma + 1) + n] = y;
+    }
+    return;
+  }
   int prev = n == 0 ? a.prev0[b] : a.draft[(size_t)b * gamma + n - 1];
   prev = checked_token(prev, V, a.status, n == 0 ? kBadPrev : kBadDraft);
   const double lse_q = a.draft_lse[(size_t)b * gamma + n];
@@ -419,7 +528,7 @@ template <typename TL, typename TF>
 __global__ __launch_bounds__(64) void residual_debug_kernel(VerifyArgs a) {
   const int tile = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
   const ReqState st = a.req[b];
-  if (!st.pending) return;
+  if (st.pending != kDrawResidual) return;
   const int v = tile * kTile + lane;
   if (v >= a.V) return;
   const int gamma = a.gamma, n = st.n, r = a.r;
@@ -484,9 +593,19 @@ hipError_t launch_row_stats(const VerifyArgs& a, int logits_dtype, hipStream_t s
   return hipGetLastError();
 }
 
-hipError_t launch_accept(const VerifyArgs& a, int logits_dtype, hipStream_t s) {
-  if (logits_dtype == DSPARK_BF16) launch(&accept_kernel<uint16_t>, a.B, 256, 0, s, a);
-  else launch(&accept_kernel<float>, a.B, 256, 0, s, a);
+hipError_t launch_verify_lazy(const VerifyArgs& a, int logits_dtype, hipStream_t s) {
+  const int n_state = a.B * (a.gamma + 1);
+  launch(&verify_init_kernel, min(64, (n_state + 255) / 256), 256, 0, s, a);
+  const long long items = (long long)(a.gamma + 1) * a.B * ((a.n_blk + kLazyBlocks - 1) / kLazyBlocks);
+  if (items > 0x7fffffffLL) return hipErrorInvalidValue;
+  const unsigned grid = (unsigned)items;
+  if (logits_dtype == DSPARK_BF16) {
+    if (a.V % 8 == 0) launch(&verify_lazy_kernel<uint16_t, true>, grid, 256, 0, s, a);
+    else launch(&verify_lazy_kernel<uint16_t, false>, grid, 256, 0, s, a);
+  } else {
+    if (a.V % 4 == 0) launch(&verify_lazy_kernel<float, true>, grid, 256, 0, s, a);
+    else launch(&verify_lazy_kernel<float, false>, grid, 256, 0, s, a);
+  }
   return hipGetLastError();
 }
 
