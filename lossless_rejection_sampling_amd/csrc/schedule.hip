@@ -65,6 +65,15 @@ __device__ float scaled_score(float c, float tau) {
   return (float)y;
 }
 
+__device__ __forceinline__ void store_coherent(double* p, double v) {
+  __hip_atomic_store(reinterpret_cast<unsigned long long*>(p), (unsigned long long)__double_as_longlong(v),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ double load_coherent(const double* p) {
+  return __longlong_as_double((long long)__hip_atomic_load(
+      reinterpret_cast<unsigned long long*>(const_cast<double*>(p)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
 __global__ __launch_bounds__(kThreads) void schedule_kernel(ScheduleArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   __shared__ int s_last;
@@ -109,17 +118,26 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(ScheduleArgs a) {
   if (!ranked) return;  // uniform: the fixed and threshold rules are done
   __syncthreads();
 
-  // candidate i: keys before it and the sum of their Q
+  // candidate i: keys before it and the sum of their Q; lane `sub` reads keys
+  // 4 (sub + 16 t) .. + 3 as one 16-byte word (keys past nk are padding that
+  // never counts: 0xFFFFFFFF with an index after every candidate)
   const int i = blockIdx.x * kCandPerGroup + (tid / kLanesPerCand), sub = tid % kLanesPerCand;
   uint32_t cnt = 0;
   unsigned long long tau = 0;
   const uint32_t qi = i < nk ? qinv[i] : 0u;
   if (i < nk) {
-    for (int k = sub; k < nk; k += kLanesPerCand) {
-      const uint32_t qk = qinv[k];
-      const bool before = qk < qi || (qk == qi && k < i);
-      cnt += before ? 1u : 0u;
-      tau += before ? (unsigned long long)(0xFFFFFFFFu - qk) : 0ull;
+    const uint4* q4 = reinterpret_cast<const uint4*>(qinv);
+    const int n4 = (nk + 3) / 4;
+    for (int k4 = sub; k4 < n4; k4 += kLanesPerCand) {
+      const uint4 w = q4[k4];
+      const uint32_t qs[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int k = 4 * k4 + e;
+        const bool before = k < nk && (qs[e] < qi || (qs[e] == qi && k < i));
+        cnt += before ? 1u : 0u;
+        tau += before ? (unsigned long long)(0xFFFFFFFFu - qs[e]) : 0ull;
+      }
     }
   }
   static_assert(kLanesPerCand == 16, "one DPP row per candidate");
@@ -134,20 +152,22 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(ScheduleArgs a) {
       const double rhs = (double)T * step_time(N + 1.0, tB, tT, np);
       if (!(lhs > rhs)) atomicMax(a.stop_enc, kNoFail - cnt);
     } else {
-      a.theta[cnt + 1] = (double)(T + q) / step_time(N + 1.0, tB, tT, np);
+      store_coherent(a.theta + cnt + 1, (double)(T + q) / step_time(N + 1.0, tB, tT, np));
     }
-    a.rank[i] = (int)cnt;
+    __hip_atomic_store(a.rank + i, (int)cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   if (a.rule == DSPARK_SCHED_ARGMAX && blockIdx.x == 0 && tid == 0)
-    a.theta[0] = (double)((unsigned long long)B << 32) / step_time((double)B, tB, tT, np);
+    store_coherent(a.theta, (double)((unsigned long long)B << 32) / step_time((double)B, tB, tT, np));
 
-  // the last workgroup to finish turns ranks into budgets
-  __threadfence();
+  // The last workgroup to finish turns ranks into budgets.  Ranks and Theta
+  // travel as agent-scope atomics (coherent across the XCDs' L2 caches without
+  // a cache-wide writeback or invalidate): every wavefront waits for its own
+  // stores to complete before the barrier, and the ticket is taken after it.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  if (tid == 0) s_last = atomicAdd(a.ticket, 1u) == gridDim.x - 1;
+  if (tid == 0) s_last = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1;
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
   int stop;
   if (a.rule == DSPARK_SCHED_EARLY_STOP) {
     const uint32_t enc = __hip_atomic_load(a.stop_enc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -157,7 +177,7 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(ScheduleArgs a) {
     double best = -1.0;
     int bm = 0x7fffffff;
     for (int m = tid; m <= nk; m += kThreads) {
-      const double th = __builtin_nontemporal_load(a.theta + m);
+      const double th = load_coherent(a.theta + m);
       if (th > best) best = th, bm = m;  // m increases: ties keep the first
     }
     wave_argmax(best, bm);
@@ -170,7 +190,8 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(ScheduleArgs a) {
   }
   for (int b = tid; b < B; b += kThreads) {
     int n = 0;
-    for (int j = 0; j < gamma; ++j) n += __builtin_nontemporal_load(a.rank + b * gamma + j) < stop ? 1 : 0;
+    for (int j = 0; j < gamma; ++j)
+      n += __hip_atomic_load(a.rank + b * gamma + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < stop ? 1 : 0;
     a.budget[b] = n;
   }
   if (tid == 0) {

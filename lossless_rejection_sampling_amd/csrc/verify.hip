@@ -31,6 +31,7 @@ namespace dspark {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+typedef uint32_t u32x4n __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int budget_of(const VerifyArgs& a, int b) {
   if (!a.budget) return a.gamma;
@@ -59,7 +60,9 @@ __device__ __forceinline__ BlockStat block_stats(const VerifyArgs& a, int row, i
       idx0 = lane * 8, stride_i = 512, per = 8;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const uint4 w = *reinterpret_cast<const uint4*>(p + idx0 + i * 512);
+        // streaming loads: every target row is read once, and W2 (read again by the
+        // residual pass) stays in the Infinity Cache
+        const u32x4n w = __builtin_nontemporal_load(reinterpret_cast<const u32x4n*>(p + idx0 + i * 512));
         const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
