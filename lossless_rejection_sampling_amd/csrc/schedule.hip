@@ -81,8 +81,9 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(ScheduleArgs a) {
   __shared__ int s_bestm[kThreads / 64];
   const int tid = threadIdx.x, B = a.B, gamma = a.gamma, np = a.n_points;
   const int nk = B * gamma;
-  uint32_t* const qinv = reinterpret_cast<uint32_t*>(smem);  // 0xFFFFFFFF - Q, candidate b * gamma + j
-  double* const tB = reinterpret_cast<double*>(smem + ((nk * 4 + 15) & ~15));
+  // key of candidate m = b * gamma + j: (0xFFFFFFFF - Q) 2^32 + m, ascending in the admission order
+  unsigned long long* const key = reinterpret_cast<unsigned long long*>(smem);
+  double* const tB = reinterpret_cast<double*>(smem + (size_t)((nk + 1) & ~1) * 8);
   double* const tT = tB + np;
   const bool ranked = a.rule == DSPARK_SCHED_EARLY_STOP || a.rule == DSPARK_SCHED_ARGMAX;
 
@@ -107,37 +108,34 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(ScheduleArgs a) {
       lead += run ? 1 : 0;
       acc = acc * cj;
       const uint32_t q = (uint32_t)floor((double)acc * 4294967296.0);
-      qinv[b * gamma + j] = 0xFFFFFFFFu - q;
+      key[b * gamma + j] = ((unsigned long long)(0xFFFFFFFFu - q) << 32) | (uint32_t)(b * gamma + j);
     }
     if (blockIdx.x == 0 && !ranked) {
       const int fixed = (int)fmin(fmax(a.param, 0.0), (double)gamma);
       a.budget[b] = a.rule == DSPARK_SCHED_FIXED ? fixed : lead;
     }
   }
+  // padding to a whole 16-byte word: a key after every candidate's, which no candidate counts
+  if (tid == 0 && (nk & 1)) key[nk] = ~0ull;
   if (bad && blockIdx.x == 0) flag_status(a.status, kBadConf);
   if (!ranked) return;  // uniform: the fixed and threshold rules are done
   __syncthreads();
 
   // candidate i: keys before it and the sum of their Q; lane `sub` reads keys
-  // 4 (sub + 16 t) .. + 3 as one 16-byte word (keys past nk are padding that
-  // never counts: 0xFFFFFFFF with an index after every candidate)
+  // 2 (sub + 16 t) and the next as one 16-byte word (the padding key never counts)
   const int i = blockIdx.x * kCandPerGroup + (tid / kLanesPerCand), sub = tid % kLanesPerCand;
   uint32_t cnt = 0;
   unsigned long long tau = 0;
-  const uint32_t qi = i < nk ? qinv[i] : 0u;
+  const unsigned long long ki = i < nk ? key[i] : 0ull;
+  const uint32_t qi = (uint32_t)(ki >> 32);
   if (i < nk) {
-    const uint4* q4 = reinterpret_cast<const uint4*>(qinv);
-    const int n4 = (nk + 3) / 4;
-    for (int k4 = sub; k4 < n4; k4 += kLanesPerCand) {
-      const uint4 w = q4[k4];
-      const uint32_t qs[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int k = 4 * k4 + e;
-        const bool before = k < nk && (qs[e] < qi || (qs[e] == qi && k < i));
-        cnt += before ? 1u : 0u;
-        tau += before ? (unsigned long long)(0xFFFFFFFFu - qs[e]) : 0ull;
-      }
+    const ulonglong2* k2 = reinterpret_cast<const ulonglong2*>(key);
+    const int n2 = (nk + 1) / 2;
+    for (int t = sub; t < n2; t += kLanesPerCand) {
+      const ulonglong2 w = k2[t];
+      const bool b0 = w.x < ki, b1 = w.y < ki;
+      cnt += (b0 ? 1u : 0u) + (b1 ? 1u : 0u);
+      tau += (b0 ? 0xFFFFFFFFull - (w.x >> 32) : 0ull) + (b1 ? 0xFFFFFFFFull - (w.y >> 32) : 0ull);
     }
   }
   static_assert(kLanesPerCand == 16, "one DPP row per candidate");
@@ -204,7 +202,14 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(ScheduleArgs a) {
 
 hipError_t launch_schedule(const ScheduleArgs& a, hipStream_t s) {
   const int nk = a.B * a.gamma;
-  const size_t lds = (size_t)((nk * 4 + 15) & ~15) + (size_t)a.n_points * 16;
+  const size_t lds = (size_t)((nk + 1) & ~1) * 8 + (size_t)a.n_points * 16;
+  static bool attr = false;
+  if (!attr) {  // dynamic LDS above 64 KB: 80 KB at B gamma = 8192 with a 1024-point table
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&schedule_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            8192 * 8 + 1024 * 16) != hipSuccess)
+      return hipErrorUnknown;
+    attr = true;
+  }
   const bool ranked = a.rule == DSPARK_SCHED_EARLY_STOP || a.rule == DSPARK_SCHED_ARGMAX;
   const int groups = ranked ? (nk + kCandPerGroup - 1) / kCandPerGroup : 1;
   launch(&schedule_kernel, groups, kThreads, lds, s, a);
