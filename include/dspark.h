@@ -31,7 +31,9 @@
  *   - `workspace` is a device buffer of at least dspark_workspace_bytes(B,
  *     gamma, V, r) bytes (dspark_schedule alone: dspark_schedule_workspace_bytes
  *     (B, gamma)), 256-byte aligned, zero-filled before its first use, owned by
- *     the caller.  Calls that share a workspace must be ordered on one stream,
+ *     the caller.  Every call that completes leaves the counters it uses at
+ *     zero again; after a call that returned DSPARK_EHIP, zero the workspace
+ *     before reusing it.  Calls that share a workspace must be ordered on one stream,
  *     with one exception: dspark_schedule touches only its own part of the
  *     workspace and the status word (atomically), so it may run on another
  *     stream concurrently with dspark_draft_round of the same round.

@@ -115,7 +115,7 @@ struct VerifyArgs {
   uint64_t seed;
   int B, gamma, V, r, n_blk, n_tiles;
   BlockStat* bstat;          // [B, gamma+1, n_blk]
-  uint32_t* rowcnt;          // [B, gamma+1] blocks of each target row done (lazy pass; zeroed by verify_init)
+  uint32_t* rowcnt;          // [B, gamma+1] work items of each target row done (lazy pass; zero between calls)
   uint32_t* vstate;          // [B] progress word of the lazy pass (rows complete, positions accepted, done)
   ReqState* req;             // [B]
   int32_t* slot_req;         // [B]

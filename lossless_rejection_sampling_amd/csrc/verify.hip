@@ -8,8 +8,6 @@
 // The residual is max(0, p - q) normalised.
 //
 // Kernels, in launch order:
-//   verify_init       zeroes the row counters, request progress and the
-//                     residual work list
 //   verify_lazy       one workgroup per (target row, request, 4 consecutive
 //                     4096-column blocks), position-major: max, exp-sum relative to the
 //                     max, argmax of the rows still needed [HBM-bound pass];
@@ -18,7 +16,10 @@
 //                     counts, and its greedy final token
 //   (gemm_stats)      residual mass of every tile of the rejected rows
 //   residual_select   one workgroup per request still drawing: a draw from the
-//                     residual of a rejected row, or the bonus from target row L
+//                     residual of a rejected row, or the bonus from target row L;
+//                     every workgroup first zeroes its request's counters of the
+//                     lazy pass (and workgroup 0 the residual work list), so a
+//                     call leaves them as the next one needs them
 //   residual_debug    optional: the normalised residual row
 // row_stats (the same statistics for every row 0..L_b) serves the analytic
 // acceptance pass.
@@ -275,13 +276,6 @@ constexpr uint32_t kProgOne = 1u << 20;
 constexpr uint32_t kVerifyDone = 0x80000000u;
 __device__ __forceinline__ int prog_of(uint32_t w) { return (int)((w >> 20) & 31u); }
 
-__global__ __launch_bounds__(256) void verify_init_kernel(VerifyArgs a) {
-  const int n = a.B * (a.gamma + 1);
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) a.rowcnt[i] = 0u;
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < a.B; i += gridDim.x * blockDim.x) a.vstate[i] = 0u;
-  if (blockIdx.x == 0 && threadIdx.x == 0) *a.slot_count = 0u;
-}
-
 // Lane 0 applies the read-modify-write; every lane gets the previous word.
 __device__ __forceinline__ uint32_t vstate_or(uint32_t* w, uint32_t bits, int lane) {
   uint32_t old = 0u;
@@ -436,6 +430,11 @@ __global__ __launch_bounds__(256) void residual_select_kernel(VerifyArgs a) {
   __shared__ int s_idx[4];
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const ReqState st = a.req[b];
+  // the lazy pass's counters of this request (and the residual work list) go
+  // back to zero for the next call: every kernel that used them has finished
+  if (tid <= a.gamma) a.rowcnt[(size_t)b * (a.gamma + 1) + tid] = 0u;
+  if (tid == 0) a.vstate[b] = 0u;
+  if (b == 0 && tid == 0) *a.slot_count = 0u;
   if (!st.pending) return;  // uniform across the workgroup
   const int gamma = a.gamma, V = a.V, nt = a.n_tiles, n = st.n, r = a.r;
   const double invT = 1.0 / (double)a.temperature[b];
@@ -597,8 +596,6 @@ hipError_t launch_row_stats(const VerifyArgs& a, int logits_dtype, hipStream_t s
 }
 
 hipError_t launch_verify_lazy(const VerifyArgs& a, int logits_dtype, hipStream_t s) {
-  const int n_state = a.B * (a.gamma + 1);
-  launch(&verify_init_kernel, min(64, (n_state + 255) / 256), 256, 0, s, a);
   const long long items = (long long)(a.gamma + 1) * a.B * ((a.n_blk + kLazyBlocks - 1) / kLazyBlocks);
   if (items > 0x7fffffffLL) return hipErrorInvalidValue;
   const unsigned grid = (unsigned)items;

@@ -89,6 +89,24 @@ def test_deterministic_and_position_offsets():
     assert not torch.equal(a.draft_tokens, c.draft_tokens)
 
 
+def test_rounds_reuse_one_workspace():
+    # every call leaves the verification counters at zero for the next one
+    rnd = wl.small_random(40, 5, 9000, 32, device=DEV, seed=11, factor_dtype=torch.bfloat16, temps=(1.0, 0.0, 0.8))
+    g = torch.Generator(device="cpu").manual_seed(2)
+    rnd.budget = torch.randint(0, rnd.gamma + 1, (rnd.B,), generator=g, dtype=torch.int32).to(DEV)
+    buf = rd.allocate(rnd, debug=True)
+    outs = []
+    for _ in range(3):
+        rd.run_round(rnd, buf)
+        torch.cuda.synchronize()
+        assert ds.dspark_status(buf.workspace) == ds.DSPARK_OK
+        outs.append((buf.out_tokens.clone(), buf.num_accepted.clone(), buf.draft_tokens.clone()))
+    for o in outs[1:]:
+        assert all(torch.equal(x, y) for x, y in zip(o, outs[0]))
+    idx = np.arange(rnd.B)
+    check(compare(rnd, buf, run_oracle(rnd, idx), idx), "reused_workspace")
+
+
 def test_bad_data_is_reported_not_faulted():
     rnd = wl.small_random(8, 3, 500, 16, device=DEV, seed=1)
     rnd.prev0 = rnd.prev0.clone()
