@@ -260,9 +260,11 @@ int dspark_acceptance(const void* target_logits, const void* base_logits, int lo
 int dspark_status(void* workspace, void* stream);
 
 /* Timing of individual kernels (measurement support).  While enabled, every
- * launch of the kernel class `kernel_class` carries a pair of HIP events in its
+ * `enabled`-th launch of the kernel class `kernel_class` (the first, then every
+ * enabled-th after it; 0 turns timing off) carries a pair of HIP events in its
  * dispatch (hipExtLaunchKernel), which take the kernel's own start and end
- * times on the caller's stream.  dspark_profile_read() waits for the recorded
+ * times on the caller's stream.  A timed launch costs a few microseconds of
+ * extra dispatch time, so a sample keeps that out of a timed region.  dspark_profile_read() waits for the recorded
  * events and returns the number of timed launches and their summed duration in
  * ms, then clears the record.  Classes: 0 draft GEMM + softmax statistics, 1 draft
  * sample, 2 verification pass (target row statistics up to the first

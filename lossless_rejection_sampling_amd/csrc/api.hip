@@ -81,8 +81,12 @@ bool dtype_ok(int d) { return d == DSPARK_BF16 || d == DSPARK_F32; }
 // ---------------------------------------------------------------------------
 struct ProfState {
   std::mutex mu;
-  bool on[kNumClasses] = {};
+  int period[kNumClasses] = {};    // 0: off; k: every k-th launch of the class is timed
+  unsigned seen[kNumClasses] = {}; // launches of the class since it was enabled
   std::vector<std::pair<hipEvent_t, hipEvent_t>> ev[kNumClasses];
+  // event pairs that were read back, reused by later scopes (creating events on
+  // every launch costs host time that shows up in the timed region)
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> pool;
 };
 ProfState& prof() {
   static ProfState p;
@@ -101,12 +105,18 @@ ProfileScope::ProfileScope(int c, hipStream_t) : cls(c), ev{nullptr, nullptr, 0}
   {
     ProfState& p = prof();
     std::lock_guard<std::mutex> g(p.mu);
-    if (!p.on[cls]) return;
+    if (p.period[cls] <= 0 || p.seen[cls]++ % (unsigned)p.period[cls] != 0) return;
+    if (!p.pool.empty()) {
+      ev.start = p.pool.back().first, ev.stop = p.pool.back().second;
+      p.pool.pop_back();
+    }
   }
-  if (hipEventCreate(&ev.start) != hipSuccess) return;
-  if (hipEventCreate(&ev.stop) != hipSuccess) {
-    (void)hipEventDestroy(ev.start);
-    return;
+  if (!ev.start) {
+    if (hipEventCreate(&ev.start) != hipSuccess) return;
+    if (hipEventCreate(&ev.stop) != hipSuccess) {
+      (void)hipEventDestroy(ev.start);
+      return;
+    }
   }
   on = true;
   t_events = &ev;
@@ -115,13 +125,12 @@ ProfileScope::ProfileScope(int c, hipStream_t) : cls(c), ev{nullptr, nullptr, 0}
 ProfileScope::~ProfileScope() {
   if (!on) return;
   t_events = outer;
-  if (ev.launches == 0) {  // nothing was launched: nothing to time
-    (void)hipEventDestroy(ev.start);
-    (void)hipEventDestroy(ev.stop);
-    return;
-  }
   ProfState& p = prof();
   std::lock_guard<std::mutex> g(p.mu);
+  if (ev.launches == 0) {  // nothing was launched: nothing to time
+    p.pool.emplace_back(ev.start, ev.stop);
+    return;
+  }
   p.ev[cls].emplace_back(ev.start, ev.stop);
 }
 
@@ -350,9 +359,11 @@ int dspark_status(void* workspace, void* stream) {
 
 int dspark_profile_enable(int kernel_class, int enabled) {
   if (kernel_class < 0 || kernel_class >= kNumClasses) return DSPARK_EINVAL;
+  if (enabled < 0) return DSPARK_EINVAL;
   ProfState& p = prof();
   std::lock_guard<std::mutex> g(p.mu);
-  p.on[kernel_class] = enabled != 0;
+  p.period[kernel_class] = enabled;
+  p.seen[kernel_class] = 0;
   return DSPARK_OK;
 }
 
@@ -371,8 +382,10 @@ int dspark_profile_read(int kernel_class, int* launches, double* total_ms) {
     if (hipEventSynchronize(e.second) != hipSuccess || hipEventElapsedTime(&ms, e.first, e.second) != hipSuccess)
       rc = DSPARK_EHIP;
     tot += ms;
-    (void)hipEventDestroy(e.first);
-    (void)hipEventDestroy(e.second);
+  }
+  {
+    std::lock_guard<std::mutex> g(p.mu);
+    p.pool.insert(p.pool.end(), evs.begin(), evs.end());
   }
   *launches = (int)evs.size();
   *total_ms = tot;

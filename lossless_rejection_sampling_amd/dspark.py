@@ -210,8 +210,9 @@ def dspark_status(workspace, stream=None) -> int:
     return int(lib().dspark_status(_dev(workspace, "workspace", torch.uint8), _stream(stream)))
 
 
-def dspark_profile_enable(kernel_class: int, enabled: bool = True):
-    _check("dspark_profile_enable", lib().dspark_profile_enable(int(kernel_class), int(bool(enabled))))
+def dspark_profile_enable(kernel_class: int, enabled=True):
+    """enabled: False/0 off, True/1 every launch, k > 1 every k-th launch."""
+    _check("dspark_profile_enable", lib().dspark_profile_enable(int(kernel_class), int(enabled)))
 
 
 def dspark_profile_read(kernel_class: int):
