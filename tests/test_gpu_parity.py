@@ -53,6 +53,9 @@ def test_tiny_round():
     dict(B=40, gamma=4, V=12345, r=128, dtype=torch.float32, fdt=torch.bfloat16, temps=(1.0, 1.2)),
     dict(B=70, gamma=3, V=9000, r=256, dtype=torch.bfloat16, fdt=torch.bfloat16, temps=(1.0, 0.0)),
     dict(B=520, gamma=2, V=3001, r=256, dtype=torch.float32, fdt=torch.bfloat16, temps=(0.9,)),
+    # more tiles than workgroups: a partial last round of tiles
+    dict(B=24, gamma=4, V=20000, r=256, dtype=torch.bfloat16, fdt=torch.bfloat16, temps=(1.0, 0.0, 0.8)),
+    dict(B=40, gamma=3, V=24000, r=128, dtype=torch.bfloat16, fdt=torch.bfloat16, temps=(1.3, 0.0)),
 ])
 def test_small_rounds(case):
     rnd = wl.small_random(case["B"], case["gamma"], case["V"], case["r"], device=DEV, seed=case["B"] + case["V"],
