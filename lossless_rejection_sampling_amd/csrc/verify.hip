@@ -310,6 +310,14 @@ __global__ __launch_bounds__(256) void verify_lazy_kernel(VerifyArgs a) {
   }
 
   const int row0 = b * (gamma + 1);
+  const TL* trow0 = static_cast<const TL*>(a.target) + (size_t)row0 * V;
+  const int32_t* xs = a.draft + (size_t)b * gamma;
+  // inputs of the test of position j + 1, which the row's last item runs: the
+  // drafted token, its draft log-probability and its target logit, requested
+  // now so that they have landed by then
+  int x_pre = 0;
+  float lq_pre = 0.0f;
+  if (wave == 0 && j < L) x_pre = xs[j], lq_pre = a.draft_logq[(size_t)b * gamma + j];
   const int blk = ch * kLazyBlocks + wave;
   if (blk < nb) {
     const BlockStat st = block_stats<TL, VEC>(a, row0 + j, blk, effective_temp(a.temperature[b]), lane);
@@ -318,6 +326,8 @@ __global__ __launch_bounds__(256) void verify_lazy_kernel(VerifyArgs a) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // complete at the agent's coherence point
     }
   }
+  float z_pre = 0.0f;
+  if (wave == 0 && j < L) z_pre = load_logit(trow0 + (size_t)j * V + min(max(x_pre, 0), V - 1));
   // count the item once every statistic of it is stored, so the item that finds
   // the row's count full reads them all with its coherent loads
   __syncthreads();
@@ -335,21 +345,21 @@ __global__ __launch_bounds__(256) void verify_lazy_kernel(VerifyArgs a) {
   const bool greedy = !(Tf > 0.0f);
   const double invT = greedy ? 0.0 : 1.0 / (double)Tf;
   const uint32_t off = a.pos_offset ? (uint32_t)a.pos_offset[b] : 0u;
-  const TL* trow0 = static_cast<const TL*>(a.target) + (size_t)row0 * V;
-  const int32_t* xs = a.draft + (size_t)b * gamma;
   int n = j;  // rows 0..n complete, positions 1..n accepted
   RowInfo ri;
   for (;;) {
     ri = row_info(a.bstat + (size_t)(row0 + n) * nb, nb, greedy, invT, lane);
     if (n == L) break;  // every drafted position accepted
     const int k = n + 1;
-    const int x = checked_token(xs[n], V, a.status, kBadDraft);
+    const bool pre = n == j;  // this item's own row: its prefetched inputs
+    const int x = checked_token(pre ? __shfl(x_pre, 0) : xs[n], V, a.status, kBadDraft);
     bool fail;
     if (greedy) {
       fail = x != ri.arg;
     } else {
-      const double lp = ((double)load_logit(trow0 + (size_t)n * V + x) - ri.M) * invT - ri.logS;
-      const double lq = (double)a.draft_logq[(size_t)b * gamma + n];
+      const float z = pre ? __shfl(z_pre, 0) : load_logit(trow0 + (size_t)n * V + x);
+      const double lp = ((double)z - ri.M) * invT - ri.logS;
+      const double lq = pre ? (double)__shfl(lq_pre, 0) : (double)a.draft_logq[(size_t)b * gamma + n];
       const double lnu = log(uniform_from_word(rng_word(a.seed, kAccept, b, k + off, 0)));
       fail = !(lnu < lp - lq);  // accept iff u < min(1, p/q), since ln u < 0
       if (a.debug_logp_logq && lane == 0) {
