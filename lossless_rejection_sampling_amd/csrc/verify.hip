@@ -41,6 +41,19 @@ __device__ __forceinline__ int budget_of(const VerifyArgs& a, int b) {
 }
 
 
+// v_exp_f32 itself: results below 2^-126 flush to zero.  A block sum taken
+// relative to the block maximum holds a term of 1, so the flushed terms cannot
+// change it; exp2f spends five more instructions per element keeping them.
+__device__ __forceinline__ float exp2_flush(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// max of three: fmaxf would first quiet (canonicalise) each value made by bit
+// operations, one more instruction per element
+__device__ __forceinline__ float max3(float x, float y, float z) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(y), "v"(z));
+  return r;
+}
+
 // ---------------------------------------------------------------------------
 // Target row statistics.  A lane holds 64 logits of the block in registers:
 // vector path, bf16: element i*512 + lane*8 + q (eight 16-byte loads);
@@ -87,17 +100,19 @@ __device__ __forceinline__ BlockStat block_stats(const VerifyArgs& a, int row, i
       z[i] = e < len ? load_logit(p + e) : -INFINITY;
     }
   }
-  float m = -INFINITY;
+  float m0 = -INFINITY, m1 = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < 64; ++i) m = fmaxf(m, z[i]);
-  m = wave_max(m);
+  for (int i = 0; i < 64; i += 4) m0 = max3(m0, z[i], z[i + 1]), m1 = max3(m1, z[i + 2], z[i + 3]);
+  const float m = wave_max(fmaxf(m0, m1));
   float s = 0.0f;
   int arg = 0x7fffffff;
   if (T > 0.0f) {
-    const float c = kLog2e / T;
+    // 2^((z - m) c) as 2^(z c - m c): one fused multiply-add per element
+    const float c = kLog2e / T, mc = m == -INFINITY ? 0.0f : m * c;
+    float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 64; ++i) s += exp2f((z[i] - m) * c);
-    s = wave_sum(s);
+    for (int i = 0; i < 64; i += 2) s0 += exp2_flush(fmaf(z[i], c, -mc)), s1 += exp2_flush(fmaf(z[i + 1], c, -mc));
+    s = wave_sum(s0 + s1);
   } else {
 #pragma unroll
     for (int i = 0; i < 64; ++i) {
