@@ -23,6 +23,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr double kLog2eD = 1.4426950408889634;
 
 // Residual-mode passes serve two calls.  The residual draw: slots are the
 // requests queued in slot_req[0..*slot_count), each at its rejected row, with the
@@ -562,6 +563,24 @@ __global__ __launch_bounds__(64) void gemm_stats_valu(GemmArgs a) {
   }
 }
 
+// Shift and mass of one block of 64 tiles held by 16 lanes (4 tiles a lane):
+// e = sum_t S_t exp((d_t - m) / T) with the fp32 maximum of the d_t as the
+// shift m.  Any shift near the largest d_t gives the same block value
+// (m - ref) / T + log(e) up to rounding, and an fp32 maximum takes half the
+// exchange steps of an fp64 one.  v_exp_f32 on the fp64 exponent rounded to
+// fp32; terms below 2^-126 of the largest flush to zero.
+__device__ __forceinline__ void block_mass(const double (&d)[4], const float (&sm)[4], double invT_log2e,
+                                           double& m_out, float& e_out) {
+  float mf = fmaxf(fmaxf((float)d[0], (float)d[1]), fmaxf((float)d[2], (float)d[3]));
+  mf = group16_max(mf);
+  const double m = (double)mf;
+  float e = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    if (sm[k] > 0.0f) e += sm[k] * __builtin_amdgcn_exp2f((float)((d[k] - m) * invT_log2e));
+  m_out = m, e_out = group16_sum(e);
+}
+
 // ---------------------------------------------------------------------------
 // One draw per request at block position pos+1 (a workgroup of 4 wavefronts
 // per request): three-level Gumbel-max over blocks of 64 tiles, tiles of 64
@@ -583,17 +602,20 @@ __device__ __forceinline__ double dot_part(const TF* h, const TF* w, int k0, int
           hv[i] = *reinterpret_cast<const uint4*>(h + k0 + 8 * i);
           wv[i] = *reinterpret_cast<const uint4*>(w + k0 + 8 * i);
         }
+      // a product of two bf16 values (8-bit significands) is exact in fp32; the
+      // sum runs in fp64 over four independent chains
+      double c[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         if (k0 + 8 * i < k1) {
           const uint32_t hh[4] = {hv[i].x, hv[i].y, hv[i].z, hv[i].w}, ww[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            acc += (double)__uint_as_float(hh[q] << 16) * (double)__uint_as_float(ww[q] << 16);
-            acc += (double)__uint_as_float(hh[q] & 0xffff0000u) * (double)__uint_as_float(ww[q] & 0xffff0000u);
+            c[q] += (double)(__uint_as_float(hh[q] << 16) * __uint_as_float(ww[q] << 16));
+            c[q] += (double)(__uint_as_float(hh[q] & 0xffff0000u) * __uint_as_float(ww[q] & 0xffff0000u));
           }
         }
-      return acc;
+      return (c[0] + c[1]) + (c[2] + c[3]);
     }
   }
   for (int k = k0; k < k1; ++k) acc += (double)load_logit(h + k) * (double)load_logit(w + k);
@@ -651,13 +673,9 @@ __global__ __launch_bounds__(256) void draft_select_kernel(DraftSelectArgs a) {
         }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        double m = fmax(fmax(d[q][0], d[q][1]), fmax(d[q][2], d[q][3]));
-        m = group16_max(m);
-        float e = 0.0f;
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-          if (sm[q][k] > 0.0f) e += sm[q][k] * expf((float)((d[q][k] - m) * invT));
-        e = group16_sum(e);
+        double m;
+        float e;
+        block_mass(d[q], sm[q], invT * kLog2eD, m, e);
         const int j = 16 * q + 4 * wave + (lane >> 4);
         if ((lane & 15) == 0 && g0 + j < nblk) s_bm[j] = m, s_be[j] = e;
       }
@@ -762,7 +780,8 @@ __global__ __launch_bounds__(256) void draft_select_kernel(DraftSelectArgs a) {
 //      together; meanwhile waves 0, 1 and 2 compute the block-, tile- and
 //      column-level Gumbel values of this draw (they depend on no data).
 //   2. Records go to LDS; 16-lane groups reduce each block; wave 0 draws the
-//      block and the row's log-sum-exp, then the tile from the LDS copy.
+//      block, then the tile from the LDS copy, while wave 1 forms the row's
+//      log-sum-exp.
 //   3. The chosen tile is recomputed in fp64 (rank split over the four
 //      wavefronts), the column drawn, and U[x] copied for the next position.
 // The arithmetic of every value that decides a draw is that of
@@ -815,33 +834,32 @@ __global__ __launch_bounds__(256) void draft_select_fast(DraftSelectArgs a) {
     const double invT = 1.0 / (double)Tf;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      double d[4];
+      double d[4], m;
+      float sm[4], e;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) d[k] = (double)rec[q][k].x + (double)rec[q][k].y;
-      double m = fmax(fmax(d[0], d[1]), fmax(d[2], d[3]));
-      m = group16_max(m);
-      float e = 0.0f;
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        if (rec[q][k].z > 0.0f) e += rec[q][k].z * expf((float)((d[k] - m) * invT));
-      e = group16_sum(e);
+      for (int k = 0; k < 4; ++k) d[k] = (double)rec[q][k].x + (double)rec[q][k].y, sm[k] = rec[q][k].z;
+      block_mass(d, sm, invT * kLog2eD, m, e);
       const int j = 16 * q + 4 * wave + (lane >> 4);
       if ((lane & 15) == 0 && j < nblk) s_bm[j] = m, s_be[j] = e;
     }
     __syncthreads();
-    if (wave == 0) {
+    if (wave == 1) {
+      // the row's log-sum-exp, beside the draw
+      double m = -INFINITY, e = 0.0;
+      if (lane < nblk) m = s_bm[lane], e = (double)s_be[lane];
+      const double gm = wave_max(m);
+      const double gs = wave_sum(e > 0.0 ? e * exp((m - gm) * invT) : 0.0);
+      if (lane == 0) s_lse = gm * invT + log(gs);
+    } else if (wave == 0) {
       const double mref = s_d[0];
-      // block (lane j) and the row's log-sum-exp
-      double val = -INFINITY, m = -INFINITY, e = 0.0;
+      // block (lane j)
+      double val = -INFINITY;
       int idx = 0x7fffffff;
       if (lane < nblk) {
-        m = s_bm[lane], e = (double)s_be[lane];
-        val = (m - mref) * invT + log(e) + s_g[0][lane];
+        val = (s_bm[lane] - mref) * invT + log((double)s_be[lane]) + s_g[0][lane];
         idx = lane;
       }
       wave_argmax(val, idx);
-      const double gm = wave_max(m);
-      const double gs = wave_sum(e > 0.0 ? e * exp((m - gm) * invT) : 0.0);
       // tile inside the chosen block
       const int blk = index_or(idx, nblk, 0);
       const int t0 = blk * kTilesPerBlock, t1 = min(t0 + kTilesPerBlock, nt);
@@ -852,7 +870,7 @@ __global__ __launch_bounds__(256) void draft_select_fast(DraftSelectArgs a) {
         ti = t0 + lane;
       }
       wave_argmax(tv, ti);
-      if (lane == 0) s_tile = index_or(ti, t1, t0), s_lse = gm * invT + log(gs);
+      if (lane == 0) s_tile = index_or(ti, t1, t0);
     }
     __syncthreads();
     tile = s_tile, lse = s_lse;
