@@ -411,57 +411,88 @@ __global__ __launch_bounds__(256) void verify_lazy_kernel(VerifyArgs a) {
 
 template <typename TF>
 __device__ __forceinline__ double dot_range(const TF* h, const TF* w, int k0, int k1) {
-  double acc = 0.0;
   if constexpr (sizeof(TF) == 2) {
-    if ((((k1 - k0) | k0) & 7) == 0) {
-      for (int k = k0; k < k1; k += 8) {
-        const uint4 hv = *reinterpret_cast<const uint4*>(h + k);
-        const uint4 wv = *reinterpret_cast<const uint4*>(w + k);
-        const uint32_t hh[4] = {hv.x, hv.y, hv.z, hv.w}, ww[4] = {wv.x, wv.y, wv.z, wv.w};
+    if ((((k1 - k0) | k0) & 7) == 0 && k1 - k0 <= 64) {
+      // every load first (one memory round trip); a product of two bf16 values
+      // is exact in fp32, and the sum runs in fp64 over four independent chains
+      uint4 hv[8], wv[8];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          acc += (double)__uint_as_float(hh[q] << 16) * (double)__uint_as_float(ww[q] << 16);
-          acc += (double)__uint_as_float(hh[q] & 0xffff0000u) * (double)__uint_as_float(ww[q] & 0xffff0000u);
+      for (int i = 0; i < 8; ++i)
+        if (k0 + 8 * i < k1) {
+          hv[i] = *reinterpret_cast<const uint4*>(h + k0 + 8 * i);
+          wv[i] = *reinterpret_cast<const uint4*>(w + k0 + 8 * i);
         }
-      }
-      return acc;
+      double c[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (k0 + 8 * i < k1) {
+          const uint32_t hh[4] = {hv[i].x, hv[i].y, hv[i].z, hv[i].w}, ww[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            c[q] += (double)(__uint_as_float(hh[q] << 16) * __uint_as_float(ww[q] << 16));
+            c[q] += (double)(__uint_as_float(hh[q] & 0xffff0000u) * __uint_as_float(ww[q] & 0xffff0000u));
+          }
+        }
+      return (c[0] + c[1]) + (c[2] + c[3]);
     }
   }
+  double acc = 0.0;
   for (int k = k0; k < k1; ++k) acc += (double)load_logit(h + k) * (double)load_logit(w + k);
   return acc;
 }
 
 // fp64 residual r(v) = max(0, p(v) - q(v)) at one column of the rejected row,
 // given the Markov bias of that column.
+// xb, zt: the column's backbone and target logits.
+__device__ __forceinline__ double residual_from(double xb, double zt, const ReqState& st, double invT, double lse_q,
+                                                double bias, double* p_out) {
+  const double d = xb + bias;
+  const double p = exp((zt - st.row_max) * invT - st.row_logsum);
+  const double q = exp(d * invT - lse_q);
+  if (p_out) *p_out = p;
+  return p > q ? p - q : 0.0;
+}
+
 template <typename TL>
 __device__ __forceinline__ double residual_at(const VerifyArgs& a, int b, const ReqState& st, double invT,
                                               double lse_q, int v, double bias, double* p_out) {
   const int V = a.V, n = st.n;
   const TL* trow = static_cast<const TL*>(a.target) + ((size_t)b * (a.gamma + 1) + n) * V;
   const TL* brow = static_cast<const TL*>(a.base) + ((size_t)b * a.gamma + n) * V;
-  const double d = (double)load_logit(brow + v) + bias;
-  const double p = exp(((double)load_logit(trow + v) - st.row_max) * invT - st.row_logsum);
-  const double q = exp(d * invT - lse_q);
-  if (p_out) *p_out = p;
-  return p > q ? p - q : 0.0;
+  return residual_from((double)load_logit(brow + v), (double)load_logit(trow + v), st, invT, lse_q, bias, p_out);
 }
 
 // One workgroup of 4 wavefronts per request that rejected: block and tile from
 // the residual tile masses, column from an fp64 recompute of the chosen tile
-// (rank split over the wavefronts).
+// (rank split over the wavefronts).  Memory round trips on the critical path:
+//   1. the request's state with the tile masses of the first 64 blocks (wave w,
+//      lane l: tile l of blocks w, w + 4, ...), the masses being independent of
+//      the state; the Gumbel values of the three levels are computed while the
+//      previous token, the draft log-sum-exp and the masses land;
+//   2. the chosen block's tile masses again (an L2 hit);
+//   3. the tile's factor rows with its backbone and target logits.
+// Block masses sum in the order of the per-block loop (wave by wave, blocks in
+// increasing order), and each wave takes one logarithm per lane for its blocks.
 template <typename TL, typename TF>
 __global__ __launch_bounds__(256) void residual_select_kernel(VerifyArgs a) {
-  __shared__ double s_val[4], s_tot[4], s_part[4][64];
+  constexpr int kPer = 16;  // blocks per wavefront in one pass: 64 blocks a pass
+  __shared__ double s_val[4], s_tot[4], s_part[4][64], s_gmid[64], s_gleaf[64];
   __shared__ int s_idx[4];
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int gamma = a.gamma, V = a.V, nt = a.n_tiles, r = a.r;
+  const int nblk = (nt + kTilesPerBlock - 1) / kTilesPerBlock;
+  const float* R = a.rsum + (size_t)b * nt;
   const ReqState st = a.req[b];
+  float rm[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) rm[i] = R[min((wave + 4 * i) * kTilesPerBlock + lane, nt - 1)];
   // the lazy pass's counters of this request (and the residual work list) go
   // back to zero for the next call: every kernel that used them has finished
   if (tid <= a.gamma) a.rowcnt[(size_t)b * (a.gamma + 1) + tid] = 0u;
   if (tid == 0) a.vstate[b] = 0u;
   if (b == 0 && tid == 0) *a.slot_count = 0u;
   if (!st.pending) return;  // uniform across the workgroup
-  const int gamma = a.gamma, V = a.V, nt = a.n_tiles, n = st.n, r = a.r;
+  const int n = st.n;
   const double invT = 1.0 / (double)a.temperature[b];
   const uint32_t off = a.pos_offset ? (uint32_t)a.pos_offset[b] : 0u;
   const uint32_t rpos = n + 1 + off;
@@ -474,23 +505,37 @@ __global__ __launch_bounds__(256) void residual_select_kernel(VerifyArgs a) {
     }
     return;
   }
-  int prev = n == 0 ? a.prev0[b] : a.draft[(size_t)b * gamma + n - 1];
-  prev = checked_token(prev, V, a.status, n == 0 ? kBadPrev : kBadDraft);
+  const int prev_raw = n == 0 ? a.prev0[b] : a.draft[(size_t)b * gamma + n - 1];
   const double lse_q = a.draft_lse[(size_t)b * gamma + n];
-  const float* R = a.rsum + (size_t)b * nt;
-  const int nblk = (nt + kTilesPerBlock - 1) / kTilesPerBlock;
+  if (wave == 1) s_gmid[lane] = gumbel(a.seed, kFinalMid, b, rpos, lane);
+  if (wave == 2) s_gleaf[lane] = gumbel(a.seed, kFinalLeaf, b, rpos, lane);
 
-  // block masses: wavefront w sums blocks w, w+4, ... (one coalesced read each)
+  // block masses and the block draw
   double tot = 0.0, best = -INFINITY;
   int bi = 0x7fffffff;
-  for (int blk = wave; blk < nblk; blk += 4) {
-    const int t = blk * kTilesPerBlock + lane;
-    const double rb = wave_sum(t < nt ? (double)R[t] : 0.0);
-    tot += rb;
-    if (rb > 0.0) {
-      const double val = log(rb) + gumbel(a.seed, kFinalTop, b, rpos, blk);
-      if (val > best) best = val, bi = blk;
+  for (int c0 = 0; c0 < nblk; c0 += 4 * kPer) {
+    if (c0 > 0) {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) rm[i] = R[min((c0 + wave + 4 * i) * kTilesPerBlock + lane, nt - 1)];
     }
+    const int my_blk = c0 + wave + 4 * lane;  // lane i < kPer: the wave's i-th block of the pass
+    const double g = lane < kPer && my_blk < nblk ? gumbel(a.seed, kFinalTop, b, rpos, my_blk) : 0.0;
+    double mine = 0.0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int blk = c0 + wave + 4 * i;
+      if (blk < nblk) {  // uniform across the wavefront
+        const int t = blk * kTilesPerBlock + lane;
+        const double rb = wave_sum(t < nt ? (double)rm[i] : 0.0);
+        tot += rb;
+        if (lane == i) mine = rb;
+      }
+    }
+    double val = -INFINITY;
+    int idx = 0x7fffffff;
+    if (lane < kPer && my_blk < nblk && mine > 0.0) val = log(mine) + g, idx = my_blk;
+    wave_argmax(val, idx);
+    if (val > best) best = val, bi = idx;  // passes in increasing block order: ties keep the lowest
   }
   if (lane == 0) s_val[wave] = best, s_idx[wave] = bi, s_tot[wave] = tot;
   __syncthreads();
@@ -511,21 +556,29 @@ __global__ __launch_bounds__(256) void residual_select_kernel(VerifyArgs a) {
     }
     return;
   }
+  // tile inside the chosen block (every wavefront, so that none waits for another)
   bi = index_or(bi, nblk, 0);
   const int t0 = bi * kTilesPerBlock, t1 = min(t0 + kTilesPerBlock, nt);
   double val = -INFINITY;
   int ti = 0x7fffffff;
-  if (t0 + lane < t1 && R[t0 + lane] > 0.0f) {
-    val = log((double)R[t0 + lane]) + gumbel(a.seed, kFinalMid, b, rpos, lane);
-    ti = t0 + lane;
+  if (t0 + lane < t1) {
+    const float rt = R[t0 + lane];
+    if (rt > 0.0f) val = log((double)rt) + s_gmid[lane], ti = t0 + lane;
   }
   wave_argmax(val, ti);
   ti = index_or(ti, t1, t0);
 
-  // Markov bias of the chosen tile in fp64, rank split over the wavefronts
+  // Markov bias of the chosen tile in fp64, rank split over the wavefronts; the
+  // column's backbone and target logits come in the same round trip
   const int v = ti * kTile + lane;
   const int kq = (r + 3) / 4, k0 = min(wave * kq, r), k1 = min(k0 + kq, r);
+  const int prev = checked_token(prev_raw, V, a.status, n == 0 ? kBadPrev : kBadDraft);
   const TF* h = static_cast<const TF*>(a.U) + (size_t)prev * r;
+  double xb = 0.0, zt = 0.0;
+  if (wave == 0 && v < V) {
+    const TL* brow = static_cast<const TL*>(a.base) + ((size_t)b * gamma + n) * V;
+    xb = (double)load_logit(brow + v), zt = (double)load_logit(trow + v);
+  }
   s_part[wave][lane] = v < V ? dot_range<TF>(h, static_cast<const TF*>(a.Wt) + (size_t)v * r, k0, k1) : 0.0;
   __syncthreads();
   if (wave != 0) return;
@@ -534,8 +587,8 @@ __global__ __launch_bounds__(256) void residual_select_kernel(VerifyArgs a) {
   if (v < V) {
     double p;
     const double bias = (s_part[0][lane] + s_part[1][lane]) + (s_part[2][lane] + s_part[3][lane]);
-    const double rv = residual_at<TL>(a, b, st, invT, lse_q, v, bias, &p);
-    const double g = gumbel(a.seed, kFinalLeaf, b, rpos, lane);
+    const double rv = residual_from(xb, zt, st, invT, lse_q, bias, &p);
+    const double g = s_gleaf[lane];
     if (rv > 0.0) lv = log(rv) + g, vi = v;
     lp = log(p) + g;
   }
