@@ -34,6 +34,7 @@ constexpr int kThreads = 256;
 constexpr int kLanesPerCand = 16;
 constexpr int kCandPerGroup = kThreads / kLanesPerCand;
 constexpr uint32_t kNoFail = 0x7fffffffu;
+constexpr int kMaxGamma = 16;  // the ABI's largest block length
 
 #pragma clang fp contract(off)
 
@@ -97,8 +98,7 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(ScheduleArgs a) {
     float acc = 1.0f;
     int lead = 0;  // leading positions above the threshold
     bool run = true;
-    for (int j = 0; j < gamma; ++j) {
-      float cj = a.conf[(size_t)b * gamma + j];
+    auto admit = [&](int j, float cj) {
       if (!(cj > 0.0f && cj < 1.0f)) {
         bad = true;
         cj = cj > 0.0f ? 0x1.fffffep-1f : 0x1p-126f;  // clamp into (0, 1); NaN -> tiny
@@ -109,6 +109,17 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(ScheduleArgs a) {
       acc = acc * cj;
       const uint32_t q = (uint32_t)floor((double)acc * 4294967296.0);
       key[b * gamma + j] = ((unsigned long long)(0xFFFFFFFFu - q) << 32) | (uint32_t)(b * gamma + j);
+    };
+    if (!a.tau) {
+      // the request's scores in one memory round trip (gamma <= kMaxGamma)
+      float cv[kMaxGamma];
+#pragma unroll
+      for (int j = 0; j < kMaxGamma; ++j) cv[j] = j < gamma ? a.conf[(size_t)b * gamma + j] : 0.5f;
+#pragma unroll
+      for (int j = 0; j < kMaxGamma; ++j)
+        if (j < gamma) admit(j, cv[j]);
+    } else {
+      for (int j = 0; j < gamma; ++j) admit(j, a.conf[(size_t)b * gamma + j]);
     }
     if (blockIdx.x == 0 && !ranked) {
       const int fixed = (int)fmin(fmax(a.param, 0.0), (double)gamma);
@@ -131,12 +142,21 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(ScheduleArgs a) {
   if (i < nk) {
     const ulonglong2* k2 = reinterpret_cast<const ulonglong2*>(key);
     const int n2 = (nk + 1) / 2;
-    for (int t = sub; t < n2; t += kLanesPerCand) {
-      const ulonglong2 w = k2[t];
+    auto count = [&](const ulonglong2& w) {
       const bool b0 = w.x < ki, b1 = w.y < ki;
       cnt += (b0 ? 1u : 0u) + (b1 ? 1u : 0u);
       tau += (b0 ? 0xFFFFFFFFull - (w.x >> 32) : 0ull) + (b1 ? 0xFFFFFFFFull - (w.y >> 32) : 0ull);
+    };
+    // eight LDS reads in flight per lane
+    int t = sub;
+    for (; t + 7 * kLanesPerCand < n2; t += 8 * kLanesPerCand) {
+      ulonglong2 w[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) w[u] = k2[t + u * kLanesPerCand];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) count(w[u]);
     }
+    for (; t < n2; t += kLanesPerCand) count(k2[t]);
   }
   static_assert(kLanesPerCand == 16, "one DPP row per candidate");
   cnt = reduce16(cnt, OpSum{});
@@ -166,17 +186,29 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(ScheduleArgs a) {
   if (tid == 0) s_last = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1;
   __syncthreads();
   if (!s_last) return;
+  // the ranks of this thread's first request, requested with the cut's inputs
+  int rk[kMaxGamma];
+  auto load_ranks = [&](int b) {
+#pragma unroll
+    for (int j = 0; j < kMaxGamma; ++j)
+      rk[j] = j < gamma ? __hip_atomic_load(a.rank + b * gamma + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+  };
+  if (tid < B) load_ranks(tid);
   int stop;
   if (a.rule == DSPARK_SCHED_EARLY_STOP) {
     const uint32_t enc = __hip_atomic_load(a.stop_enc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     stop = enc ? (int)(kNoFail - enc) : nk;
   } else {
-    // the first largest Theta over the cuts m = 0..nk
+    // the first largest Theta over the cuts m = 0..nk, 8 loads in flight a thread
     double best = -1.0;
     int bm = 0x7fffffff;
-    for (int m = tid; m <= nk; m += kThreads) {
-      const double th = load_coherent(a.theta + m);
-      if (th > best) best = th, bm = m;  // m increases: ties keep the first
+    for (int m0 = tid; m0 <= nk; m0 += 8 * kThreads) {
+      double th[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) th[u] = m0 + u * kThreads <= nk ? load_coherent(a.theta + m0 + u * kThreads) : -1.0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (th[u] > best) best = th[u], bm = m0 + u * kThreads;  // m increases: ties keep the first
     }
     wave_argmax(best, bm);
     if ((tid & 63) == 0) s_best[tid >> 6] = best, s_bestm[tid >> 6] = bm;
@@ -187,9 +219,10 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(ScheduleArgs a) {
     stop = index_or(bm, nk + 1, 0);
   }
   for (int b = tid; b < B; b += kThreads) {
+    if (b != tid) load_ranks(b);
     int n = 0;
-    for (int j = 0; j < gamma; ++j)
-      n += __hip_atomic_load(a.rank + b * gamma + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < stop ? 1 : 0;
+#pragma unroll
+    for (int j = 0; j < kMaxGamma; ++j) n += j < gamma && rk[j] < stop ? 1 : 0;
     a.budget[b] = n;
   }
   if (tid == 0) {
