@@ -33,6 +33,7 @@ N_SETS = 3
 
 
 TIMING_PERIOD = 7
+ROUND_REPS = 60
 
 
 def parse():
@@ -165,6 +166,10 @@ def main():
     ds.dspark_profile_enable(ds.KERNEL_CLASSES[dominant], False)
     assert ds.dspark_status(bufs[0].workspace) == ds.DSPARK_OK
 
+    # per-round distribution, after the timed region: ROUND_REPS rounds, each
+    # between HIP events on the stream the rounds run on
+    round_ms = round_distribution(step, args.steps)
+
     budgets = bufs[0].budget.cpu().numpy()
     verified = int(budgets.sum())
     emitted = int(bufs[0].num_emitted.sum().item())
@@ -231,12 +236,31 @@ def main():
                    "B": base_round.B, "gamma": base_round.gamma, "V": base_round.V, "r": base_round.r,
                    "verified_per_round": verified, "emitted_per_round": emitted,
                    "emitted_tokens_per_s": emitted / sec_per_step},
+        "round_ms": round_ms,
         "roofline": roof,
         "kernels": kernels,
         "cpu_baseline": cpu,
         "extras": extras,
     }
     print(json.dumps(line), flush=True)
+
+
+def round_distribution(step, start, reps=None):
+    """Median, 10th and 90th percentile of single-round times (ms), each round
+    between two HIP events recorded on the current stream."""
+    import numpy as np
+    import torch
+
+    reps = reps or ROUND_REPS
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i, (e0, e1) in enumerate(evs):
+        e0.record()
+        step(start + i)
+        e1.record()
+    torch.cuda.synchronize()
+    t = np.array([e0.elapsed_time(e1) for e0, e1 in evs])
+    return dict(reps=reps, median=float(np.median(t)), p10=float(np.percentile(t, 10)),
+                p90=float(np.percentile(t, 90)))
 
 
 def measure_peaks(reps=3):
@@ -376,6 +400,26 @@ def cpu_baseline(rnd, budgets, seconds):
         done += 1
     per_req = t_work / done
     round_s = per_req * rnd.B + t_sched
+    # the same at one thread, on the first requests of the sample
+    single = None
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            n1, t1 = 0, 0.0
+            while t1 < seconds / 4 and n1 < done:
+                idx = [n1]
+                t = torch.as_tensor(idx, device=rnd.base.device)
+                base, target = h(rnd.base.index_select(0, t)), h(rnd.target.index_select(0, t))
+                prev0, T = h(rnd.prev0.index_select(0, t)), h(rnd.temperature.index_select(0, t))
+                c0 = time.perf_counter()
+                dr = od.draft_round(base, U, W, prev0, T, rnd.seed, req_ids=idx)
+                od.verify(target, base, U, W, prev0, dr.tokens, T, rnd.seed, sched.budget[idx], req_ids=idx)
+                t1 += time.perf_counter() - c0
+                n1 += 1
+            single = {"value": float(np.sum(budgets)) / (t1 / n1 * rnd.B + t_sched), "cores": 1,
+                      "sample": f"{n1} requests ({t1:.1f} s), same extrapolation"}
+    except Exception:
+        single = None
     return {
         "value": float(np.sum(budgets)) / round_s,
         "unit": "verified draft tokens/s",
@@ -383,6 +427,7 @@ def cpu_baseline(rnd, budgets, seconds):
         "kind": "oracle",
         "sample": f"{done} of {rnd.B} requests timed whole (draft + verify, {t_work:.1f} s) plus the "
                   f"scheduler over all {rnd.B} ({t_sched:.2f} s), extrapolated per request to the batch",
+        "single_thread": single,
     }
 
 
