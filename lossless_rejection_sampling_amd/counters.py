@@ -10,6 +10,7 @@ bench.py reports the traffic only while that hash still matches.
   python3 -m lossless_rejection_sampling_amd.counters summarize CSV KERNEL COUNTER
   python3 -m lossless_rejection_sampling_amd.counters report BENCH_FETCH BENCH_WRITE COPY_FETCH COPY_WRITE KERNEL CLASS
   python3 -m lossless_rejection_sampling_amd.counters mfma CSV KERNEL CLASS FLOPS_PER_LAUNCH
+  python3 -m lossless_rejection_sampling_amd.counters table BENCH_FETCH BENCH_WRITE COPY_FETCH COPY_WRITE
   python3 -m lossless_rejection_sampling_amd.counters source-hash
 """
 
@@ -128,6 +129,48 @@ def report(bench_fetch, bench_write, copy_fetch, copy_write, kernel, cls, comman
     return "\n".join(lines)
 
 
+def short_name(name: str) -> str:
+    m = re.search(r"::([A-Za-z_0-9]+)(<[^()]*>)?\(", name)
+    return (m.group(1) + (m.group(2) or "")) if m else name[:60]
+
+
+def kernel_table(bench_fetch, bench_write, copy_fetch, copy_write) -> str:
+    """Markdown table of FETCH_SIZE and WRITE_SIZE per dispatch (scaled to bytes)
+    for every library kernel in the two counter runs."""
+    kf = calibration(copy_fetch, "FETCH_SIZE")
+    kw = calibration(copy_write, "WRITE_SIZE")
+
+    def means(path, counter):
+        acc = {}
+        with open(path, newline="") as f:
+            for row in csv.DictReader(f):
+                name = row.get("Kernel_Name", "")
+                if "dspark" not in name or row.get("Counter_Name") != counter:
+                    continue
+                d = acc.setdefault(short_name(name), [0, 0.0, 0.0])
+                d[0] += 1
+                d[1] += float(row["Counter_Value"])
+                d[2] += float(row["End_Timestamp"]) - float(row["Start_Timestamp"])
+        return {k: (n, v / n, ns / n) for k, (n, v, ns) in acc.items()}
+
+    fe, wr = means(bench_fetch, "FETCH_SIZE"), means(bench_write, "WRITE_SIZE")
+    lines = [
+        "| kernel | dispatches | fetch MB | write MB | total MB per launch | duration us (fetch run) | GB/s |",
+        "|---|---:|---:|---:|---:|---:|---:|",
+    ]
+    rows = []
+    for k in fe:
+        if k not in wr:
+            continue
+        n, fkib, ns = fe[k]
+        fb, wb = fkib * kf, wr[k][1] * kw
+        rows.append((k, n, fb, wb, ns))
+    for k, n, fb, wb, ns in sorted(rows, key=lambda x: -(x[2] + x[3]) * x[1]):
+        lines.append(f"| `{k}` | {n} | {fb / 1e6:.2f} | {wb / 1e6:.2f} | {(fb + wb) / 1e6:.2f} | {ns / 1e3:.1f} | "
+                     f"{(fb + wb) / ns:.0f} |")
+    return "\n".join(lines) + "\n"
+
+
 MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
 MOPS_FLOPS = 512           # SQ_INSTS_VALU_MFMA_MOPS_* count units of 512 flops
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
@@ -187,6 +230,9 @@ def mfma_report(path: str, kernel: str, cls: str, flops_per_launch: float) -> st
 def main(argv):
     if len(argv) == 7 and argv[0] == "report":
         print(report(*argv[1:]), end="")
+        return
+    if len(argv) == 5 and argv[0] == "table":
+        print(kernel_table(*argv[1:]), end="")
         return
     if len(argv) == 5 and argv[0] == "mfma":
         print(mfma_report(argv[1], argv[2], argv[3], float(argv[4])), end="")

@@ -1284,7 +1284,14 @@ __global__ __launch_bounds__(512, 1) void gemm_residual_coalesced(GemmArgs a) {
   if (walkers < 1) walkers = 1;
   const int group = (int)blockIdx.x / walkers;
   const int nt = a.n_tiles, V = a.V;
-  if (group >= ngroups || (int)blockIdx.x - group * walkers >= nt) return;  // uniform
+  // Walker w = blockIdx.x - group walkers runs on XCD w % 8 and takes tiles
+  // run_pos, run_pos + walkers, ...: in each round of `walkers` tiles, the
+  // walkers of one XCD take walkers / 8 adjacent tiles, so the 4-byte masses
+  // of neighbouring tiles of a slot's row meet in one L2 and leave it as whole
+  // lines (dealt round robin, each line was written back piecemeal by 8 L2s).
+  const int w = (int)blockIdx.x - group * walkers;
+  const int run_pos = (walkers & 7) == 0 ? (w & 7) * (walkers >> 3) + (w >> 3) : w;
+  if (group >= ngroups || run_pos >= nt) return;  // uniform
   const int sg0 = group * kResSlots;
   const uint16_t* Wt = static_cast<const uint16_t*>(a.Wt);
 
@@ -1412,7 +1419,7 @@ __global__ __launch_bounds__(512, 1) void gemm_residual_coalesced(GemmArgs a) {
   };
 
   const int G = walkers;
-  int t = (int)blockIdx.x - group * walkers;
+  int t = run_pos;
   f32x16 acc0, acc1;
   fill_w(t, 0);
   if (t + G < nt) fill_w(t + G, 1);
