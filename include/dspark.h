@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define DSPARK_ABI_VERSION 3
+#define DSPARK_ABI_VERSION 4
 
 enum dspark_status_code {
   DSPARK_OK = 0,
@@ -186,6 +186,24 @@ int dspark_schedule(const float* conf, const double* sps_B, const double* sps_va
 int dspark_schedule_ex(const float* conf, const float* tau, const double* sps_B, const double* sps_val,
                        int n_points, int B, int gamma, int rule, double param, int32_t* budget,
                        void* workspace, void* stream);
+
+/*
+ * dspark_draft_schedule -- dspark_draft_round followed by dspark_schedule_ex on
+ * the same stream and workspace, in one call ([P1], [P2]).  The scheduler reads
+ * only the confidence scores, so it does not depend on the draft: its
+ * workgroups run in the same launch as the draw of the last block position
+ * (both are bound by memory latency, not bandwidth), when that draw uses the
+ * kernel for rows of at most 4096 tiles (V <= 262144); otherwise it is a launch
+ * of its own after the draft round.  Outputs, arithmetic and errors are those
+ * of the two calls; the arguments are theirs (budget as in dspark_schedule_ex).
+ * Workspace: dspark_workspace_bytes(B, gamma, V, r).
+ */
+int dspark_draft_schedule(const void* base_logits, int logits_dtype, const void* U, const void* W,
+                          int factor_dtype, const int32_t* prev0, const float* temperature, uint64_t seed,
+                          const int32_t* pos_offset, int B, int gamma, int V, int r, int32_t* draft_tokens,
+                          float* draft_logq, double* draft_lse, const float* conf, const float* tau,
+                          const double* sps_B, const double* sps_val, int n_points, int rule, double param,
+                          int32_t* budget, void* workspace, void* stream);
 
 /*
  * dspark_verify -- [P3] lossless verification with the [P4] bonus token.

@@ -143,6 +143,95 @@ using namespace dspark;
     if ((expr) != hipSuccess) return DSPARK_EHIP; \
   } while (0)
 
+namespace {
+
+// Arguments of the scheduler over `workspace` (its part of the layout and the
+// status word), or DSPARK_EINVAL with nothing enqueued.
+int schedule_args(const float* conf, const float* tau, const double* sps_B, const double* sps_val, int n_points,
+                  int B, int gamma, int rule, double param, int32_t* budget, void* workspace, ScheduleArgs& a) {
+  if (!schedule_sizes_ok(B, gamma)) return DSPARK_EINVAL;
+  if (rule < DSPARK_SCHED_EARLY_STOP || rule > DSPARK_SCHED_THRESHOLD) return DSPARK_EINVAL;
+  const bool table = rule == DSPARK_SCHED_EARLY_STOP || rule == DSPARK_SCHED_ARGMAX;
+  if (table && (n_points < 2 || n_points > 1024 || !sps_B || !sps_val)) return DSPARK_EINVAL;
+  if (!(param == param)) return DSPARK_EINVAL;  // NaN
+  if (!conf || !budget || !workspace) return DSPARK_EINVAL;
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return DSPARK_EINVAL;
+  a = ScheduleArgs{};
+  a.conf = conf, a.tau = tau, a.sps_B = sps_B, a.sps_val = sps_val, a.n_points = table ? n_points : 0;
+  a.B = B, a.gamma = gamma, a.rule = rule, a.param = param, a.budget = budget;
+  a.status = at<uint32_t>(workspace, 0);
+  a.ticket = a.status + 2, a.stop_enc = a.status + 3;
+  a.rank = at<int32_t>(workspace, align_up(kHeaderBytes));
+  a.theta = at<double>(workspace, align_up(kHeaderBytes) + align_up((size_t)B * gamma * sizeof(int32_t)));
+  return DSPARK_OK;
+}
+
+int draft_args_ok(const void* base_logits, int logits_dtype, const void* U, const void* W, int factor_dtype,
+                  const int32_t* prev0, const float* temperature, int B, int gamma, int V, int r,
+                  int32_t* draft_tokens, float* draft_logq, double* draft_lse, void* workspace) {
+  if (!sizes_ok(B, gamma, V, r) || !dtype_ok(logits_dtype) || !dtype_ok(factor_dtype)) return DSPARK_EINVAL;
+  if (!base_logits || !U || !W || !prev0 || !temperature || !draft_tokens || !draft_logq || !draft_lse ||
+      !workspace)
+    return DSPARK_EINVAL;
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return DSPARK_EINVAL;
+  return DSPARK_OK;
+}
+
+// The draft round on validated arguments; with `sched`, the scheduler too: in
+// the launch of the last draw when that draw uses the fast kernel, else after it.
+int draft_round(const void* base_logits, int logits_dtype, const void* U, const void* W, int factor_dtype,
+                const int32_t* prev0, const float* temperature, uint64_t seed, const int32_t* pos_offset, int B,
+                int gamma, int V, int r, int32_t* draft_tokens, float* draft_logq, double* draft_lse,
+                void* workspace, hipStream_t s, const ScheduleArgs* sched) {
+  const Layout L = layout(B, gamma, V, r);
+  uint32_t* status = at<uint32_t>(workspace, L.header);
+
+  GemmArgs g{};
+  g.base = base_logits, g.U = U, g.Wt = W, g.prev0 = prev0, g.draft = draft_tokens;
+  g.temperature = temperature;
+  g.B = B, g.gamma = gamma, g.V = V, g.r = r, g.n_tiles = L.n_tiles;
+  g.tstat = at<TileStat>(workspace, L.tstat);
+  g.status = status;
+
+  DraftSelectArgs d{};
+  d.base = base_logits, d.U = U, d.Wt = W, d.prev0 = prev0, d.temperature = temperature;
+  d.pos_offset = pos_offset, d.tstat = g.tstat, d.seed = seed;
+  d.B = B, d.gamma = gamma, d.V = V, d.r = r, d.n_tiles = L.n_tiles;
+  d.draft = draft_tokens, d.logq = draft_logq, d.lse = draft_lse, d.status = status;
+  // the streaming GEMM takes the U rows of the previous tokens from this table
+  // (filled by the draw of the previous position) instead of gathering them
+  const bool table = factor_dtype == DSPARK_BF16 && (r == 128 || r == 256);
+  d.hrows = table ? at<void>(workspace, L.hrows) : nullptr;
+
+  for (int pos = 0; pos < gamma; ++pos) {
+    g.pos = pos;
+    g.hrows = pos > 0 ? d.hrows : nullptr;
+    d.pos = pos;
+    {
+      ProfileScope ps(kClsDraftGemm, s);
+      DSPARK_TRY(launch_gemm_stats(g, logits_dtype, factor_dtype, false, s));
+    }
+    if (sched && pos == gamma - 1) {
+      // the last draw and the scheduler, both bound by latency, in one launch
+      ProfileScope ps(kClsDraftSelect, s);
+      const hipError_t e = launch_draft_select_schedule(d, *sched, logits_dtype, factor_dtype, s);
+      if (e == hipSuccess) return DSPARK_OK;
+      if (e != hipErrorNotSupported) return DSPARK_EHIP;
+    }
+    {
+      ProfileScope ps(kClsDraftSelect, s);
+      DSPARK_TRY(launch_draft_select(d, logits_dtype, factor_dtype, s));
+    }
+  }
+  if (sched) {
+    ProfileScope ps(kClsSchedule, s);
+    DSPARK_TRY(launch_schedule(*sched, s));
+  }
+  return DSPARK_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int dspark_abi_version(void) { return DSPARK_ABI_VERSION; }
@@ -173,66 +262,37 @@ int dspark_draft_round(const void* base_logits, int logits_dtype, const void* U,
                        uint64_t seed, const int32_t* pos_offset, int B, int gamma, int V, int r,
                        int32_t* draft_tokens, float* draft_logq, double* draft_lse, void* workspace,
                        void* stream) {
-  if (!sizes_ok(B, gamma, V, r) || !dtype_ok(logits_dtype) || !dtype_ok(factor_dtype)) return DSPARK_EINVAL;
-  if (!base_logits || !U || !W || !prev0 || !temperature || !draft_tokens || !draft_logq || !draft_lse ||
-      !workspace)
-    return DSPARK_EINVAL;
-  if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return DSPARK_EINVAL;
-  const Layout L = layout(B, gamma, V, r);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  uint32_t* status = at<uint32_t>(workspace, L.header);
+  const int ok = draft_args_ok(base_logits, logits_dtype, U, W, factor_dtype, prev0, temperature, B, gamma, V, r,
+                               draft_tokens, draft_logq, draft_lse, workspace);
+  if (ok != DSPARK_OK) return ok;
+  return draft_round(base_logits, logits_dtype, U, W, factor_dtype, prev0, temperature, seed, pos_offset, B, gamma,
+                     V, r, draft_tokens, draft_logq, draft_lse, workspace, static_cast<hipStream_t>(stream),
+                     nullptr);
+}
 
-  GemmArgs g{};
-  g.base = base_logits, g.U = U, g.Wt = W, g.prev0 = prev0, g.draft = draft_tokens;
-  g.temperature = temperature;
-  g.B = B, g.gamma = gamma, g.V = V, g.r = r, g.n_tiles = L.n_tiles;
-  g.tstat = at<TileStat>(workspace, L.tstat);
-  g.status = status;
-
-  DraftSelectArgs d{};
-  d.base = base_logits, d.U = U, d.Wt = W, d.prev0 = prev0, d.temperature = temperature;
-  d.pos_offset = pos_offset, d.tstat = g.tstat, d.seed = seed;
-  d.B = B, d.gamma = gamma, d.V = V, d.r = r, d.n_tiles = L.n_tiles;
-  d.draft = draft_tokens, d.logq = draft_logq, d.lse = draft_lse, d.status = status;
-  // the streaming GEMM takes the U rows of the previous tokens from this table
-  // (filled by the draw of the previous position) instead of gathering them
-  const bool table = factor_dtype == DSPARK_BF16 && (r == 128 || r == 256);
-  d.hrows = table ? at<void>(workspace, L.hrows) : nullptr;
-
-  for (int pos = 0; pos < gamma; ++pos) {
-    g.pos = pos;
-    g.hrows = pos > 0 ? d.hrows : nullptr;
-    d.pos = pos;
-    {
-      ProfileScope ps(kClsDraftGemm, s);
-      DSPARK_TRY(launch_gemm_stats(g, logits_dtype, factor_dtype, false, s));
-    }
-    {
-      ProfileScope ps(kClsDraftSelect, s);
-      DSPARK_TRY(launch_draft_select(d, logits_dtype, factor_dtype, s));
-    }
-  }
-  return DSPARK_OK;
+int dspark_draft_schedule(const void* base_logits, int logits_dtype, const void* U, const void* W,
+                          int factor_dtype, const int32_t* prev0, const float* temperature, uint64_t seed,
+                          const int32_t* pos_offset, int B, int gamma, int V, int r, int32_t* draft_tokens,
+                          float* draft_logq, double* draft_lse, const float* conf, const float* tau,
+                          const double* sps_B, const double* sps_val, int n_points, int rule, double param,
+                          int32_t* budget, void* workspace, void* stream) {
+  ScheduleArgs a;
+  int ok = schedule_args(conf, tau, sps_B, sps_val, n_points, B, gamma, rule, param, budget, workspace, a);
+  if (ok != DSPARK_OK) return ok;
+  ok = draft_args_ok(base_logits, logits_dtype, U, W, factor_dtype, prev0, temperature, B, gamma, V, r, draft_tokens,
+                     draft_logq, draft_lse, workspace);
+  if (ok != DSPARK_OK) return ok;
+  return draft_round(base_logits, logits_dtype, U, W, factor_dtype, prev0, temperature, seed, pos_offset, B, gamma,
+                     V, r, draft_tokens, draft_logq, draft_lse, workspace, static_cast<hipStream_t>(stream), &a);
 }
 
 int dspark_schedule_ex(const float* conf, const float* tau, const double* sps_B, const double* sps_val,
                        int n_points, int B, int gamma, int rule, double param, int32_t* budget,
                        void* workspace, void* stream) {
-  if (!schedule_sizes_ok(B, gamma)) return DSPARK_EINVAL;
-  if (rule < DSPARK_SCHED_EARLY_STOP || rule > DSPARK_SCHED_THRESHOLD) return DSPARK_EINVAL;
-  const bool table = rule == DSPARK_SCHED_EARLY_STOP || rule == DSPARK_SCHED_ARGMAX;
-  if (table && (n_points < 2 || n_points > 1024 || !sps_B || !sps_val)) return DSPARK_EINVAL;
-  if (!(param == param)) return DSPARK_EINVAL;  // NaN
-  if (!conf || !budget || !workspace) return DSPARK_EINVAL;
-  if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return DSPARK_EINVAL;
+  ScheduleArgs a;
+  const int ok = schedule_args(conf, tau, sps_B, sps_val, n_points, B, gamma, rule, param, budget, workspace, a);
+  if (ok != DSPARK_OK) return ok;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  ScheduleArgs a{};
-  a.conf = conf, a.tau = tau, a.sps_B = sps_B, a.sps_val = sps_val, a.n_points = table ? n_points : 0;
-  a.B = B, a.gamma = gamma, a.rule = rule, a.param = param, a.budget = budget;
-  a.status = at<uint32_t>(workspace, 0);
-  a.ticket = a.status + 2, a.stop_enc = a.status + 3;
-  a.rank = at<int32_t>(workspace, align_up(kHeaderBytes));
-  a.theta = at<double>(workspace, align_up(kHeaderBytes) + align_up((size_t)B * gamma * sizeof(int32_t)));
   ProfileScope ps(kClsSchedule, s);
   DSPARK_TRY(launch_schedule(a, s));
   return DSPARK_OK;

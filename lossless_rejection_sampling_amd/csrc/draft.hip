@@ -14,6 +14,7 @@
 
 #include "dspark.h"
 #include "kernels.hpp"
+#include "schedule_body.hpp"
 
 namespace dspark {
 namespace {
@@ -787,7 +788,7 @@ __global__ __launch_bounds__(256) void draft_select_kernel(DraftSelectArgs a) {
 // The arithmetic of every value that decides a draw is that of
 // draft_select_kernel.
 template <typename TL, typename TF>
-__global__ __launch_bounds__(256) void draft_select_fast(DraftSelectArgs a) {
+__device__ __forceinline__ void draft_select_block(const DraftSelectArgs& a, int b) {
   constexpr int kMaxTiles = kTilesPerBlock * 64;
   __shared__ double s_d[kMaxTiles];     // ref + mx of every tile
   __shared__ float s_sum[kMaxTiles];    // exp-sum of every tile
@@ -796,7 +797,7 @@ __global__ __launch_bounds__(256) void draft_select_fast(DraftSelectArgs a) {
   __shared__ float s_be[64];
   __shared__ double s_val[4], s_lse;
   __shared__ int s_idx[4], s_tile;
-  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int V = a.V, r = a.r, gamma = a.gamma, nt = a.n_tiles, pos = a.pos;
   const int nblk = (nt + kTilesPerBlock - 1) / kTilesPerBlock;
   const TileStat* ts = a.tstat + (size_t)b * nt;
@@ -932,6 +933,26 @@ __global__ __launch_bounds__(256) void draft_select_fast(DraftSelectArgs a) {
       for (int i = lane; i * 8 < r; i += 64) dst[i] = src[i];
     }
   }
+}
+
+template <typename TL, typename TF>
+__global__ __launch_bounds__(256) void draft_select_fast(DraftSelectArgs a) {
+  draft_select_block<TL, TF>(a, blockIdx.x);
+}
+
+// The last draw of a round and the scheduler (independent of each other, both
+// bound by memory latency) in one launch: workgroups 0..B-1 draw, the rest are
+// the scheduler's workgroups.
+struct SelectScheduleArgs {
+  DraftSelectArgs d;
+  ScheduleArgs s;
+};
+
+template <typename TL, typename TF>
+__global__ __launch_bounds__(256) void draft_select_schedule(SelectScheduleArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  if ((int)blockIdx.x < a.d.B) draft_select_block<TL, TF>(a.d, blockIdx.x);
+  else schedule_block(a.s, (int)blockIdx.x - a.d.B, (int)gridDim.x - a.d.B, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -1796,6 +1817,30 @@ hipError_t launch_gemm_stats(const GemmArgs& a, int logits_dtype, int factor_dty
                     : gemm_dispatch<uint16_t, false>(a, factor_dtype, vec, s, parts);
   return residual ? gemm_dispatch<float, true>(a, factor_dtype, vec, s, parts)
                   : gemm_dispatch<float, false>(a, factor_dtype, vec, s, parts);
+}
+
+template <typename TL, typename TF>
+hipError_t launch_select_schedule_t(const DraftSelectArgs& d, const ScheduleArgs& sa, hipStream_t stream) {
+  const void* fn = reinterpret_cast<const void*>(&draft_select_schedule<TL, TF>);
+  static bool attr = false;
+  if (!attr) {  // the scheduler's dynamic LDS reaches 80 KB at B gamma = 8192 with a 1024-point table
+    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 8192 * 8 + 1024 * 16) != hipSuccess)
+      return hipErrorUnknown;
+    attr = true;
+  }
+  const SelectScheduleArgs a{d, sa};
+  launch(&draft_select_schedule<TL, TF>, dim3(d.B + schedule_groups(sa)), 256, schedule_lds_bytes(sa), stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_draft_select_schedule(const DraftSelectArgs& d, const ScheduleArgs& sa, int logits_dtype,
+                                        int factor_dtype, hipStream_t stream) {
+  if (d.n_tiles > kTilesPerBlock * 64) return hipErrorNotSupported;
+  if (logits_dtype == DSPARK_BF16)
+    return factor_dtype == DSPARK_BF16 ? launch_select_schedule_t<uint16_t, uint16_t>(d, sa, stream)
+                                       : launch_select_schedule_t<uint16_t, float>(d, sa, stream);
+  return factor_dtype == DSPARK_BF16 ? launch_select_schedule_t<float, uint16_t>(d, sa, stream)
+                                     : launch_select_schedule_t<float, float>(d, sa, stream);
 }
 
 hipError_t launch_draft_select(const DraftSelectArgs& a, int logits_dtype, int factor_dtype,

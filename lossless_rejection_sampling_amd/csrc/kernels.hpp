@@ -170,5 +170,13 @@ struct ScheduleArgs {
 };
 
 hipError_t launch_schedule(const ScheduleArgs& a, hipStream_t s);
+int schedule_groups(const ScheduleArgs& a);        // workgroups of one scheduler launch
+size_t schedule_lds_bytes(const ScheduleArgs& a);  // its dynamic LDS
+
+// The draw of position d.pos and the scheduler in one launch (B + schedule_groups
+// workgroups).  Returns hipErrorNotSupported, having enqueued nothing, when the
+// draw needs the general kernel (more than 4096 tiles).
+hipError_t launch_draft_select_schedule(const DraftSelectArgs& d, const ScheduleArgs& s, int logits_dtype,
+                                        int factor_dtype, hipStream_t stream);
 
 }  // namespace dspark

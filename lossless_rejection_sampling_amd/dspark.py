@@ -43,6 +43,8 @@ _SIG = {
     "dspark_schedule_workspace_bytes": (ctypes.c_size_t, [_I, _I]),
     "dspark_draft_round": (_I, [_P, _I, _P, _P, _I, _P, _P, ctypes.c_uint64, _P,
                                 _I, _I, _I, _I, _P, _P, _P, _P, _P]),
+    "dspark_draft_schedule": (_I, [_P, _I, _P, _P, _I, _P, _P, ctypes.c_uint64, _P, _I, _I, _I, _I, _P, _P, _P,
+                                   _P, _P, _P, _P, _I, _I, ctypes.c_double, _P, _P, _P]),
     "dspark_schedule": (_I, [_P, _P, _P, _I, _I, _I, _P, _P, _P]),
     "dspark_schedule_ex": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_double, _P, _P, _P]),
     "dspark_verify": (_I, [_P, _P, _I, _P, _P, _I, _P, _P, _P, _P, _P, _P, ctypes.c_uint64, _P,
@@ -143,6 +145,31 @@ def dspark_draft_round(base_logits, U, W, prev0, temperature, seed, pos_offset,
         _dev(draft_logq, "draft_logq", torch.float32), _dev(draft_lse, "draft_lse", torch.float64),
         _dev(workspace, "workspace", torch.uint8), _stream(stream))
     _check("dspark_draft_round", rc)
+
+
+def dspark_draft_schedule(base_logits, U, W, prev0, temperature, seed, pos_offset, draft_tokens, draft_logq,
+                          draft_lse, conf, tau, sps_B, sps_val, rule, param, budget, workspace, stream=None):
+    """dspark_draft_round then dspark_schedule_ex in one call (the scheduler runs
+    in the launch of the last draw)."""
+    B, gamma, V = base_logits.shape
+    r = U.shape[1]
+    if tuple(U.shape) != (V, r) or tuple(W.shape) != (V, r) or U.dtype != W.dtype:
+        raise ValueError("U and W must both be [V, r] of one dtype")
+    if tuple(conf.shape) != (B, gamma):
+        raise ValueError("conf must be [B, gamma]")
+    code = SCHED_RULES[rule] if isinstance(rule, str) else int(rule)
+    n = int(sps_B.numel()) if sps_B is not None else 0
+    rc = lib().dspark_draft_schedule(
+        _dev(base_logits, "base_logits"), _dtype_code(base_logits), _dev(U, "U"), _dev(W, "W"),
+        _dtype_code(U), _dev(prev0, "prev0", torch.int32), _dev(temperature, "temperature", torch.float32),
+        int(seed) & (2 ** 64 - 1), _dev(pos_offset, "pos_offset", torch.int32, optional=True),
+        B, gamma, V, r, _dev(draft_tokens, "draft_tokens", torch.int32),
+        _dev(draft_logq, "draft_logq", torch.float32), _dev(draft_lse, "draft_lse", torch.float64),
+        _dev(conf, "conf", torch.float32), _dev(tau, "tau", torch.float32, optional=True),
+        _dev(sps_B, "sps_B", torch.float64, optional=True), _dev(sps_val, "sps_val", torch.float64, optional=True),
+        n, code, float(param), _dev(budget, "budget", torch.int32),
+        _dev(workspace, "workspace", torch.uint8), _stream(stream))
+    _check("dspark_draft_schedule", rc)
 
 
 def dspark_schedule(conf, sps_B, sps_val, budget, workspace, stream=None):

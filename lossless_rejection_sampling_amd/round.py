@@ -60,6 +60,13 @@ def draft(rnd: Round, buf: Buffers, stream=None):
                           buf.draft_tokens, buf.draft_logq, buf.draft_lse, buf.workspace, stream)
 
 
+def draft_schedule(rnd: Round, buf: Buffers, stream=None):
+    """The draft round and the scheduler in one call (scheduled rounds)."""
+    ds.dspark_draft_schedule(rnd.base, rnd.U, rnd.Wt, rnd.prev0, rnd.temperature, rnd.seed, rnd.pos_offset,
+                             buf.draft_tokens, buf.draft_logq, buf.draft_lse, rnd.conf, None, buf.sps_B,
+                             buf.sps_val, "early_stop", 0.0, buf.budget, buf.workspace, stream)
+
+
 def schedule(rnd: Round, buf: Buffers, stream=None):
     if rnd.scheduled:
         ds.dspark_schedule(rnd.conf, buf.sps_B, buf.sps_val, buf.budget, buf.workspace, stream)
@@ -72,10 +79,12 @@ def verify(rnd: Round, buf: Buffers, stream=None):
                      buf.debug_logp_logq, buf.debug_residual, stream)
 
 
-def run_round(rnd: Round, buf: Buffers, stream=None, side_stream=None):
-    """One round on ``stream`` (default: the current stream).  With a
-    ``side_stream`` the scheduler, which reads only the confidence scores, runs
-    there concurrently with drafting, and verification waits for it."""
+def run_round(rnd: Round, buf: Buffers, stream=None, side_stream=None, combined=True):
+    """One round on ``stream`` (default: the current stream).  A scheduled round
+    drafts and schedules in one call (``combined``: the scheduler runs in the
+    launch of the last draw), or in two calls; with a ``side_stream`` the
+    scheduler, which reads only the confidence scores, runs there concurrently
+    with drafting instead, and verification waits for it."""
     main = torch.cuda.current_stream() if stream is None else stream
     if side_stream is not None and rnd.scheduled:
         side_stream.wait_stream(main)
@@ -84,6 +93,8 @@ def run_round(rnd: Round, buf: Buffers, stream=None, side_stream=None):
         done.record(side_stream)
         draft(rnd, buf, main)
         main.wait_event(done)
+    elif combined and rnd.scheduled:
+        draft_schedule(rnd, buf, main)
     else:
         draft(rnd, buf, main)
         schedule(rnd, buf, main)

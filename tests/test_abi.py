@@ -25,7 +25,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_error_strings(lib):
-    assert ds.dspark_abi_version() == 3
+    assert ds.dspark_abi_version() == 4
     assert ds.error_string(0) == "ok"
     assert "argument" in ds.error_string(-1)
     assert "device" in ds.error_string(-3)
@@ -78,5 +78,13 @@ def test_host_argument_checks_return_einval(lib):
     assert ex(fake, nul, fake, fake, 16, 4, 4, 9, 0.0, fake, fake, nul) == ds.DSPARK_EINVAL
     assert ex(fake, nul, nul, nul, 0, 4, 4, 2, float("nan"), fake, fake, nul) == ds.DSPARK_EINVAL
     assert ex(fake, nul, nul, nul, 0, 4, 4, 1, 0.0, fake, fake, nul) == ds.DSPARK_EINVAL
+    # draft + schedule in one call: the checks of both calls, before anything is enqueued
+    dsch = lib.dspark_draft_schedule
+    assert dsch(fake, 0, fake, fake, 0, fake, fake, 1, nul, 4, 5, 100, 16, fake, fake, fake,
+                fake, nul, fake, fake, 16, 9, 0.0, fake, fake, nul) == ds.DSPARK_EINVAL      # unknown rule
+    assert dsch(fake, 0, fake, fake, 0, fake, fake, 1, nul, 4, 5, 100, 16, fake, fake, fake,
+                nul, nul, fake, fake, 16, 0, 0.0, fake, fake, nul) == ds.DSPARK_EINVAL       # no scores
+    assert dsch(fake, 7, fake, fake, 0, fake, fake, 1, nul, 4, 5, 100, 16, fake, fake, fake,
+                fake, nul, fake, fake, 16, 0, 0.0, fake, fake, nul) == ds.DSPARK_EINVAL      # unknown dtype
     assert lib.dspark_status(nul, nul) == ds.DSPARK_EINVAL
     assert lib.dspark_profile_enable(99, 1) == ds.DSPARK_EINVAL

@@ -110,6 +110,33 @@ def test_rounds_reuse_one_workspace():
     check(compare(rnd, buf, run_oracle(rnd, idx), idx), "reused_workspace")
 
 
+@pytest.mark.parametrize("case", [
+    # the scheduler in the launch of the last draw
+    dict(B=64, gamma=5, V=20000, r=256, dtype=torch.bfloat16, temps=(1.0, 0.0)),
+    dict(B=300, gamma=4, V=5000, r=128, dtype=torch.bfloat16, temps=(0.8,)),
+    # rows of more than 4096 tiles: the general draw kernel, the scheduler after it
+    dict(B=6, gamma=3, V=270000, r=64, dtype=torch.float32, temps=(1.0, 0.0)),
+])
+def test_draft_schedule_matches_two_calls(case):
+    rnd = wl.small_random(case["B"], case["gamma"], case["V"], case["r"], device=DEV, seed=case["V"] % 97,
+                          dtype=case["dtype"], factor_dtype=torch.bfloat16, temps=case["temps"])
+    g = torch.Generator(device=DEV).manual_seed(case["B"])
+    rnd.conf = wl.confidence_scores(rnd.B, rnd.gamma, g, DEV)
+    rnd.sps_B, rnd.sps_val = wl.sps_table_linear()
+    say(f"[draft_schedule] B={rnd.B} gamma={rnd.gamma} V={rnd.V} r={rnd.r}")
+    bufs = []
+    for combined in (False, True):
+        buf = rd.allocate(rnd, debug=True)
+        rd.run_round(rnd, buf, combined=combined)
+        torch.cuda.synchronize()
+        assert ds.dspark_status(buf.workspace) == ds.DSPARK_OK
+        bufs.append(buf)
+    for name in ("draft_tokens", "draft_logq", "draft_lse", "budget", "out_tokens", "num_accepted", "num_emitted"):
+        assert torch.equal(getattr(bufs[0], name), getattr(bufs[1], name)), name
+    idx = np.arange(min(rnd.B, 24))
+    check(compare(rnd, bufs[1], run_oracle(rnd, idx), idx), "draft_schedule")
+
+
 def test_bad_data_is_reported_not_faulted():
     rnd = wl.small_random(8, 3, 500, 16, device=DEV, seed=1)
     rnd.prev0 = rnd.prev0.clone()
