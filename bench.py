@@ -292,7 +292,8 @@ def measure_peaks(reps=3):
     flops = blocks * 4 * iters * 4 * 32768
     torch.cuda.empty_cache()
     return {"stream_read_GB_s": (2 << 30) / t_read / 1e9, "mfma_bf16_TFLOP_s": flops / t_mfma / 1e12,
-            "how": "streaming read of 2 GiB (8192 WGs x 256 lanes, 8 x 16-byte loads in flight per lane); "
+            "how": "streaming read of 2 GiB (one contiguous 8 KB chunk per wavefront, 8 x 16-byte "
+                   "non-temporal loads in flight per lane); "
                    "1024 WGs x 4 waves x 4096 rounds of 4 independent v_mfma_f32_32x32x16_bf16 chains"}
 
 

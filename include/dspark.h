@@ -297,8 +297,8 @@ int dspark_profile_read(int kernel_class, int* launches, double* total_ms);
  * device uint32 that is written only in a case that does not occur (it keeps
  * the work from being optimised away).
  *   dspark_peak_stream_read: reads the `bytes` (a positive multiple of 16)
- *     of the device buffer `buf` once, 8192 workgroups of 256 lanes striding
- *     over it with 8 loads of 16 bytes in flight per lane.
+ *     of the device buffer `buf` once: every wavefront one contiguous 8 KB
+ *     chunk, its eight 16-byte streaming loads per lane all in flight.
  *   dspark_peak_mfma_bf16: `blocks` workgroups of 4 wavefronts, each running
  *     `iters` rounds of 4 independent v_mfma_f32_32x32x16_bf16 chains:
  *     blocks * 4 * iters * 4 * 32768 flops.
