@@ -1254,8 +1254,10 @@ hipError_t launch_draft_stream(const GemmArgs& a, hipStream_t s) {
       return hipErrorUnknown;
     if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
       return hipErrorUnknown;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 512, lds) != hipSuccess || per_cu < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 512, lds) != hipSuccess || per_cu < 1) {
       per_cu = 1;
+      (void)hipGetLastError();  // handled here: not to be reported with the launch below
+    }
     max_wg = cus * per_cu;
   }
   const int groups = (a.B + kSlotsPerGroup - 1) / kSlotsPerGroup;
@@ -1710,8 +1712,10 @@ hipError_t launch_residual_stream(const GemmArgs& a, hipStream_t s, int* parts) 
       return hipErrorUnknown;
     if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
       return hipErrorUnknown;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 512, lds) != hipSuccess || per_cu < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 512, lds) != hipSuccess || per_cu < 1) {
       per_cu = 1;
+      (void)hipGetLastError();  // handled here: not to be reported with the launch below
+    }
     mw = cus * per_cu;
   }
   // the residual draw may need every request; the acceptance pass has B gamma slots
@@ -1735,8 +1739,10 @@ hipError_t launch_residual_coalesced(const GemmArgs& a, hipStream_t s) {
       return hipErrorUnknown;
     if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
       return hipErrorUnknown;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 512, lds) != hipSuccess || per_cu < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 512, lds) != hipSuccess || per_cu < 1) {
       per_cu = 1;
+      (void)hipGetLastError();  // handled here: not to be reported with the launch below
+    }
     max_wg = cus * per_cu;
   }
   // enough workgroups to give every CU one, and at least one per tile of every
@@ -1759,8 +1765,10 @@ hipError_t launch_pipelined(const GemmArgs& a, hipStream_t s) {
       return hipErrorUnknown;
     if (lds > 64 * 1024 && hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
       return hipErrorUnknown;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64 * kLdsWaves, lds) != hipSuccess || per_cu < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64 * kLdsWaves, lds) != hipSuccess || per_cu < 1) {
       per_cu = 1;
+      (void)hipGetLastError();  // handled here: not to be reported with the launch below
+    }
     max_wg = cus * per_cu;
   }
   const int groups = (max_slots(a, RESIDUAL) + kSlotsPerGroup - 1) / kSlotsPerGroup;
