@@ -56,6 +56,8 @@ def test_tiny_round():
     # more tiles than workgroups: a partial last round of tiles
     dict(B=24, gamma=4, V=20000, r=256, dtype=torch.bfloat16, fdt=torch.bfloat16, temps=(1.0, 0.0, 0.8)),
     dict(B=40, gamma=3, V=24000, r=128, dtype=torch.bfloat16, fdt=torch.bfloat16, temps=(1.3, 0.0)),
+    # more than 4096 tiles (the general draw) over bf16 streams: 4219 tiles, 123 in a partial last round
+    dict(B=4, gamma=2, V=270000, r=128, dtype=torch.bfloat16, fdt=torch.bfloat16, temps=(1.0, 0.0)),
 ])
 def test_small_rounds(case):
     rnd = wl.small_random(case["B"], case["gamma"], case["V"], case["r"], device=DEV, seed=case["B"] + case["V"],
