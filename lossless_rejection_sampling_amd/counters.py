@@ -85,6 +85,11 @@ def calibration(path: str, counter: str) -> float:
     return COPY_BYTES / vals[len(vals) // 2]
 
 
+def _run_dir(csv_path: str) -> str:
+    """The rocprofv3 output directory (-d) of a counter CSV at <dir>/run_counter_collection.csv."""
+    return os.path.dirname(csv_path) or "."
+
+
 def report(bench_fetch, bench_write, copy_fetch, copy_write, kernel, cls, command_note=""):
     """Markdown summary with the machine-readable `traffic:` line bench.py reads."""
     f = summarize(bench_fetch, kernel, "FETCH_SIZE")
@@ -99,17 +104,16 @@ def report(bench_fetch, bench_write, copy_fetch, copy_write, kernel, cls, comman
         "(run from /tmp with TMPDIR=/tmp, repository at /root/repo):",
         "",
         "```",
-        "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc/bench_fetch -o run --output-format csv -- "
+        f"rocprofv3 --pmc FETCH_SIZE -d {_run_dir(bench_fetch)} -o run --output-format csv -- "
         "python3 /root/repo/bench.py --steps 2 --warmup 1 --no-cpu-baseline",
-        "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc/bench_write -o run --output-format csv -- "
+        f"rocprofv3 --pmc WRITE_SIZE -d {_run_dir(bench_write)} -o run --output-format csv -- "
         "python3 /root/repo/bench.py --steps 2 --warmup 1 --no-cpu-baseline",
-        "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc/copy_fetch -o run --output-format csv -- "
+        f"rocprofv3 --pmc FETCH_SIZE -d {_run_dir(copy_fetch)} -o run --output-format csv -- "
         "python3 /root/repo/bench.py --calibrate-copy",
-        "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc/copy_write -o run --output-format csv -- "
+        f"rocprofv3 --pmc WRITE_SIZE -d {_run_dir(copy_write)} -o run --output-format csv -- "
         "python3 /root/repo/bench.py --calibrate-copy",
-        "python3 -m lossless_rejection_sampling_amd.counters report gpurun_out/pmc/bench_fetch/run_counter_collection.csv "
-        "gpurun_out/pmc/bench_write/run_counter_collection.csv gpurun_out/pmc/copy_fetch/run_counter_collection.csv "
-        f"gpurun_out/pmc/copy_write/run_counter_collection.csv {kernel} {cls}",
+        f"python3 -m lossless_rejection_sampling_amd.counters report {bench_fetch} {bench_write} {copy_fetch} "
+        f"{copy_write} {kernel} {cls}",
         "```",
         "",
         f"Calibration: a {COPY_BYTES >> 20} MiB ({COPY_BYTES >> 10} KiB) device copy (`{COPY_KERNEL}`, median of "
@@ -203,10 +207,9 @@ def mfma_report(path: str, kernel: str, cls: str, flops_per_launch: float) -> st
         "One `rocprofv3 --pmc` run (run from /tmp with TMPDIR=/tmp, repository at /root/repo):",
         "",
         "```",
-        f"rocprofv3 --pmc {' '.join(MFMA_COUNTERS)} -d gpurun_out/pmc/bench_mfma -o run --output-format csv -- "
+        f"rocprofv3 --pmc {' '.join(MFMA_COUNTERS)} -d {_run_dir(path)} -o run --output-format csv -- "
         "python3 /root/repo/bench.py --steps 2 --warmup 1 --no-cpu-baseline",
-        "python3 -m lossless_rejection_sampling_amd.counters mfma gpurun_out/pmc/bench_mfma/run_counter_collection.csv "
-        f"{kernel} {cls} {flops_per_launch:.0f}",
+        f"python3 -m lossless_rejection_sampling_amd.counters mfma {path} {kernel} {cls} {flops_per_launch:.0f}",
         "```",
         "",
         "| quantity | per launch (mean of %d dispatches) |" % len(rows),
