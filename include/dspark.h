@@ -44,9 +44,13 @@
  *     argument errors return DSPARK_EINVAL before anything is enqueued; a failed
  *     launch returns DSPARK_EHIP.  Data errors found on the device (a token id
  *     outside [0, V), a budget outside [0, gamma], a negative or NaN
- *     temperature, a confidence outside (0, 1)) set a bit in the workspace's
- *     status word; the offending value is clamped so that every kernel stays in
- *     bounds, and dspark_status() reports DSPARK_EDATA.
+ *     temperature, a confidence outside (0, 1), a step-rate table whose batch
+ *     sizes are not strictly increasing or whose rates are not positive and
+ *     finite) set a bit in the workspace's status word; the offending value is
+ *     clamped so that every kernel stays in bounds (with a bad table the budgets
+ *     are unspecified), and dspark_status() reports DSPARK_EDATA.  Arguments that
+ *     live in device memory (the table included) are checked there, not on the
+ *     host, so that no call synchronises.
  *   - Sizes: B >= 1, 1 <= gamma <= 16, V >= 1, r >= 1.
  *   - Randomness: Philox4x32-10 (Salmon et al., SC'11) keyed by `seed`, with
  *     counter (draw index / 4, block position + pos_offset[b], request b,
@@ -62,7 +66,7 @@
 extern "C" {
 #endif
 
-#define DSPARK_ABI_VERSION 4
+#define DSPARK_ABI_VERSION 5
 
 enum dspark_status_code {
   DSPARK_OK = 0,
@@ -74,6 +78,17 @@ enum dspark_status_code {
 enum dspark_dtype {
   DSPARK_BF16 = 0, /* bfloat16 */
   DSPARK_F32 = 1   /* IEEE float32 */
+};
+
+/* Layout of the Markov head's second factor W2, an r x V matrix on the pages
+ * ([P1]: B = W1 W2).  Every call that reads W2 takes the layout explicitly. */
+enum dspark_w_layout {
+  DSPARK_W_VOCAB_MAJOR = 0, /* [V, r] row-major: row v holds column v of W2, the
+                               r values one vocabulary column contracts over
+                               contiguous.  The only layout the round reads. */
+  DSPARK_W_RANK_MAJOR = 1   /* [r, V] row-major: W2 as the pages print it.  Not
+                               read by the round (DSPARK_EINVAL): pack it once
+                               with dspark_pack_w2. */
 };
 
 /* Verify-budget rules of dspark_schedule_ex. */
@@ -100,6 +115,21 @@ size_t dspark_workspace_bytes(int B, int gamma, int V, int r);
 size_t dspark_schedule_workspace_bytes(int B, int gamma);
 
 /*
+ * dspark_pack_w2 -- the Markov head's second factor ([P1], section "Un po' di
+ * autoregressione basta": B = W1 W2 with W2 of r rows by V columns) from the
+ * pages' [r, V] layout into the vocabulary-major [V, r] layout the round reads
+ * (DSPARK_W_VOCAB_MAJOR): W_packed[v, rho] = W[rho, v].  W2 is a static weight,
+ * so a caller holding it as [r, V] packs it once and passes W_packed to every
+ * round.
+ *
+ *   W         [r, V] factor_dtype   device, read only
+ *   W_packed  [V, r] factor_dtype   device, written; must not overlap W
+ * Errors: DSPARK_EINVAL for a NULL pointer, V or r < 1, or an unknown dtype;
+ * DSPARK_EHIP for a failed launch.  Only enqueues work on `stream`.
+ */
+int dspark_pack_w2(const void* W, int factor_dtype, int V, int r, void* W_packed, void* stream);
+
+/*
  * dspark_draft_round -- [P1] eq. p_k with the Markov head.
  *
  * For k = 1..gamma, for every request b:
@@ -113,6 +143,8 @@ size_t dspark_schedule_workspace_bytes(int B, int gamma);
  *   W            [V, r]         factor_dtype   second factor W2 of [P1] stored
  *                                              vocabulary-major: row v holds
  *                                              column v of W2 (W2 = W^T)
+ *   w_layout     DSPARK_W_VOCAB_MAJOR (anything else: DSPARK_EINVAL, nothing
+ *                enqueued; a [r, V] W2 is packed with dspark_pack_w2)
  *   prev0        [B] int32      last committed token of each request
  *   temperature  [B] float32    >= 0; 0 = greedy
  *   seed                        Philox key
@@ -126,7 +158,7 @@ size_t dspark_schedule_workspace_bytes(int B, int gamma);
  *                                   that dspark_verify can rebuild q_k exactly
  */
 int dspark_draft_round(const void* base_logits, int logits_dtype,
-                       const void* U, const void* W, int factor_dtype,
+                       const void* U, const void* W, int factor_dtype, int w_layout,
                        const int32_t* prev0, const float* temperature,
                        uint64_t seed, const int32_t* pos_offset,
                        int B, int gamma, int V, int r,
@@ -148,7 +180,8 @@ int dspark_draft_round(const void* base_logits, int logits_dtype,
  *
  *   conf     [B, gamma] float32  confidence scores, each in (0, 1)
  *   sps_B    [n_points] float64  batch sizes in tokens, strictly increasing
- *   sps_val  [n_points] float64  steps per second at those sizes, > 0
+ *   sps_val  [n_points] float64  steps per second at those sizes, > 0 and finite
+ *            (a table that breaks either rule is reported as a data error)
  *   budget   [B] int32 out       verify budgets in [0, gamma]
  * Limits: n_points in [2, 1024], B * gamma <= 8192.  The position of each
  * candidate in the order above is computed directly (the number of candidates
@@ -199,7 +232,7 @@ int dspark_schedule_ex(const float* conf, const float* tau, const double* sps_B,
  * Workspace: dspark_workspace_bytes(B, gamma, V, r).
  */
 int dspark_draft_schedule(const void* base_logits, int logits_dtype, const void* U, const void* W,
-                          int factor_dtype, const int32_t* prev0, const float* temperature, uint64_t seed,
+                          int factor_dtype, int w_layout, const int32_t* prev0, const float* temperature, uint64_t seed,
                           const int32_t* pos_offset, int B, int gamma, int V, int r, int32_t* draft_tokens,
                           float* draft_logq, double* draft_lse, const float* conf, const float* tau,
                           const double* sps_B, const double* sps_val, int n_points, int rule, double param,
@@ -220,8 +253,8 @@ int dspark_draft_schedule(const void* base_logits, int logits_dtype, const void*
  * target argmax.
  *
  *   target_logits [B, gamma+1, V] logits_dtype
- *   base_logits, U, W, prev0, temperature, seed, pos_offset: as given to
- *                 dspark_draft_round for the same round
+ *   base_logits, U, W, w_layout, prev0, temperature, seed, pos_offset: as
+ *                 given to dspark_draft_round for the same round
  *   draft_tokens, draft_logq, draft_lse: its outputs
  *   budget       [B] int32 or NULL
  * Outputs:
@@ -234,7 +267,7 @@ int dspark_draft_schedule(const void* base_logits, int logits_dtype, const void*
  *                 requests that rejected (untouched elsewhere)
  */
 int dspark_verify(const void* target_logits, const void* base_logits, int logits_dtype,
-                  const void* U, const void* W, int factor_dtype,
+                  const void* U, const void* W, int factor_dtype, int w_layout,
                   const int32_t* prev0, const int32_t* draft_tokens,
                   const float* draft_logq, const double* draft_lse,
                   const int32_t* budget, const float* temperature,
@@ -258,8 +291,8 @@ int dspark_verify(const void* target_logits, const void* base_logits, int logits
  * passes given that x_1..x_{k-1} were accepted.  Greedy requests (T_b = 0):
  * 1 if draft_tokens[b, k-1] is the target row's lowest-index maximum, else 0.
  *
- *   target_logits [B, gamma+1, V], base_logits [B, gamma, V], U, W, prev0,
- *   temperature: as for dspark_verify; draft_tokens, draft_lse: the outputs of
+ *   target_logits [B, gamma+1, V], base_logits [B, gamma, V], U, W, w_layout,
+ *   prev0, temperature: as for dspark_verify; draft_tokens, draft_lse: the outputs of
  *   dspark_draft_round for the same inputs.
  *   c_star        [B, gamma] float64 out.
  * Reads every target and backbone row once plus W2 per group of 128 positions;
@@ -267,7 +300,7 @@ int dspark_verify(const void* target_logits, const void* base_logits, int logits
  * calls (ordered on one stream: it empties the residual work list).
  */
 int dspark_acceptance(const void* target_logits, const void* base_logits, int logits_dtype,
-                      const void* U, const void* W, int factor_dtype,
+                      const void* U, const void* W, int factor_dtype, int w_layout,
                       const int32_t* prev0, const int32_t* draft_tokens, const double* draft_lse,
                       const float* temperature, int B, int gamma, int V, int r,
                       double* c_star, void* workspace, void* stream);

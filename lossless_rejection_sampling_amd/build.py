@@ -14,7 +14,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT_DIR = os.path.join(PKG, "_lib")
 LIB_PATH = os.path.join(OUT_DIR, "libdspark.so")
-SOURCES = ["api.hip", "draft.hip", "verify.hip", "schedule.hip", "peaks.hip"]
+SOURCES = ["api.hip", "draft.hip", "verify.hip", "schedule.hip", "pack.hip", "peaks.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -3,6 +3,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <map>
 #include <mutex>
 #include <vector>
 
@@ -97,7 +98,49 @@ ProfState& prof() {
 
 namespace {
 thread_local KernelEvents* t_events = nullptr;
+
+struct SetupKey {
+  const void* fn;
+  int dev, threads;
+  size_t lds;
+  bool operator<(const SetupKey& o) const {
+    if (fn != o.fn) return fn < o.fn;
+    if (dev != o.dev) return dev < o.dev;
+    if (threads != o.threads) return threads < o.threads;
+    return lds < o.lds;
+  }
+};
+}  // namespace
+
+hipError_t kernel_setup(const void* fn, int threads, size_t lds, int* groups) {
+  static std::mutex mu;
+  static std::map<SetupKey, int> done;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const SetupKey key{fn, dev, threads, lds};
+  std::lock_guard<std::mutex> g(mu);
+  auto it = done.find(key);
+  if (it != done.end()) {
+    *groups = it->second;
+    return hipSuccess;
+  }
+  int cus = 0, per_cu = 0;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  if (lds > 64 * 1024) {
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, lds) != hipSuccess || per_cu < 1) {
+    per_cu = 1;
+    (void)hipGetLastError();  // handled here: not to be reported with a later launch
+  }
+  *groups = cus * per_cu;
+  done.emplace(key, *groups);
+  return hipSuccess;
 }
+
 
 KernelEvents* kernel_events() { return t_events; }
 
@@ -167,9 +210,10 @@ int schedule_args(const float* conf, const float* tau, const double* sps_B, cons
 }
 
 int draft_args_ok(const void* base_logits, int logits_dtype, const void* U, const void* W, int factor_dtype,
-                  const int32_t* prev0, const float* temperature, int B, int gamma, int V, int r,
+                  int w_layout, const int32_t* prev0, const float* temperature, int B, int gamma, int V, int r,
                   int32_t* draft_tokens, float* draft_logq, double* draft_lse, void* workspace) {
   if (!sizes_ok(B, gamma, V, r) || !dtype_ok(logits_dtype) || !dtype_ok(factor_dtype)) return DSPARK_EINVAL;
+  if (w_layout != DSPARK_W_VOCAB_MAJOR) return DSPARK_EINVAL;
   if (!base_logits || !U || !W || !prev0 || !temperature || !draft_tokens || !draft_logq || !draft_lse ||
       !workspace)
     return DSPARK_EINVAL;
@@ -257,12 +301,19 @@ size_t dspark_schedule_workspace_bytes(int B, int gamma) {
          align_up(((size_t)B * gamma + 1) * sizeof(double));
 }
 
+int dspark_pack_w2(const void* W, int factor_dtype, int V, int r, void* W_packed, void* stream) {
+  if (!W || !W_packed || V < 1 || r < 1 || !dtype_ok(factor_dtype)) return DSPARK_EINVAL;
+  const int es = factor_dtype == DSPARK_BF16 ? 2 : 4;
+  DSPARK_TRY(launch_pack_w2(W, W_packed, es, V, r, static_cast<hipStream_t>(stream)));
+  return DSPARK_OK;
+}
+
 int dspark_draft_round(const void* base_logits, int logits_dtype, const void* U, const void* W,
-                       int factor_dtype, const int32_t* prev0, const float* temperature,
+                       int factor_dtype, int w_layout, const int32_t* prev0, const float* temperature,
                        uint64_t seed, const int32_t* pos_offset, int B, int gamma, int V, int r,
                        int32_t* draft_tokens, float* draft_logq, double* draft_lse, void* workspace,
                        void* stream) {
-  const int ok = draft_args_ok(base_logits, logits_dtype, U, W, factor_dtype, prev0, temperature, B, gamma, V, r,
+  const int ok = draft_args_ok(base_logits, logits_dtype, U, W, factor_dtype, w_layout, prev0, temperature, B, gamma, V, r,
                                draft_tokens, draft_logq, draft_lse, workspace);
   if (ok != DSPARK_OK) return ok;
   return draft_round(base_logits, logits_dtype, U, W, factor_dtype, prev0, temperature, seed, pos_offset, B, gamma,
@@ -271,7 +322,7 @@ int dspark_draft_round(const void* base_logits, int logits_dtype, const void* U,
 }
 
 int dspark_draft_schedule(const void* base_logits, int logits_dtype, const void* U, const void* W,
-                          int factor_dtype, const int32_t* prev0, const float* temperature, uint64_t seed,
+                          int factor_dtype, int w_layout, const int32_t* prev0, const float* temperature, uint64_t seed,
                           const int32_t* pos_offset, int B, int gamma, int V, int r, int32_t* draft_tokens,
                           float* draft_logq, double* draft_lse, const float* conf, const float* tau,
                           const double* sps_B, const double* sps_val, int n_points, int rule, double param,
@@ -279,7 +330,7 @@ int dspark_draft_schedule(const void* base_logits, int logits_dtype, const void*
   ScheduleArgs a;
   int ok = schedule_args(conf, tau, sps_B, sps_val, n_points, B, gamma, rule, param, budget, workspace, a);
   if (ok != DSPARK_OK) return ok;
-  ok = draft_args_ok(base_logits, logits_dtype, U, W, factor_dtype, prev0, temperature, B, gamma, V, r, draft_tokens,
+  ok = draft_args_ok(base_logits, logits_dtype, U, W, factor_dtype, w_layout, prev0, temperature, B, gamma, V, r, draft_tokens,
                      draft_logq, draft_lse, workspace);
   if (ok != DSPARK_OK) return ok;
   return draft_round(base_logits, logits_dtype, U, W, factor_dtype, prev0, temperature, seed, pos_offset, B, gamma,
@@ -305,12 +356,13 @@ int dspark_schedule(const float* conf, const double* sps_B, const double* sps_va
 }
 
 int dspark_verify(const void* target_logits, const void* base_logits, int logits_dtype, const void* U,
-                  const void* W, int factor_dtype, const int32_t* prev0, const int32_t* draft_tokens,
+                  const void* W, int factor_dtype, int w_layout, const int32_t* prev0, const int32_t* draft_tokens,
                   const float* draft_logq, const double* draft_lse, const int32_t* budget,
                   const float* temperature, uint64_t seed, const int32_t* pos_offset, int B, int gamma,
                   int V, int r, int32_t* out_tokens, int32_t* num_accepted, int32_t* num_emitted,
                   float* debug_logp_logq, float* debug_residual, void* workspace, void* stream) {
   if (!sizes_ok(B, gamma, V, r) || !dtype_ok(logits_dtype) || !dtype_ok(factor_dtype)) return DSPARK_EINVAL;
+  if (w_layout != DSPARK_W_VOCAB_MAJOR) return DSPARK_EINVAL;
   if (!target_logits || !base_logits || !U || !W || !prev0 || !draft_tokens || !draft_logq || !draft_lse ||
       !temperature || !out_tokens || !num_accepted || !num_emitted || !workspace)
     return DSPARK_EINVAL;
@@ -358,10 +410,11 @@ int dspark_verify(const void* target_logits, const void* base_logits, int logits
 }
 
 int dspark_acceptance(const void* target_logits, const void* base_logits, int logits_dtype, const void* U,
-                      const void* W, int factor_dtype, const int32_t* prev0, const int32_t* draft_tokens,
+                      const void* W, int factor_dtype, int w_layout, const int32_t* prev0, const int32_t* draft_tokens,
                       const double* draft_lse, const float* temperature, int B, int gamma, int V, int r,
                       double* c_star, void* workspace, void* stream) {
   if (!sizes_ok(B, gamma, V, r) || !dtype_ok(logits_dtype) || !dtype_ok(factor_dtype)) return DSPARK_EINVAL;
+  if (w_layout != DSPARK_W_VOCAB_MAJOR) return DSPARK_EINVAL;
   if (!target_logits || !base_logits || !U || !W || !prev0 || !draft_tokens || !draft_lse || !temperature ||
       !c_star || !workspace)
     return DSPARK_EINVAL;

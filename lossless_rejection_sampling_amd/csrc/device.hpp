@@ -22,7 +22,7 @@ enum : uint32_t {
 
 // Bits of the workspace status word.
 enum : uint32_t {
-  kBadPrev = 1u, kBadDraft = 2u, kBadBudget = 4u, kBadTemp = 8u, kBadConf = 16u,
+  kBadPrev = 1u, kBadDraft = 2u, kBadBudget = 4u, kBadTemp = 8u, kBadConf = 16u, kBadTable = 32u,
 };
 
 // Softmax statistics of one 64-column tile of one draft row:

@@ -1244,22 +1244,10 @@ __global__ __launch_bounds__(512, 1) void gemm_draft_stream(GemmArgs a) {
 
 template <int R>
 hipError_t launch_draft_stream(const GemmArgs& a, hipStream_t s) {
-  static int max_wg = 0;
   const size_t lds = (size_t)kStages * (WLayout<R, kStageCols>::BYTES + 8 * kXStageBytes);
-  const void* fn = reinterpret_cast<const void*>(&gemm_draft_stream<R>);
-  if (!max_wg) {
-    int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      return hipErrorUnknown;
-    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-      return hipErrorUnknown;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 512, lds) != hipSuccess || per_cu < 1) {
-      per_cu = 1;
-      (void)hipGetLastError();  // handled here: not to be reported with the launch below
-    }
-    max_wg = cus * per_cu;
-  }
+  int max_wg = 0;
+  const hipError_t e = kernel_setup(reinterpret_cast<const void*>(&gemm_draft_stream<R>), 512, lds, &max_wg);
+  if (e != hipSuccess) return e;
   const int groups = (a.B + kSlotsPerGroup - 1) / kSlotsPerGroup;
   const int wg_x = max(1, min(a.n_tiles, max_wg / groups));
   launch(&gemm_draft_stream<R>, dim3(wg_x, groups), 512, lds, s, a);
@@ -1700,24 +1688,12 @@ __global__ __launch_bounds__(512, 1) void gemm_residual_stream(GemmArgs a) {
 
 template <int R>
 hipError_t launch_residual_stream(const GemmArgs& a, hipStream_t s, int* parts) {
-  static int max_wg[2] = {0, 0};
   const size_t lds = (size_t)kRStages * (WLayout<R, kStageCols>::BYTES + 8 * 2 * kXStageBytes);
   const void* fn = a.tv ? reinterpret_cast<const void*>(&gemm_residual_stream<R, true>)
                        : reinterpret_cast<const void*>(&gemm_residual_stream<R, false>);
-  int& mw = max_wg[a.tv ? 1 : 0];
-  if (!mw) {
-    int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      return hipErrorUnknown;
-    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-      return hipErrorUnknown;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 512, lds) != hipSuccess || per_cu < 1) {
-      per_cu = 1;
-      (void)hipGetLastError();  // handled here: not to be reported with the launch below
-    }
-    mw = cus * per_cu;
-  }
+  int mw = 0;
+  const hipError_t e = kernel_setup(fn, 512, lds, &mw);
+  if (e != hipSuccess) return e;
   // the residual draw may need every request; the acceptance pass has B gamma slots
   const int groups = (max_slots(a, true) + kSlotsPerGroup - 1) / kSlotsPerGroup;
   const int wg_x = max(1, min(a.n_tiles, mw / groups));
@@ -1729,22 +1705,10 @@ hipError_t launch_residual_stream(const GemmArgs& a, hipStream_t s, int* parts) 
 
 template <int R>
 hipError_t launch_residual_coalesced(const GemmArgs& a, hipStream_t s) {
-  static int max_wg = 0;
   const size_t lds = (size_t)2 * (kTile * R * 2) + (size_t)4 * (kResSlots * kTile * 2);
-  const void* fn = reinterpret_cast<const void*>(&gemm_residual_coalesced<R>);
-  if (!max_wg) {
-    int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      return hipErrorUnknown;
-    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-      return hipErrorUnknown;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 512, lds) != hipSuccess || per_cu < 1) {
-      per_cu = 1;
-      (void)hipGetLastError();  // handled here: not to be reported with the launch below
-    }
-    max_wg = cus * per_cu;
-  }
+  int max_wg = 0;
+  const hipError_t e = kernel_setup(reinterpret_cast<const void*>(&gemm_residual_coalesced<R>), 512, lds, &max_wg);
+  if (e != hipSuccess) return e;
   // enough workgroups to give every CU one, and at least one per tile of every
   // possible slot group when the batch is small
   const int groups = (max_slots(a, true) + kResSlots - 1) / kResSlots;
@@ -1755,22 +1719,11 @@ hipError_t launch_residual_coalesced(const GemmArgs& a, hipStream_t s) {
 
 template <typename TL, bool RESIDUAL, int R>
 hipError_t launch_pipelined(const GemmArgs& a, hipStream_t s) {
-  static int max_wg = 0;
   const size_t lds = (size_t)kRing * (2 * (R / 16) * 1024);
-  const void* fn = reinterpret_cast<const void*>(&gemm_stats_lds<TL, RESIDUAL, R>);
-  if (!max_wg) {
-    int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      return hipErrorUnknown;
-    if (lds > 64 * 1024 && hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-      return hipErrorUnknown;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64 * kLdsWaves, lds) != hipSuccess || per_cu < 1) {
-      per_cu = 1;
-      (void)hipGetLastError();  // handled here: not to be reported with the launch below
-    }
-    max_wg = cus * per_cu;
-  }
+  int max_wg = 0;
+  const hipError_t e =
+      kernel_setup(reinterpret_cast<const void*>(&gemm_stats_lds<TL, RESIDUAL, R>), 64 * kLdsWaves, lds, &max_wg);
+  if (e != hipSuccess) return e;
   const int groups = (max_slots(a, RESIDUAL) + kSlotsPerGroup - 1) / kSlotsPerGroup;
   const int threads = 64 * min(kLdsWaves, (max_slots(a, RESIDUAL) + 31) / 32);
   const int wg_x = max(1, min(a.n_tiles, max_wg / groups));
@@ -1829,13 +1782,11 @@ hipError_t launch_gemm_stats(const GemmArgs& a, int logits_dtype, int factor_dty
 
 template <typename TL, typename TF>
 hipError_t launch_select_schedule_t(const DraftSelectArgs& d, const ScheduleArgs& sa, hipStream_t stream) {
-  const void* fn = reinterpret_cast<const void*>(&draft_select_schedule<TL, TF>);
-  static bool attr = false;
-  if (!attr) {  // the scheduler's dynamic LDS reaches 80 KB at B gamma = 8192 with a 1024-point table
-    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 8192 * 8 + 1024 * 16) != hipSuccess)
-      return hipErrorUnknown;
-    attr = true;
-  }
+  // the scheduler's dynamic LDS reaches 80 KB at B gamma = 8192 with a 1024-point table
+  int unused = 0;
+  const hipError_t e = kernel_setup(reinterpret_cast<const void*>(&draft_select_schedule<TL, TF>), 256,
+                                    8192 * 8 + 1024 * 16, &unused);
+  if (e != hipSuccess) return e;
   const SelectScheduleArgs a{d, sa};
   launch(&draft_select_schedule<TL, TF>, dim3(d.B + schedule_groups(sa)), 256, schedule_lds_bytes(sa), stream, a);
   return hipGetLastError();

@@ -34,6 +34,14 @@ struct ProfileScope {
   bool on;
 };
 
+// One-time set-up of a kernel on the current device, safe under concurrent host
+// threads (done once per kernel, device and LDS size, under a lock): raises the
+// kernel's dynamic-LDS limit to `lds` when that exceeds 64 KB and stores in
+// *groups the device's CU count times the workgroups of `threads` threads that
+// fit on one CU (1 per CU if the occupancy query fails).  Returns the error of a
+// failed device query or attribute call (nothing is cached then).
+hipError_t kernel_setup(const void* fn, int threads, size_t lds, int* groups);
+
 // Launch of a kernel taking one argument struct, timed by the open ProfileScope.
 // Errors are left for hipGetLastError(), as with the <<<>>> launch.
 template <typename Arg, typename A>
@@ -178,5 +186,8 @@ size_t schedule_lds_bytes(const ScheduleArgs& a);  // its dynamic LDS
 // draw needs the general kernel (more than 4096 tiles).
 hipError_t launch_draft_select_schedule(const DraftSelectArgs& d, const ScheduleArgs& s, int logits_dtype,
                                         int factor_dtype, hipStream_t stream);
+
+// W2 [r, V] row-major -> [V, r] row-major (elements of 2 or 4 bytes).
+hipError_t launch_pack_w2(const void* w, void* out, int elem_bytes, int V, int r, hipStream_t s);
 
 }  // namespace dspark

@@ -45,13 +45,11 @@ size_t schedule_lds_bytes(const ScheduleArgs& a) {
 
 hipError_t launch_schedule(const ScheduleArgs& a, hipStream_t s) {
   const size_t lds = schedule_lds_bytes(a);
-  static bool attr = false;
-  if (!attr) {  // dynamic LDS above 64 KB: 80 KB at B gamma = 8192 with a 1024-point table
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&schedule_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            8192 * 8 + 1024 * 16) != hipSuccess)
-      return hipErrorUnknown;
-    attr = true;
-  }
+  // dynamic LDS above 64 KB: 80 KB at B gamma = 8192 with a 1024-point table
+  int unused = 0;
+  const hipError_t e =
+      kernel_setup(reinterpret_cast<const void*>(&schedule_kernel), kThreads, 8192 * 8 + 1024 * 16, &unused);
+  if (e != hipSuccess) return e;
   launch(&schedule_kernel, schedule_groups(a), kThreads, lds, s, a);
   return hipGetLastError();
 }

@@ -70,10 +70,16 @@ __device__ __forceinline__ void schedule_block(const ScheduleArgs& a, int bid, i
   double* const tT = tB + np;
   const bool ranked = a.rule == DSPARK_SCHED_EARLY_STOP || a.rule == DSPARK_SCHED_ARGMAX;
 
+  // the table: batch sizes strictly increasing, rates positive and finite (else
+  // a status bit; the budgets are then unspecified, every access stays in bounds)
+  bool bad_table = false;
   for (int i = tid; i < np; i += kThreads) {
-    tB[i] = a.sps_B[i];
-    tT[i] = 1.0 / a.sps_val[i];
+    const double bi = a.sps_B[i], vi = a.sps_val[i];
+    tB[i] = bi;
+    tT[i] = 1.0 / vi;
+    if (!(vi > 0.0 && vi < INFINITY) || !(bi < INFINITY) || (i > 0 && !(bi > a.sps_B[i - 1]))) bad_table = true;
   }
+  if (bad_table && bid == 0) flag_status(a.status, kBadTable);
   bool bad = false;
   const float thr = (float)a.param;
   for (int b = tid; b < B; b += kThreads) {

@@ -107,11 +107,13 @@ __device__ __forceinline__ BlockStat block_stats(const VerifyArgs& a, int row, i
   float s = 0.0f;
   int arg = 0x7fffffff;
   if (T > 0.0f) {
-    // 2^((z - m) c) as 2^(z c - m c): one fused multiply-add per element
-    const float c = kLog2e / T, mc = m == -INFINITY ? 0.0f : m * c;
+    // 2^((z - m) c): the difference first (exact for bf16 inputs, one rounding
+    // relative to |z - m| for fp32), so the terms near the maximum carry no
+    // error proportional to |m| / T, as a shift by a rounded m c would
+    const float c = kLog2e / T, mm = m == -INFINITY ? 0.0f : m;
     float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 64; i += 2) s0 += exp2_flush(fmaf(z[i], c, -mc)), s1 += exp2_flush(fmaf(z[i + 1], c, -mc));
+    for (int i = 0; i < 64; i += 2) s0 += exp2_flush((z[i] - mm) * c), s1 += exp2_flush((z[i + 1] - mm) * c);
     s = wave_sum(s0 + s1);
   } else {
 #pragma unroll

@@ -22,6 +22,7 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "dspark.h")
 
 DSPARK_BF16, DSPARK_F32 = 0, 1
 DSPARK_OK, DSPARK_EINVAL, DSPARK_EHIP, DSPARK_EDATA = 0, -1, -2, -3
+DSPARK_W_VOCAB_MAJOR, DSPARK_W_RANK_MAJOR = 0, 1
 SCHED_RULES = {"early_stop": 0, "argmax": 1, "fixed": 2, "threshold": 3}
 KERNEL_CLASSES = {"draft_gemm": 0, "draft_select": 1, "row_stats": 2, "accept": 3,
                   "residual_gemm": 4, "residual_select": 5, "schedule": 6, "acceptance": 7}
@@ -41,15 +42,16 @@ _SIG = {
     "dspark_error_string": (ctypes.c_char_p, [_I]),
     "dspark_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
     "dspark_schedule_workspace_bytes": (ctypes.c_size_t, [_I, _I]),
-    "dspark_draft_round": (_I, [_P, _I, _P, _P, _I, _P, _P, ctypes.c_uint64, _P,
+    "dspark_pack_w2": (_I, [_P, _I, _I, _I, _P, _P]),
+    "dspark_draft_round": (_I, [_P, _I, _P, _P, _I, _I, _P, _P, ctypes.c_uint64, _P,
                                 _I, _I, _I, _I, _P, _P, _P, _P, _P]),
-    "dspark_draft_schedule": (_I, [_P, _I, _P, _P, _I, _P, _P, ctypes.c_uint64, _P, _I, _I, _I, _I, _P, _P, _P,
-                                   _P, _P, _P, _P, _I, _I, ctypes.c_double, _P, _P, _P]),
+    "dspark_draft_schedule": (_I, [_P, _I, _P, _P, _I, _I, _P, _P, ctypes.c_uint64, _P, _I, _I, _I, _I, _P, _P,
+                                   _P, _P, _P, _P, _P, _I, _I, ctypes.c_double, _P, _P, _P]),
     "dspark_schedule": (_I, [_P, _P, _P, _I, _I, _I, _P, _P, _P]),
     "dspark_schedule_ex": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_double, _P, _P, _P]),
-    "dspark_verify": (_I, [_P, _P, _I, _P, _P, _I, _P, _P, _P, _P, _P, _P, ctypes.c_uint64, _P,
+    "dspark_verify": (_I, [_P, _P, _I, _P, _P, _I, _I, _P, _P, _P, _P, _P, _P, ctypes.c_uint64, _P,
                            _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]),
-    "dspark_acceptance": (_I, [_P, _P, _I, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _P]),
+    "dspark_acceptance": (_I, [_P, _P, _I, _P, _P, _I, _I, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _P]),
     "dspark_status": (_I, [_P, _P]),
     "dspark_profile_enable": (_I, [_I, _I]),
     "dspark_profile_read": (_I, [_I, ctypes.POINTER(_I), ctypes.POINTER(ctypes.c_double)]),
@@ -130,16 +132,39 @@ def dspark_schedule_workspace_bytes(B: int, gamma: int) -> int:
     return int(lib().dspark_schedule_workspace_bytes(B, gamma))
 
 
+def _w_layout(U, W, V, w_layout):
+    """The layout code of W2: given, or read from its shape ([V, r]: vocabulary-major,
+    [r, V]: rank-major, which the round calls reject)."""
+    r = U.shape[1]
+    if tuple(U.shape) != (V, r) or U.dtype != W.dtype:
+        raise ValueError("U must be [V, r] with the dtype of W")
+    if w_layout is None:
+        if tuple(W.shape) == (V, r):
+            return DSPARK_W_VOCAB_MAJOR
+        if tuple(W.shape) == (r, V):
+            return DSPARK_W_RANK_MAJOR
+        raise ValueError("W must be [V, r] (vocabulary-major) or [r, V]")
+    return int(w_layout)
+
+
+def dspark_pack_w2(W, W_packed, stream=None):
+    """W [r, V] -> W_packed [V, r] (the vocabulary-major layout the round reads)."""
+    r, V = W.shape
+    if tuple(W_packed.shape) != (V, r) or W_packed.dtype != W.dtype:
+        raise ValueError("W_packed must be [V, r] with the dtype of W")
+    _check("dspark_pack_w2", lib().dspark_pack_w2(_dev(W, "W"), _dtype_code(W), V, r,
+                                                  _dev(W_packed, "W_packed"), _stream(stream)))
+
+
 def dspark_draft_round(base_logits, U, W, prev0, temperature, seed, pos_offset,
-                       draft_tokens, draft_logq, draft_lse, workspace, stream=None):
-    """base_logits [B, gamma, V]; U, W [V, r] (W = second factor, vocabulary-major)."""
+                       draft_tokens, draft_logq, draft_lse, workspace, stream=None, w_layout=None):
+    """base_logits [B, gamma, V]; U [V, r]; W = second factor, [V, r] vocabulary-major."""
     B, gamma, V = base_logits.shape
     r = U.shape[1]
-    if tuple(U.shape) != (V, r) or tuple(W.shape) != (V, r) or U.dtype != W.dtype:
-        raise ValueError("U and W must both be [V, r] of one dtype")
+    lay = _w_layout(U, W, V, w_layout)
     rc = lib().dspark_draft_round(
         _dev(base_logits, "base_logits"), _dtype_code(base_logits), _dev(U, "U"), _dev(W, "W"),
-        _dtype_code(U), _dev(prev0, "prev0", torch.int32), _dev(temperature, "temperature", torch.float32),
+        _dtype_code(U), lay, _dev(prev0, "prev0", torch.int32), _dev(temperature, "temperature", torch.float32),
         int(seed) & (2 ** 64 - 1), _dev(pos_offset, "pos_offset", torch.int32, optional=True),
         B, gamma, V, r, _dev(draft_tokens, "draft_tokens", torch.int32),
         _dev(draft_logq, "draft_logq", torch.float32), _dev(draft_lse, "draft_lse", torch.float64),
@@ -148,20 +173,20 @@ def dspark_draft_round(base_logits, U, W, prev0, temperature, seed, pos_offset,
 
 
 def dspark_draft_schedule(base_logits, U, W, prev0, temperature, seed, pos_offset, draft_tokens, draft_logq,
-                          draft_lse, conf, tau, sps_B, sps_val, rule, param, budget, workspace, stream=None):
+                          draft_lse, conf, tau, sps_B, sps_val, rule, param, budget, workspace, stream=None,
+                          w_layout=None):
     """dspark_draft_round then dspark_schedule_ex in one call (the scheduler runs
     in the launch of the last draw)."""
     B, gamma, V = base_logits.shape
     r = U.shape[1]
-    if tuple(U.shape) != (V, r) or tuple(W.shape) != (V, r) or U.dtype != W.dtype:
-        raise ValueError("U and W must both be [V, r] of one dtype")
+    lay = _w_layout(U, W, V, w_layout)
     if tuple(conf.shape) != (B, gamma):
         raise ValueError("conf must be [B, gamma]")
     code = SCHED_RULES[rule] if isinstance(rule, str) else int(rule)
     n = int(sps_B.numel()) if sps_B is not None else 0
     rc = lib().dspark_draft_schedule(
         _dev(base_logits, "base_logits"), _dtype_code(base_logits), _dev(U, "U"), _dev(W, "W"),
-        _dtype_code(U), _dev(prev0, "prev0", torch.int32), _dev(temperature, "temperature", torch.float32),
+        _dtype_code(U), lay, _dev(prev0, "prev0", torch.int32), _dev(temperature, "temperature", torch.float32),
         int(seed) & (2 ** 64 - 1), _dev(pos_offset, "pos_offset", torch.int32, optional=True),
         B, gamma, V, r, _dev(draft_tokens, "draft_tokens", torch.int32),
         _dev(draft_logq, "draft_logq", torch.float32), _dev(draft_lse, "draft_lse", torch.float64),
@@ -197,14 +222,15 @@ def dspark_schedule_ex(conf, tau, sps_B, sps_val, rule, param, budget, workspace
 
 def dspark_verify(target_logits, base_logits, U, W, prev0, draft_tokens, draft_logq, draft_lse,
                   budget, temperature, seed, pos_offset, out_tokens, num_accepted, num_emitted,
-                  workspace, debug_logp_logq=None, debug_residual=None, stream=None):
+                  workspace, debug_logp_logq=None, debug_residual=None, stream=None, w_layout=None):
     B, gamma, V = base_logits.shape
     r = U.shape[1]
     if tuple(target_logits.shape) != (B, gamma + 1, V) or target_logits.dtype != base_logits.dtype:
         raise ValueError("target_logits must be [B, gamma+1, V] with the dtype of base_logits")
+    lay = _w_layout(U, W, V, w_layout)
     rc = lib().dspark_verify(
         _dev(target_logits, "target_logits"), _dev(base_logits, "base_logits"), _dtype_code(base_logits),
-        _dev(U, "U"), _dev(W, "W"), _dtype_code(U), _dev(prev0, "prev0", torch.int32),
+        _dev(U, "U"), _dev(W, "W"), _dtype_code(U), lay, _dev(prev0, "prev0", torch.int32),
         _dev(draft_tokens, "draft_tokens", torch.int32), _dev(draft_logq, "draft_logq", torch.float32),
         _dev(draft_lse, "draft_lse", torch.float64), _dev(budget, "budget", torch.int32, optional=True),
         _dev(temperature, "temperature", torch.float32), int(seed) & (2 ** 64 - 1),
@@ -218,15 +244,16 @@ def dspark_verify(target_logits, base_logits, U, W, prev0, draft_tokens, draft_l
 
 
 def dspark_acceptance(target_logits, base_logits, U, W, prev0, draft_tokens, draft_lse, temperature,
-                      c_star, workspace, stream=None):
+                      c_star, workspace, stream=None, w_layout=None):
     """c_star [B, gamma] float64 out: sum_v min(p_k, q_k) of every drafted position."""
     B, gamma, V = base_logits.shape
     r = U.shape[1]
     if tuple(target_logits.shape) != (B, gamma + 1, V) or target_logits.dtype != base_logits.dtype:
         raise ValueError("target_logits must be [B, gamma+1, V] with the dtype of base_logits")
+    lay = _w_layout(U, W, V, w_layout)
     rc = lib().dspark_acceptance(
         _dev(target_logits, "target_logits"), _dev(base_logits, "base_logits"), _dtype_code(base_logits),
-        _dev(U, "U"), _dev(W, "W"), _dtype_code(U), _dev(prev0, "prev0", torch.int32),
+        _dev(U, "U"), _dev(W, "W"), _dtype_code(U), lay, _dev(prev0, "prev0", torch.int32),
         _dev(draft_tokens, "draft_tokens", torch.int32), _dev(draft_lse, "draft_lse", torch.float64),
         _dev(temperature, "temperature", torch.float32), B, gamma, V, r,
         _dev(c_star, "c_star", torch.float64), _dev(workspace, "workspace", torch.uint8), _stream(stream))

@@ -25,7 +25,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_error_strings(lib):
-    assert ds.dspark_abi_version() == 4
+    assert ds.dspark_abi_version() == 5
     assert ds.error_string(0) == "ok"
     assert "argument" in ds.error_string(-1)
     assert "device" in ds.error_string(-3)
@@ -54,22 +54,42 @@ def test_host_argument_checks_return_einval(lib):
     P = ctypes.c_void_p
     nul = P(None)
     fake = P(256)  # never dereferenced: the checks fail before any launch
+    VM, RM = ds.DSPARK_W_VOCAB_MAJOR, ds.DSPARK_W_RANK_MAJOR
     # B = 0
-    rc = lib.dspark_draft_round(fake, 0, fake, fake, 0, fake, fake, 1, nul, 0, 5, 100, 16,
+    rc = lib.dspark_draft_round(fake, 0, fake, fake, 0, VM, fake, fake, 1, nul, 0, 5, 100, 16,
                                 fake, fake, fake, fake, nul)
     assert rc == ds.DSPARK_EINVAL
     # unknown dtype
-    rc = lib.dspark_draft_round(fake, 7, fake, fake, 0, fake, fake, 1, nul, 4, 5, 100, 16,
+    rc = lib.dspark_draft_round(fake, 7, fake, fake, 0, VM, fake, fake, 1, nul, 4, 5, 100, 16,
                                 fake, fake, fake, fake, nul)
     assert rc == ds.DSPARK_EINVAL
+    # W2 declared [r, V] (the pages' layout): the round reads only the packed layout
+    rc = lib.dspark_draft_round(fake, 0, fake, fake, 0, RM, fake, fake, 1, nul, 4, 5, 100, 16,
+                                fake, fake, fake, fake, nul)
+    assert rc == ds.DSPARK_EINVAL
+    rc = lib.dspark_draft_round(fake, 0, fake, fake, 0, 5, fake, fake, 1, nul, 4, 5, 100, 16,
+                                fake, fake, fake, fake, nul)
+    assert rc == ds.DSPARK_EINVAL
+    rc = lib.dspark_verify(fake, fake, 0, fake, fake, 0, RM, fake, fake, fake, fake, nul, fake, 1, nul,
+                           4, 5, 100, 16, fake, fake, fake, nul, nul, fake, nul)
+    assert rc == ds.DSPARK_EINVAL
+    rc = lib.dspark_acceptance(fake, fake, 0, fake, fake, 0, RM, fake, fake, fake, fake, 4, 5, 100, 16,
+                               fake, fake, nul)
+    assert rc == ds.DSPARK_EINVAL
     # missing workspace
-    rc = lib.dspark_verify(fake, fake, 0, fake, fake, 0, fake, fake, fake, fake, nul, fake, 1, nul,
+    rc = lib.dspark_verify(fake, fake, 0, fake, fake, 0, VM, fake, fake, fake, fake, nul, fake, 1, nul,
                            4, 5, 100, 16, fake, fake, fake, nul, nul, nul, nul)
     assert rc == ds.DSPARK_EINVAL
     # misaligned workspace
-    rc = lib.dspark_verify(fake, fake, 0, fake, fake, 0, fake, fake, fake, fake, nul, fake, 1, nul,
+    rc = lib.dspark_verify(fake, fake, 0, fake, fake, 0, VM, fake, fake, fake, fake, nul, fake, 1, nul,
                            4, 5, 100, 16, fake, fake, fake, nul, nul, P(257), nul)
     assert rc == ds.DSPARK_EINVAL
+    # packing W2: pointers, sizes and dtype are checked before any launch
+    assert lib.dspark_pack_w2(nul, 0, 100, 16, fake, nul) == ds.DSPARK_EINVAL
+    assert lib.dspark_pack_w2(fake, 0, 100, 16, nul, nul) == ds.DSPARK_EINVAL
+    assert lib.dspark_pack_w2(fake, 0, 0, 16, fake, nul) == ds.DSPARK_EINVAL
+    assert lib.dspark_pack_w2(fake, 0, 100, 0, fake, nul) == ds.DSPARK_EINVAL
+    assert lib.dspark_pack_w2(fake, 3, 100, 16, fake, nul) == ds.DSPARK_EINVAL
     # scheduler limits: too many candidates, too few table points
     assert lib.dspark_schedule(fake, fake, fake, 16, 1025, 8, fake, fake, nul) == ds.DSPARK_EINVAL
     assert lib.dspark_schedule(fake, fake, fake, 1, 4, 4, fake, fake, nul) == ds.DSPARK_EINVAL
@@ -80,11 +100,22 @@ def test_host_argument_checks_return_einval(lib):
     assert ex(fake, nul, nul, nul, 0, 4, 4, 1, 0.0, fake, fake, nul) == ds.DSPARK_EINVAL
     # draft + schedule in one call: the checks of both calls, before anything is enqueued
     dsch = lib.dspark_draft_schedule
-    assert dsch(fake, 0, fake, fake, 0, fake, fake, 1, nul, 4, 5, 100, 16, fake, fake, fake,
+    assert dsch(fake, 0, fake, fake, 0, VM, fake, fake, 1, nul, 4, 5, 100, 16, fake, fake, fake,
                 fake, nul, fake, fake, 16, 9, 0.0, fake, fake, nul) == ds.DSPARK_EINVAL      # unknown rule
-    assert dsch(fake, 0, fake, fake, 0, fake, fake, 1, nul, 4, 5, 100, 16, fake, fake, fake,
+    assert dsch(fake, 0, fake, fake, 0, VM, fake, fake, 1, nul, 4, 5, 100, 16, fake, fake, fake,
                 nul, nul, fake, fake, 16, 0, 0.0, fake, fake, nul) == ds.DSPARK_EINVAL       # no scores
-    assert dsch(fake, 7, fake, fake, 0, fake, fake, 1, nul, 4, 5, 100, 16, fake, fake, fake,
+    assert dsch(fake, 7, fake, fake, 0, VM, fake, fake, 1, nul, 4, 5, 100, 16, fake, fake, fake,
                 fake, nul, fake, fake, 16, 0, 0.0, fake, fake, nul) == ds.DSPARK_EINVAL      # unknown dtype
+    assert dsch(fake, 0, fake, fake, 0, RM, fake, fake, 1, nul, 4, 5, 100, 16, fake, fake, fake,
+                fake, nul, fake, fake, 16, 0, 0.0, fake, fake, nul) == ds.DSPARK_EINVAL      # [r, V] W2
     assert lib.dspark_status(nul, nul) == ds.DSPARK_EINVAL
     assert lib.dspark_profile_enable(99, 1) == ds.DSPARK_EINVAL
+
+
+def test_binding_reads_the_layout_from_the_shape():
+    import torch
+    U = torch.zeros((100, 16))
+    assert ds._w_layout(U, torch.zeros((100, 16)), 100, None) == ds.DSPARK_W_VOCAB_MAJOR
+    assert ds._w_layout(U, torch.zeros((16, 100)), 100, None) == ds.DSPARK_W_RANK_MAJOR
+    with pytest.raises(ValueError):
+        ds._w_layout(U, torch.zeros((50, 16)), 100, None)
