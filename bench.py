@@ -79,23 +79,29 @@ def measured_traffic(kernel_name):
     return rec["bytes"]
 
 
-def algorithmic(rnd, budgets, emitted):
+def algorithmic(rnd, budgets, emitted, rejected):
     """Bytes and flops each kernel class must move / perform per launch (what
-    the method needs, not what the kernels happen to do).  Verification needs
-    the target rows up to the first rejection only: rows 0..n_b of request b,
-    sum_b (n_b + 1) = sum of the emitted counts."""
+    the method needs, not what the kernels happen to do), counted as the
+    measurement plan of the hot path counts them:
+      draft step   the backbone row of every request (B V), W2 once per round
+                   (V r / gamma per step: the factor is the same at every block
+                   position), the U rows of the previous tokens (B r); the
+                   kernel's own tile records are overhead, reported apart;
+      verification target rows 0..n_b of request b (sum_b (n_b + 1) rows = the
+                   emitted count: the rows up to the first rejection);
+      residual     for every rejected request one target and one backbone row,
+                   plus W2 once."""
     B, g, V, r = rnd.B, rnd.gamma, rnd.V, rnd.r
     es = rnd.base.element_size()
     fs = rnd.U.element_size()
     n_tiles = -(-V // 64)
     rows = int(sum(int(e) for e in emitted))
     return {
-        # one draft step: backbone row of every request, W2 once, U rows gathered,
-        # tile statistics written
-        "draft_gemm": dict(bytes=B * V * es + V * r * fs + B * r * fs + B * n_tiles * 16,
-                           flops=2.0 * B * r * V, per="draft step"),
-        # target rows 0..n_b of every request read once (statistics, tests, final tokens)
+        "draft_gemm": dict(bytes=B * V * es + V * r * fs / g + B * r * fs,
+                           overhead_bytes=B * n_tiles * 16, flops=2.0 * B * r * V, per="draft step"),
         "row_stats": dict(bytes=rows * V * es, flops=0.0, per="verify"),
+        "residual_gemm": dict(bytes=rejected * 2 * V * es + V * r * fs, flops=2.0 * rejected * r * V,
+                              per="verify"),
     }
 
 
@@ -172,11 +178,13 @@ def main():
 
     budgets = bufs[0].budget.cpu().numpy()
     verified = int(budgets.sum())
+    n_acc = bufs[0].num_accepted.cpu().numpy()
     emitted = int(bufs[0].num_emitted.sum().item())
+    rejected = int((n_acc < budgets).sum())
     sec_per_step = (t1 - t0) / args.steps
     value = verified / sec_per_step
 
-    alg = algorithmic(base_round, budgets, bufs[0].num_emitted.cpu().numpy())
+    alg = algorithmic(base_round, budgets, bufs[0].num_emitted.cpu().numpy(), rejected)
     kernels = {}
     for name, st in per_class.items():
         if st["launches"]:
@@ -184,28 +192,35 @@ def main():
     for name, a in alg.items():
         if name in kernels:
             us = kernels[name]["avg_us"]
+            kernels[name]["algorithmic_bytes"] = a["bytes"]
             kernels[name]["GB_s"] = a["bytes"] / (us * 1e-6) / 1e9
+            kernels[name]["frac_hbm"] = kernels[name]["GB_s"] / HBM_PEAK_GBS
             if a["flops"]:
                 kernels[name]["TFLOP_s"] = a["flops"] / (us * 1e-6) / 1e12
+                kernels[name]["frac_mfma_bf16"] = kernels[name]["TFLOP_s"] / MFMA_BF16_PEAK_TFLOPS
 
     dom_avg_s = dom_ms / max(dom_n, 1) / 1e3
-    if dominant in alg and alg[dominant]["flops"] and dominant == "draft_gemm":
-        a = alg[dominant]
-        ach_bw = a["bytes"] / dom_avg_s / 1e9
-        ach_fl = a["flops"] / dom_avg_s / 1e12
-        # bound set by the arithmetic intensity of this launch against the ridge
-        if a["flops"] / a["bytes"] > MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
-            roof = dict(bound="mfma", achieved=ach_fl, peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s")
-        else:
-            roof = dict(bound="hbm", achieved=ach_bw, peak=HBM_PEAK_GBS, unit="GB/s")
+    a = alg.get(dominant, dict(bytes=0.0, flops=0.0))
+    ach_bw = a["bytes"] / dom_avg_s / 1e9
+    ach_fl = a["flops"] / dom_avg_s / 1e12
+    # bound set by the launch's arithmetic intensity against the ridge of the peaks
+    if a["flops"] and a["flops"] / a["bytes"] > MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
+        roof = dict(bound="mfma", achieved=ach_fl, peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s")
     else:
-        a = alg.get(dominant, dict(bytes=0.0))
-        roof = dict(bound="hbm", achieved=a["bytes"] / dom_avg_s / 1e9, peak=HBM_PEAK_GBS, unit="GB/s")
+        roof = dict(bound="hbm", achieved=ach_bw, peak=HBM_PEAK_GBS, unit="GB/s")
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = measured_traffic(dominant)
+    traffic = measured_traffic(dominant)
+    roof["traffic"] = traffic
+    roof["algorithmic_bytes"] = a["bytes"]
+    roof["traffic_over_algorithmic"] = traffic / a["bytes"] if traffic else None
     roof["kernel"] = dominant
     roof["avg_us"] = dom_avg_s * 1e6
     roof["timed_launches"] = dom_n
+    if a["flops"]:
+        roof["mfma"] = dict(achieved=ach_fl, peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                            frac=ach_fl / MFMA_BF16_PEAK_TFLOPS, flops=a["flops"])
+    if "overhead_bytes" in a:
+        roof["overhead_bytes"] = a["overhead_bytes"]
     # the same achieved rate against what this device reaches in plain kernels
     peaks = measure_peaks()
     roof["measured_peak"] = peaks
@@ -213,6 +228,7 @@ def main():
                                                    else peaks["mfma_bf16_TFLOP_s"])
 
     extras = measure_extras(rounds[0], bufs[0])
+    extras["full_budget"] = full_budget_round(rounds, args.steps)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -235,6 +251,7 @@ def main():
                                "T=1, confidence-scheduled budgets",
                    "B": base_round.B, "gamma": base_round.gamma, "V": base_round.V, "r": base_round.r,
                    "verified_per_round": verified, "emitted_per_round": emitted,
+                   "rejected_per_round": rejected,
                    "emitted_tokens_per_s": emitted / sec_per_step},
         "round_ms": round_ms,
         "roofline": roof,
@@ -243,6 +260,56 @@ def main():
         "extras": extras,
     }
     print(json.dumps(line), flush=True)
+
+
+def full_budget_round(rounds, steps):
+    """The same inputs verified at the full budget L = gamma (no scheduler):
+    verified tokens/s and per-kernel times, timed as the headline (three input
+    sets in rotation, K rounds between synchronisations)."""
+    import dataclasses
+
+    import torch
+
+    from lossless_rejection_sampling_amd import dspark as ds
+    from lossless_rejection_sampling_amd import round as rd
+
+    full = [dataclasses.replace(r, conf=None, budget=None) for r in rounds]
+    bufs = [rd.allocate(r) for r in full]
+    step = lambda i: rd.run_round(full[i % N_SETS], bufs[i % N_SETS])
+    for i in range(3):
+        step(i)
+    torch.cuda.synchronize()
+    for c in ds.KERNEL_CLASSES.values():
+        ds.dspark_profile_enable(c, True)
+    for i in range(N_SETS * 2):
+        step(i)
+    torch.cuda.synchronize()
+    per = {}
+    for name, c in ds.KERNEL_CLASSES.items():
+        n, ms = ds.dspark_profile_read(c)
+        ds.dspark_profile_enable(c, False)
+        if n:
+            per[name] = dict(avg_us=1e3 * ms / n, launches_per_round=n / (N_SETS * 2))
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / steps
+    assert ds.dspark_status(bufs[0].workspace) == ds.DSPARK_OK
+    B, g = full[0].B, full[0].gamma
+    n_acc = bufs[0].num_accepted.cpu().numpy()
+    emitted = int(bufs[0].num_emitted.sum().item())
+    alg = algorithmic(full[0], None, bufs[0].num_emitted.cpu().numpy(), int((n_acc < g).sum()))
+    for name, a in alg.items():
+        if name in per:
+            us = per[name]["avg_us"]
+            per[name]["GB_s"] = a["bytes"] / (us * 1e-6) / 1e9
+            per[name]["frac_hbm"] = per[name]["GB_s"] / HBM_PEAK_GBS
+    out = {"verified_per_round": B * g, "emitted_per_round": emitted, "ms_per_step": sec * 1e3,
+           "verified_tokens_per_s": B * g / sec, "emitted_tokens_per_s": emitted / sec, "kernels": per}
+    del bufs
+    torch.cuda.empty_cache()
+    return out
 
 
 def round_distribution(step, start, reps=None):
@@ -365,69 +432,91 @@ def measure_extras(rnd, buf, reps=5):
     return {"acceptance_pass": acc, "schedulers": sched, "sequential_temperature_scaling": sts}
 
 
-def cpu_baseline(rnd, budgets, seconds):
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(rnd, budgets, seconds, threads=None):
     """The oracle, as it stands, on a bounded sample of the same round: whole
-    requests (draft of every position, verify with the GPU-granted budgets)
-    until about ``seconds`` of CPU time; the scheduler runs over the full batch
-    once.  Reported as verified draft tokens per second."""
+    requests (draft of every position, verify with the GPU-granted budgets),
+    spread over a pool of host threads (one BLAS thread each; numpy releases
+    the interpreter lock inside its array operations), until about ``seconds``
+    of wall time; the scheduler runs over the full batch once.  Reported as
+    verified draft tokens per second, extrapolated per request to the batch."""
+    import concurrent.futures as cf
+
     import numpy as np
-    import torch
 
     from lossless_rejection_sampling_amd import workloads as wl
     from oracle import dspark as od
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
-    except Exception:
-        threads = 1
+    threads = threads or max(1, min(16, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity")
+                                  else (os.cpu_count() or 1)))
     h = wl.to_host
     U, W = h(rnd.U), h(rnd.W)
     conf = h(rnd.conf)
     t_start = time.perf_counter()
     sched = od.schedule(conf, rnd.sps_B, rnd.sps_val)
     t_sched = time.perf_counter() - t_start
-    done, verified, t_work = 0, 0, 0.0
-    while t_work < seconds and done < rnd.B:
-        idx = [done]
-        t = torch.as_tensor(idx, device=rnd.base.device)
-        base, target = h(rnd.base.index_select(0, t)), h(rnd.target.index_select(0, t))
-        prev0, T = h(rnd.prev0.index_select(0, t)), h(rnd.temperature.index_select(0, t))
-        c0 = time.perf_counter()
+
+    def one(b):
+        idx = [b]
+        base, target = h(rnd.base[b:b + 1]), h(rnd.target[b:b + 1])
+        prev0, T = h(rnd.prev0[b:b + 1]), h(rnd.temperature[b:b + 1])
         dr = od.draft_round(base, U, W, prev0, T, rnd.seed, req_ids=idx)
         od.verify(target, base, U, W, prev0, dr.tokens, T, rnd.seed, sched.budget[idx], req_ids=idx)
-        t_work += time.perf_counter() - c0
-        verified += int(sched.budget[done])
-        done += 1
-    per_req = t_work / done
-    round_s = per_req * rnd.B + t_sched
-    # the same at one thread, on the first requests of the sample
-    single = None
+        return b
+
+    def run(n_threads, budget_s):
+        done = 0
+        t0 = time.perf_counter()
+        with cf.ThreadPoolExecutor(n_threads) as ex:
+            futs = []
+            nxt = 0
+            while nxt < min(rnd.B, n_threads):
+                futs.append(ex.submit(one, nxt))
+                nxt += 1
+            while futs:
+                f = futs.pop(0)
+                f.result()
+                done += 1
+                if time.perf_counter() - t0 < budget_s and nxt < rnd.B:
+                    futs.append(ex.submit(one, nxt))
+                    nxt += 1
+        return done, time.perf_counter() - t0
+
     try:
         from threadpoolctl import threadpool_limits
-        with threadpool_limits(limits=1):
-            n1, t1 = 0, 0.0
-            while t1 < seconds / 4 and n1 < done:
-                idx = [n1]
-                t = torch.as_tensor(idx, device=rnd.base.device)
-                base, target = h(rnd.base.index_select(0, t)), h(rnd.target.index_select(0, t))
-                prev0, T = h(rnd.prev0.index_select(0, t)), h(rnd.temperature.index_select(0, t))
-                c0 = time.perf_counter()
-                dr = od.draft_round(base, U, W, prev0, T, rnd.seed, req_ids=idx)
-                od.verify(target, base, U, W, prev0, dr.tokens, T, rnd.seed, sched.budget[idx], req_ids=idx)
-                t1 += time.perf_counter() - c0
-                n1 += 1
-            single = {"value": float(np.sum(budgets)) / (t1 / n1 * rnd.B + t_sched), "cores": 1,
-                      "sample": f"{n1} requests ({t1:.1f} s), same extrapolation"}
+        limit = threadpool_limits(limits=1)
     except Exception:
-        single = None
+        limit = None
+    try:
+        done, wall = run(threads, seconds)
+        d1, w1 = run(1, seconds / 4)
+    finally:
+        if limit is not None:
+            limit.restore_original_limits()
+    verified = float(np.sum(budgets))
+    round_s = wall / done * rnd.B + t_sched
+    single = {"value": verified / (w1 / d1 * rnd.B + t_sched), "cores": 1,
+              "sample": f"{d1} requests ({w1:.1f} s) on one thread, same extrapolation"}
     return {
-        "value": float(np.sum(budgets)) / round_s,
+        "value": verified / round_s,
         "unit": "verified draft tokens/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"{done} of {rnd.B} requests timed whole (draft + verify, {t_work:.1f} s) plus the "
-                  f"scheduler over all {rnd.B} ({t_sched:.2f} s), extrapolated per request to the batch",
+        "cpu_model": _cpu_model(),
+        "host_cpus_visible": os.cpu_count(),
+        "sample": f"{done} of {rnd.B} requests timed whole (draft + verify) on {threads} threads in "
+                  f"{wall:.1f} s, plus the scheduler over all {rnd.B} ({t_sched:.2f} s), extrapolated per "
+                  f"request to the batch",
         "single_thread": single,
     }
 

@@ -190,15 +190,24 @@ namespace {
 
 // Arguments of the scheduler over `workspace` (its part of the layout and the
 // status word), or DSPARK_EINVAL with nothing enqueued.
-int schedule_args(const float* conf, const float* tau, const double* sps_B, const double* sps_val, int n_points,
-                  int B, int gamma, int rule, double param, int32_t* budget, void* workspace, ScheduleArgs& a) {
+int schedule_args_ok(const float* conf, const double* sps_B, const double* sps_val, int n_points, int B, int gamma,
+                     int rule, double param, int32_t* budget) {
   if (!schedule_sizes_ok(B, gamma)) return DSPARK_EINVAL;
   if (rule < DSPARK_SCHED_EARLY_STOP || rule > DSPARK_SCHED_THRESHOLD) return DSPARK_EINVAL;
   const bool table = rule == DSPARK_SCHED_EARLY_STOP || rule == DSPARK_SCHED_ARGMAX;
   if (table && (n_points < 2 || n_points > 1024 || !sps_B || !sps_val)) return DSPARK_EINVAL;
   if (!(param == param)) return DSPARK_EINVAL;  // NaN
-  if (!conf || !budget || !workspace) return DSPARK_EINVAL;
+  if (!conf || !budget) return DSPARK_EINVAL;
+  return DSPARK_OK;
+}
+
+int schedule_args(const float* conf, const float* tau, const double* sps_B, const double* sps_val, int n_points,
+                  int B, int gamma, int rule, double param, int32_t* budget, void* workspace, ScheduleArgs& a) {
+  const int ok = schedule_args_ok(conf, sps_B, sps_val, n_points, B, gamma, rule, param, budget);
+  if (ok != DSPARK_OK) return ok;
+  if (!workspace) return DSPARK_EINVAL;
   if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return DSPARK_EINVAL;
+  const bool table = rule == DSPARK_SCHED_EARLY_STOP || rule == DSPARK_SCHED_ARGMAX;
   a = ScheduleArgs{};
   a.conf = conf, a.tau = tau, a.sps_B = sps_B, a.sps_val = sps_val, a.n_points = table ? n_points : 0;
   a.B = B, a.gamma = gamma, a.rule = rule, a.param = param, a.budget = budget;

@@ -12,15 +12,19 @@ the shapes the pages give (blocks of 4-16 tokens, the deployed 5-token block,
 batch sizes up to 1024 requests, vocabularies of the Qwen3 / DeepSeek-V3 / Gemma
 families) and the distributions stated for each workload below.
 
-Every generator is deterministic for a given ``device``: tensors are drawn with
-a ``torch.Generator`` seeded from the workload's fixed seed.  The same tensor
-object is then handed to both sides of a comparison.
+The full-size workloads are drawn on the host (numpy PCG64, see
+``host_normal``) and then moved to ``device``, so a run on any device and a
+run of the CPU oracle see bit-identical inputs; the small generic rounds of
+the edge-case tests (``small_random``) are drawn with a ``torch.Generator`` on
+the device and handed, as the same tensor, to both sides of a comparison.
 """
 
 from __future__ import annotations
 
 import dataclasses
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 from typing import Optional
 
 import numpy as np
@@ -94,6 +98,46 @@ def _randn(shape, g, device, std=1.0, dtype=torch.float32):
     return torch.randn(shape, generator=g, device=device, dtype=torch.float32).mul_(std).to(dtype)
 
 
+# ---------------------------------------------------------------------------
+# Host generation.  The full-size workloads are drawn on the host with numpy's
+# PCG64 so that the CPU oracle can be run on exactly the inputs a GPU run sees:
+# a tensor is filled in fixed chunks of 2^22 elements, chunk i from its own
+# stream keyed by (seed, tag, i), so the values do not depend on how many threads
+# fill it; small draws (permutations, token ids, row choices) come from one
+# stream keyed by (seed, tag).
+# ---------------------------------------------------------------------------
+_CHUNK = 1 << 22
+_THREADS = max(1, min(16, os.cpu_count() or 1))
+
+
+def _stream(seed: int, tag: int, i: int = 0) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, tag, i])))
+
+
+def host_normal(shape, seed: int, tag: int, std: float = 1.0) -> np.ndarray:
+    """float32 array of `shape` with N(0, std^2) entries (std applied in fp32)."""
+    out = np.empty(int(np.prod(shape)), dtype=np.float32)
+    n = out.size
+    chunks = range((n + _CHUNK - 1) // _CHUNK)
+
+    def fill(i):
+        seg = out[i * _CHUNK:min(n, (i + 1) * _CHUNK)]
+        _stream(seed, tag, i).standard_normal(seg.size, dtype=np.float32, out=seg)
+        if std != 1.0:
+            seg *= np.float32(std)
+
+    with ThreadPoolExecutor(_THREADS) as ex:
+        list(ex.map(fill, chunks))
+    return out.reshape(shape)
+
+
+def _t(a: np.ndarray, device, dtype=None) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.to(device)
+
+
 def sps_table_linear(n_points: int = 16, t0_us: float = 20000.0, dt_us: float = 5.0):
     """Synthetic monotone step-rate table: batch sizes round(2**(10 i / 15)) for
     i = 0..15 (1 .. 1024 tokens) with step time t(B) = t0 + dt * B microseconds."""
@@ -102,13 +146,29 @@ def sps_table_linear(n_points: int = 16, t0_us: float = 20000.0, dt_us: float = 
     return Bs, steps_per_s
 
 
+def sps_table_curved():
+    """A step-rate table whose step time is not linear in the batch: 8 points
+    from 1 to 512 tokens with t(B) = 20000 + 40 sqrt(B) + 0.02 B^2 microseconds
+    (a flat launch-bound start, then a compute-bound rise).  Verify batches of a
+    few hundred requests reach past its last point, where the scheduler extends
+    the last segment."""
+    Bs = np.array([1.0, 4.0, 16.0, 48.0, 96.0, 192.0, 320.0, 512.0])
+    t_us = 20000.0 + 40.0 * np.sqrt(Bs) + 0.02 * Bs ** 2
+    return Bs, 1.0e6 / t_us
+
+
 def confidence_scores(B: int, gamma: int, g, device):
-    """c[b, j-1] = sigmoid(N(1.5 - 0.4 j, 1)) for block position j = 1..gamma."""
-    j = torch.arange(1, gamma + 1, device=device, dtype=torch.float32)
-    z = torch.randn((B, gamma), generator=g, device=device, dtype=torch.float32) + (1.5 - 0.4 * j)
-    c = torch.sigmoid(z)
+    """c[b, j-1] = sigmoid(N(1.5 - 0.4 j, 1)) for block position j = 1..gamma.
+    `g` is a torch.Generator (drawn with torch) or an int seed (drawn on the host)."""
+    j = np.arange(1, gamma + 1, dtype=np.float64)
+    if isinstance(g, torch.Generator):
+        z = torch.randn((B, gamma), generator=g, device=g.device, dtype=torch.float32).double().cpu().numpy()
+    else:
+        z = _stream(int(g), 90).standard_normal((B, gamma))
+    c = (1.0 / (1.0 + np.exp(-(z + (1.5 - 0.4 * j))))).astype(np.float32)
     # keep strictly inside (0, 1) in fp32
-    return c.clamp_(min=1.0e-7, max=1.0 - 2.0 ** -24)
+    c = np.clip(c, np.float32(1.0e-7), np.float32(1.0 - 2.0 ** -24))
+    return torch.from_numpy(c).to(device)
 
 
 def tiny(device="cpu") -> Round:
@@ -116,23 +176,29 @@ def tiny(device="cpu") -> Round:
     target[:, :4] + N(0, 0.5^2); Markov head rank 16 with fp32 factors N(0, 1/16);
     prev0 uniform; Philox seed 0; full verify."""
     B, gamma, V, r = 4, 4, 1024, 16
-    g = _gen(device, 1234 + 1)
-    target = _randn((B, gamma + 1, V), g, device, std=2.0)
-    base = target[:, :gamma] + _randn((B, gamma, V), g, device, std=0.5)
-    U = _randn((V, r), g, device, std=0.25)
-    Wt = _randn((V, r), g, device, std=0.25)
-    prev0 = torch.randint(0, V, (B,), generator=g, device=device, dtype=torch.int64).to(torch.int32)
-    T = torch.ones(B, device=device, dtype=torch.float32)
-    return Round("tiny", target.contiguous(), base.contiguous(), U, Wt, prev0, T, seed=0)
+    seed = 1234 + 1
+    target = host_normal((B, gamma + 1, V), seed, 1, std=2.0)
+    base = target[:, :gamma] + host_normal((B, gamma, V), seed, 2, std=0.5)
+    U = host_normal((V, r), seed, 3, std=0.25)
+    Wt = host_normal((V, r), seed, 4, std=0.25)
+    prev0 = _stream(seed, 5).integers(0, V, B).astype(np.int32)
+    T = np.ones(B, dtype=np.float32)
+    return Round("tiny", _t(target, device), _t(base, device), _t(U, device), _t(Wt, device),
+                 _t(prev0, device), _t(T, device), seed=0)
 
 
-def _boosted_target(B, gamma, V, g, device, std=3.0, boost=6.0, frac=0.05):
-    """bf16 target logits N(0, std^2) with one fixed seeded set of floor(frac*V)
+def _boosted_target(B, gamma, V, seed, std=3.0, boost=6.0, frac=0.05):
+    """fp32 target logits N(0, std^2) with one fixed seeded set of floor(frac*V)
     vocabulary ids raised by ``boost`` in every row (peaked distributions)."""
-    t = torch.randn((B, gamma + 1, V), generator=g, device=device, dtype=torch.float32).mul_(std)
-    ids = torch.randperm(V, generator=g, device=device)[: int(frac * V)]
-    t[:, :, ids] += boost
-    return t.to(torch.bfloat16)
+    t = host_normal((B, gamma + 1, V), seed, 1, std=std)
+    ids = _stream(seed, 2).permutation(V)[: int(frac * V)]
+    t[:, :, ids] += np.float32(boost)
+    return t
+
+
+def _bf16_sum(a: np.ndarray, b: np.ndarray, device) -> torch.Tensor:
+    """bf16(a + b) with a + b formed in fp32, on the device."""
+    return (_t(a, device) + _t(b, device)).to(torch.bfloat16)
 
 
 def dspark5(B=64, V=151936, gamma=5, r=256, device="cpu", seed_base=1234 + 2, T=1.0,
@@ -141,47 +207,56 @@ def dspark5(B=64, V=151936, gamma=5, r=256, device="cpu", seed_base=1234 + 2, T=
     ids boosted by +6; backbone logits = target + N(0, 1) (bf16); Markov factors
     bf16 N(0, 1/256); uniform previous tokens; T = 1.  With ``scheduled`` the
     round also carries confidence scores and the synthetic step-rate table."""
-    g = _gen(device, seed_base)
-    target = _boosted_target(B, gamma, V, g, device)
-    base = (target[:, :gamma].float() + _randn((B, gamma, V), g, device)).to(torch.bfloat16)
-    U = _randn((V, r), g, device, std=1.0 / 16.0, dtype=torch.bfloat16)
-    Wt = _randn((V, r), g, device, std=1.0 / 16.0, dtype=torch.bfloat16)
-    prev0 = torch.randint(0, V, (B,), generator=g, device=device, dtype=torch.int64).to(torch.int32)
+    seed = seed_base
+    target = _t(_boosted_target(B, gamma, V, seed), device, torch.bfloat16)
+    noise = host_normal((B, gamma, V), seed, 3)
+    base = (target[:, :gamma].float() + _t(noise, device)).to(torch.bfloat16)
+    del noise
+    U = _t(host_normal((V, r), seed, 4, std=1.0 / 16.0), device, torch.bfloat16)
+    Wt = _t(host_normal((V, r), seed, 5, std=1.0 / 16.0), device, torch.bfloat16)
+    prev0 = _t(_stream(seed, 6).integers(0, V, B).astype(np.int32), device)
     Tt = torch.full((B,), T, device=device, dtype=torch.float32)
     rnd = Round(name or f"dspark5_B{B}", target.contiguous(), base.contiguous(), U, Wt, prev0, Tt,
                 seed=20260706)
     if scheduled:
-        rnd.conf = confidence_scores(B, gamma, g, device)
+        rnd.conf = confidence_scores(B, gamma, seed, device)
         rnd.sps_B, rnd.sps_val = sps_table_linear()
     return rnd
 
 
-def headline(device="cpu") -> Round:
+def headline(device="cpu", scheduled=True) -> Round:
     """B=256, gamma=5, V=151936, r=256: the DSpark-5 generator at B=256 with the
-    confidence-scheduled verify (scores and step-rate table as in ``scheduled``)."""
-    return dspark5(B=256, device=device, seed_base=1234 + 6, scheduled=True, name="headline_B256")
+    confidence-scheduled verify (scores and step-rate table as in ``scheduled``);
+    ``scheduled=False``: the same inputs verified at the full budget L = gamma."""
+    rnd = dspark5(B=256, device=device, seed_base=1234 + 6, scheduled=True, name="headline_B256")
+    if not scheduled:
+        rnd.conf = None
+        rnd.name = "headline_B256_full"
+    return rnd
 
 
 def block_length(gamma: int, B=256, V=151936, r=256, device="cpu") -> Round:
     """Block-length scaling at T = 0.8.  Each target row independently: 70% peaked
     (N(0, 2^2) with one uniform id +10), 30% flat N(0, 1).  Backbone row j =
     target row j-1 + N(0, sigma_j^2), sigma_j = 0.5 + 1.5 (j-1)/(gamma-1)."""
-    g = _gen(device, 1234 + 3 + 100 * gamma)
+    seed = 1234 + 3 + 100 * gamma
     rows = B * (gamma + 1)
-    t = torch.randn((rows, V), generator=g, device=device, dtype=torch.float32)
-    peaked = torch.rand((rows,), generator=g, device=device) < 0.7
-    scale = torch.where(peaked, torch.tensor(2.0, device=device), torch.tensor(1.0, device=device))
-    t.mul_(scale[:, None])
-    hot = torch.randint(0, V, (rows,), generator=g, device=device)
-    t[torch.arange(rows, device=device), hot] += torch.where(peaked, 10.0, 0.0)
-    target = t.view(B, gamma + 1, V).to(torch.bfloat16)
-    sig = torch.tensor([0.5 + 1.5 * (j - 1) / max(gamma - 1, 1) for j in range(1, gamma + 1)],
-                       device=device, dtype=torch.float32)
-    noise = torch.randn((B, gamma, V), generator=g, device=device, dtype=torch.float32) * sig[None, :, None]
-    base = (target[:, :gamma].float() + noise).to(torch.bfloat16)
-    U = _randn((V, r), g, device, std=1.0 / 16.0, dtype=torch.bfloat16)
-    Wt = _randn((V, r), g, device, std=1.0 / 16.0, dtype=torch.bfloat16)
-    prev0 = torch.randint(0, V, (B,), generator=g, device=device, dtype=torch.int64).to(torch.int32)
+    t = host_normal((rows, V), seed, 1)
+    rs = _stream(seed, 2)
+    peaked = rs.random(rows) < 0.7
+    hot = rs.integers(0, V, rows)
+    t *= np.where(peaked, np.float32(2.0), np.float32(1.0))[:, None]
+    t[np.arange(rows), hot] += np.where(peaked, np.float32(10.0), np.float32(0.0))
+    target = _t(t.reshape(B, gamma + 1, V), device, torch.bfloat16)
+    del t
+    sig = np.array([0.5 + 1.5 * (j - 1) / max(gamma - 1, 1) for j in range(1, gamma + 1)], dtype=np.float32)
+    noise = host_normal((B, gamma, V), seed, 3)
+    noise *= sig[None, :, None]
+    base = (target[:, :gamma].float() + _t(noise, device)).to(torch.bfloat16)
+    del noise
+    U = _t(host_normal((V, r), seed, 4, std=1.0 / 16.0), device, torch.bfloat16)
+    Wt = _t(host_normal((V, r), seed, 5, std=1.0 / 16.0), device, torch.bfloat16)
+    prev0 = _t(_stream(seed, 6).integers(0, V, B).astype(np.int32), device)
     Tt = torch.full((B,), 0.8, device=device, dtype=torch.float32)
     return Round(f"block_length_g{gamma}", target.contiguous(), base.contiguous(), U, Wt, prev0, Tt,
                  seed=7000 + gamma)
@@ -199,21 +274,26 @@ def stress(B=1024, V=262144, gamma=8, r=256, device="cpu") -> Round:
     (the row maximum copied onto one other random id); backbone = target +
     N(0, 1.5^2) in fp32; bf16 factors; T = 0 for even requests and 1.3 for odd
     ones; verify budgets from the confidence scheduler with the 16-point table."""
-    g = _gen(device, 1234 + 5)
-    target = torch.randn((B, gamma + 1, V), generator=g, device=device, dtype=torch.float32).mul_(8.0)
-    rows = target.view(-1, V)
+    seed = 1234 + 5
+    target = host_normal((B, gamma + 1, V), seed, 1, std=8.0)
+    rows = target.reshape(-1, V)
+    rs = _stream(seed, 2)
     n_tie = max(1, int(math.ceil(0.001 * rows.shape[0])))
-    tie_rows = torch.randperm(rows.shape[0], generator=g, device=device)[:n_tie]
-    tie_cols = torch.randint(0, V, (n_tie,), generator=g, device=device)
-    mx = rows[tie_rows].max(dim=1).values
-    rows[tie_rows, tie_cols] = mx
-    base = target[:, :gamma] + _randn((B, gamma, V), g, device, std=1.5)
-    U = _randn((V, r), g, device, std=1.0 / 16.0, dtype=torch.bfloat16)
-    Wt = _randn((V, r), g, device, std=1.0 / 16.0, dtype=torch.bfloat16)
-    prev0 = torch.randint(0, V, (B,), generator=g, device=device, dtype=torch.int64).to(torch.int32)
+    tie_rows = rs.permutation(rows.shape[0])[:n_tie]
+    tie_cols = rs.integers(0, V, n_tie)
+    rows[tie_rows, tie_cols] = rows[tie_rows].max(axis=1)
+    base = host_normal((B, gamma, V), seed, 3, std=1.5)
+    base += target[:, :gamma]
+    target_t = _t(target, device)
+    del target, rows
+    base_t = _t(base, device)
+    del base
+    U = _t(host_normal((V, r), seed, 4, std=1.0 / 16.0), device, torch.bfloat16)
+    Wt = _t(host_normal((V, r), seed, 5, std=1.0 / 16.0), device, torch.bfloat16)
+    prev0 = _t(_stream(seed, 6).integers(0, V, B).astype(np.int32), device)
     Tt = torch.where(torch.arange(B, device=device) % 2 == 0, 0.0, 1.3).to(torch.float32)
-    rnd = Round(f"stress_B{B}", target.contiguous(), base.contiguous(), U, Wt, prev0, Tt, seed=99)
-    rnd.conf = confidence_scores(B, gamma, g, device)
+    rnd = Round(f"stress_B{B}", target_t, base_t, U, Wt, prev0, Tt, seed=99)
+    rnd.conf = confidence_scores(B, gamma, seed, device)
     rnd.sps_B, rnd.sps_val = sps_table_linear()
     return rnd
 
@@ -233,6 +313,21 @@ def small_random(B, gamma, V, r, device="cpu", seed=0, dtype=torch.float32, fact
     Tt = tv[torch.arange(B, device=device) % len(temps)]
     return Round(f"small_{B}x{gamma}x{V}", target.to(dtype).contiguous(), base.to(dtype).contiguous(),
                  U, Wt, prev0, Tt, seed=seed)
+
+
+def input_fingerprint(rnd: Round) -> np.ndarray:
+    """Weighted float64 sums over strided samples of every input tensor: a cheap
+    check that two runs (on any device) drew the same inputs."""
+
+    def f(t, step):
+        if t is None:
+            return 0.0
+        x = t.detach().reshape(-1)[::step].to(torch.float64)
+        w = torch.arange(1, x.numel() + 1, dtype=torch.float64, device=x.device).remainder(97)
+        return float((x * w).sum())
+
+    return np.array([f(rnd.target, 4099), f(rnd.base, 4097), f(rnd.U, 1031), f(rnd.Wt, 1033),
+                     f(rnd.prev0, 1), f(rnd.temperature, 1), f(rnd.conf, 1)])
 
 
 def to_host(t: Optional[torch.Tensor]) -> Optional[np.ndarray]:

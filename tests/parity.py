@@ -15,6 +15,7 @@ of a large sample.
 
 from __future__ import annotations
 
+import os
 import sys
 from dataclasses import dataclass
 
@@ -135,3 +136,54 @@ def check(rep: Report, name: str, max_flag_frac=1e-4):
     assert not rep.mismatches, rep.mismatches[:5]
     # a single flagged row is allowed in a small sample; beyond that the rate bar applies
     assert rep.flagged_rows <= max(1, max_flag_frac * rep.rows), rep
+
+
+GOLDEN_DIR = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "rounds")
+
+
+def load_golden(name: str):
+    """Whole-batch oracle expectations written by tests/golden/make_round_goldens.py."""
+    path = os.path.join(GOLDEN_DIR, f"{name}.npz")
+    with np.load(path, allow_pickle=False) as z:
+        return {k: z[k] for k in z.files}
+
+
+def compare_golden(rnd: wl.Round, buf: rd.Buffers, gold: dict, name: str):
+    """Every request of a GPU round against the oracle's whole-batch expectations
+    (same bar as ``compare``; requests the oracle flags are excused)."""
+    fp = wl.input_fingerprint(rnd)
+    assert np.allclose(fp, gold["fingerprint"], rtol=1e-9, atol=0), f"{name}: inputs differ from the golden's"
+    h = lambda x: x.detach().cpu().numpy()
+    B, g = rnd.B, rnd.gamma
+    budget = h(buf.budget) if buf.budget is not None else np.full(B, g)
+    if float(gold["sched_min_gap"]) > od.SCHED_FLAG:
+        assert np.array_equal(budget, gold["budget"]), f"{name}: budgets differ"
+    ok = ~gold["flagged"]
+    bad = []
+    draft = h(buf.draft_tokens)
+    out, nacc, nemit = h(buf.out_tokens), h(buf.num_accepted), h(buf.num_emitted)
+    for b in np.nonzero(ok)[0]:
+        if not np.array_equal(draft[b], gold["draft_tokens"][b]):
+            bad.append((int(b), "draft", draft[b].tolist(), gold["draft_tokens"][b].tolist()))
+        elif not np.array_equal(out[b], gold["out_tokens"][b]) or nacc[b] != gold["num_accepted"][b] \
+                or nemit[b] != gold["num_accepted"][b] + 1:
+            bad.append((int(b), "verify", out[b].tolist(), gold["out_tokens"][b].tolist()))
+    assert not bad, f"{name}: {len(bad)} requests differ: {bad[:4]}"
+    T = h(rnd.temperature)
+    s = ok & (T > 0)
+    logq = h(buf.draft_logq).astype(np.float64)[s]
+    lq_ref = gold["draft_logq"][s]
+    assert np.allclose(logq, lq_ref, atol=1e-5, rtol=1e-6), f"{name}: ln q"
+    assert np.allclose(np.exp(logq), np.exp(lq_ref), atol=ATOL_P, rtol=RTOL_P), f"{name}: q"
+    assert np.allclose(h(buf.draft_lse)[s], gold["draft_lse"][s], rtol=1e-6, atol=0), f"{name}: draft lse"
+    if buf.debug_logp_logq is not None:
+        dbg = h(buf.debug_logp_logq)[s]
+        want_p, want_q = gold["logp"][s], gold["logq"][s]
+        tested = ~np.isnan(want_p)   # positions whose accept test ran
+        assert np.allclose(dbg[..., 0][tested], want_p[tested], atol=1e-5, rtol=1e-6), f"{name}: ln p"
+        assert np.allclose(np.exp(dbg[..., 0][tested]), np.exp(want_p[tested]), atol=ATOL_P, rtol=RTOL_P)
+        assert np.allclose(dbg[..., 1][tested], want_q[tested], atol=1e-5, rtol=1e-6), f"{name}: ln q at verify"
+    rows, fl = int(gold["rows"]), int(gold["rows_flagged"])
+    say(f"[{name}] whole batch: requests={B} compared={int(ok.sum())} rows={rows} flagged_rows={fl} "
+        f"verified={int(budget.sum())} accepted={int(nacc.sum())}")
+    assert fl < 1e-4 * rows + 1, f"{name}: flagged rows {fl} of {rows}"

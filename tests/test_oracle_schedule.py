@@ -109,3 +109,37 @@ def test_rejects_bad_tables():
         od.schedule(_conf(2, 2, 0), np.array([4.0, 2.0]), np.array([1.0, 1.0]))
     with pytest.raises(ValueError):
         od.schedule(_conf(2, 2, 0), np.array([4.0]), np.array([1.0]))
+
+
+def test_step_time_hand_computed_non_linear_table():
+    # t = 1/SPS at B = 2, 6, 10 is 1, 3, 11 (slopes 1/2 then 2 per token): below
+    # the first point the first value, linear inside each segment, and beyond the
+    # last point the last segment extended.  Every value below is exact in fp64.
+    Bs = [2.0, 6.0, 10.0]
+    t_tab = [1.0, 3.0, 11.0]
+    want = {0.0: 1.0, 1.0: 1.0, 2.0: 1.0, 4.0: 2.0, 6.0: 3.0, 7.0: 5.0, 8.0: 7.0, 10.0: 11.0,
+            12.0: 15.0, 20.0: 31.0, 1000.0: 1991.0}
+    for N, t in want.items():
+        assert od.step_time(N, Bs, t_tab) == t, N
+    # a plain clamp beyond the table or the first segment's slope would give
+    # 11 / 7 at N = 12; the interpolation inside the table agrees with numpy's
+    for N in np.linspace(2.0, 10.0, 33):
+        assert od.step_time(float(N), Bs, t_tab) == pytest.approx(float(np.interp(N, Bs, t_tab)), rel=1e-15)
+
+
+def test_scheduler_admission_crossing_the_last_table_point():
+    # Two requests, two positions; the table ends at 3 tokens: t(1) = t(2) = 10,
+    # t(3) = 12, so beyond it t(N) = 12 + 2 (N - 3).  Prefix survivals
+    # a = (0.9, 0.72) and (0.5, 0.25), in units of 2^32 of tau:
+    #   tau = 2,    N = 2: (2 + 0.9) t(2) = 29     > 2 t(3) = 24         admit
+    #   tau = 2.9,  N = 3: (2.9 + 0.72) t(3) = 43.44 > 2.9 t(4) = 40.6   admit
+    #   tau = 3.62, N = 4: (3.62 + 0.5) t(4) = 57.68 > 3.62 t(5) = 57.92 fails: stop
+    # (a table clamped at its last value would admit all four candidates).
+    conf = np.array([[0.9, 0.8], [0.5, 0.5]], dtype=np.float32)
+    Bs = np.array([1.0, 2.0, 3.0])
+    sps = 1.0 / np.array([10.0, 10.0, 12.0])
+    res = od.schedule(conf, Bs, sps)
+    assert res.budget.tolist() == [2, 0]
+    assert res.admitted == 2
+    flat = od.schedule(conf, Bs, 1.0 / np.array([10.0, 10.0, 10.0]))
+    assert flat.budget.tolist() == [2, 2]
