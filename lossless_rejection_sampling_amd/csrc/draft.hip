@@ -349,7 +349,9 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const f32x16 (&
       double rmax, rlsum;
       residual_rowstats(a, rq, pos, rmax, rlsum);
       const float c = kLog2e / T;
-      const float kp = (float)((rmax / (double)T + rlsum) * 1.4426950408889634);
+      // p = 2^((z - max) c - ln S log2 e): the difference first (an exact input
+      // value is subtracted), so no term carries an error proportional to max / T
+      const float mz = (float)rmax, kp = (float)(rlsum * 1.4426950408889634);
       const double lse_q = a.draft_lse[(size_t)rq * a.gamma + pos];
       const float kq = (float)((lse_q - (double)ref / (double)T) * 1.4426950408889634);
 #pragma unroll
@@ -357,7 +359,7 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const f32x16 (&
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const float zv = (full || acc_col(tile * kTile, vb, e, half) < a.V) ? z.get(vb, e) : -INFINITY;
-          const float p = __builtin_amdgcn_exp2f(fmaf(zv, c, -kp));
+          const float p = __builtin_amdgcn_exp2f(fmaf(zv - mz, c, -kp));
           const float q = __builtin_amdgcn_exp2f(fmaf(t[vb][e], c, -kq));
           rs += residual_mass(a, p, q);
         }
@@ -971,10 +973,11 @@ __global__ __launch_bounds__(256) void draft_select_schedule(SelectScheduleArgs 
 //    32 backbone-logit rows (64 bytes each, private to the wavefront).  No
 //    register is ever the target of an outstanding load inside the loop, and
 //    every wait is explicit.
-//  * The backbone logits seed the accumulator, so the MFMA chain yields
-//    t = (x - ref) + bias directly, ref being the slot's logit at the tile's
-//    first column (an exact input value).
-//  * Iteration u seeds and issues the MFMAs of stage u+1 interleaved with the
+//  * The accumulator sums the bias alone (it starts at zero, so its roundings
+//    are at the bias's scale); the epilogue forms t = (x - ref) + bias with one
+//    rounding, ref being the slot's logit at the tile's first column (an exact
+//    input value, so x - ref is exact).
+//  * Iteration u issues the MFMAs of stage u+1 interleaved with the
 //    statistics of stage u; the two stages of a tile are merged into one
 //    record; the wait at the end covers only the loads of stage u+2.
 // ---------------------------------------------------------------------------
@@ -1129,21 +1132,27 @@ __global__ __launch_bounds__(512, 1) void gemm_draft_stream(GemmArgs a) {
   const int wbase = WL::at(l32, half);          // operand base: storage row l32, chunk half
   const int xbase = half * 1024 + l32 * 16;     // this lane's first logit chunk in a stage
 
-  // accumulator seed x - ref from the logits of stage slot `slot`; the first
-  // stage of a tile also sets ref (its column 0, held by lane l32 of half 0)
+  // the accumulator of a stage starts at zero (it sums the bias alone, at the
+  // bias's own scale); the first stage of a tile also sets ref (its column 0,
+  // held by lane l32 of half 0)
   auto seed = [&](int slot, bool first, f32x16& acc, float& ref) {
-    const u32x4 w0 = *reinterpret_cast<const u32x4*>(xring + slot * kXStageBytes + xbase);
-    const u32x4 w1 = *reinterpret_cast<const u32x4*>(xring + slot * kXStageBytes + xbase + 512);
     if (first) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(xring + slot * kXStageBytes + xbase);
       float even, odd;
-      row_pair<32>(__uint_as_float(w0[0] << 16), even, odd);
+      row_pair<32>(__uint_as_float(w << 16), even, odd);
       ref = even;
     }
 #pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+  };
+  // this lane's 16 backbone logits of stage slot `slot`
+  auto read_x = [&](int slot, float (&x)[16]) {
+    const u32x4 w0 = *reinterpret_cast<const u32x4*>(xring + slot * kXStageBytes + xbase);
+    const u32x4 w1 = *reinterpret_cast<const u32x4*>(xring + slot * kXStageBytes + xbase + 512);
+#pragma unroll
     for (int e = 0; e < 16; ++e) {
       const uint32_t w = e < 8 ? w0[(e & 7) >> 1] : w1[(e & 7) >> 1];
-      const float xv = (e & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
-      acc[e] = xv - ref;
+      x[e] = (e & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
     }
   };
   // operand of k-step ks: storage row l32, chunk 2 ks + half of the W2 stage in ring slot `slot`
@@ -1181,9 +1190,10 @@ __global__ __launch_bounds__(512, 1) void gemm_draft_stream(GemmArgs a) {
     sum = pair_sum(sum);
   };
 
-  // Iteration u (stage u in ring slot S = u % 4 has its t values in `cur`;
-  // stage u+1 in slot S+1 has landed):
-  //   seed `next` from stage u+1's logits; issue stage u+4 into slot S; run the
+  // Iteration u (stage u in ring slot S = u % 4 has its bias in `cur`; stage
+  // u+1 in slot S+1 has landed):
+  //   take stage u's backbone logits from slot S (t = (x - ref) + bias, one
+  //   rounding); seed `next` for stage u+1; issue stage u+4 into slot S; run the
   //   MFMAs of stage u+1 with the statistics of stage u; on a tile's second
   //   stage (odd u) merge with the first and store the record; wait for stage
   //   u+2, issued in iteration u-2 (or in the prologue), barrier.  The loads
@@ -1196,10 +1206,16 @@ __global__ __launch_bounds__(512, 1) void gemm_draft_stream(GemmArgs a) {
   auto step = [&](auto S_, f32x16& cur, f32x16& next, int u) {
     constexpr int S = decltype(S_)::value;
     constexpr bool second = S & 1;  // stage u is the second half of its tile
+    float x[16];
+    read_x(S, x);
     if (second) seed((S + 1) % kStages, true, next, ref0);   // next tile's first stage sets its ref
     else seed((S + 1) % kStages, false, next, ref0);         // same tile, same ref
+    // slot S is rewritten below: its logits must have reached registers
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     dma_w(u + 4, S);
     dma_x(u + 4, S);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) cur[e] = (x[e] - ref1) + cur[e];
     const int c0 = tile * kTile + (second ? kStageCols : 0);
     if (c0 + kStageCols > V) {  // a ragged stage: columns >= V do not exist
 #pragma unroll
@@ -1310,12 +1326,15 @@ __global__ __launch_bounds__(512, 1) void gemm_residual_coalesced(GemmArgs a) {
   bool valid;
   slot_info<true>(a, sg0 + sl, nslots, rq, pos, prev, valid);
   const bool active = sg0 + (wave & 3) * 32 < nslots;
-  float T = 1.0f, kp = 0.0f;
+  // p = 2^((z - max) c - ln S log2 e): the difference first (max is an exact
+  // input value), so no term carries an error proportional to max / T
+  float T = 1.0f, mz = 0.0f, kp = 0.0f;
   double lse_q = 0.0;
   if (valid) {
     T = effective_temp(a.temperature[rq]);
     const ReqState st = a.req[rq];
-    kp = (float)(((double)st.row_max / (double)T + st.row_logsum) * 1.4426950408889634);
+    mz = (float)st.row_max;
+    kp = (float)(st.row_logsum * 1.4426950408889634);
     lse_q = a.draft_lse[(size_t)rq * a.gamma + pos];
   }
   if (!(T > 0.0f)) T = 1.0f;  // greedy rows never hold a residual draw
@@ -1422,7 +1441,7 @@ __global__ __launch_bounds__(512, 1) void gemm_residual_coalesced(GemmArgs a) {
     float rs = 0.0f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(zv[e], c, -kp));
+      const float p = __builtin_amdgcn_exp2f(fmaf(zv[e] - mz, c, -kp));
       const float q = __builtin_amdgcn_exp2f(fmaf((xv[e] - ref) + acc[e], c, -kq));
       rs += fmaxf(p - q, 0.0f);
     }
@@ -1473,8 +1492,9 @@ __global__ __launch_bounds__(512, 1) void gemm_residual_coalesced(GemmArgs a) {
 // A workgroup of 8 wavefronts owns 256 slots and walks 64-column tiles as two
 // 32-column stages; W2 rows (shared) and each wavefront's backbone and target
 // rows (private) reach LDS by direct loads into three-stage rings, two stages
-// ahead.  Iteration u seeds and issues the MFMAs of stage u+1 (so t = (x -
-// ref) + bias comes out of the accumulator) with the masses of stage u: per
+// ahead.  Iteration u issues the MFMAs of stage u+1 (the accumulator sums the
+// bias alone; t = (x - ref) + bias is formed with one rounding) with the
+// masses of stage u: per
 // column p = exp(z / T - ln Z_p), q = exp((ref + t) / T - lse_q) and
 // max(0, p - q) (the residual draw) or min(p, q) (the acceptance pass).  The
 // residual draw needs each tile's mass; the acceptance pass only the total, so
@@ -1542,7 +1562,9 @@ __global__ __launch_bounds__(512, 1) void gemm_residual_stream(GemmArgs a) {
   __builtin_amdgcn_s_waitcnt(0x0070 | (0xF << 8));  // vmcnt(0)
   const double invT = 1.0 / (double)T;
   const float cT = kLog2e / T;
-  const float kp = (float)((rmax * invT + rlsum) * 1.4426950408889634);
+  // p = 2^((z - max) c - ln S log2 e): the difference first (max is an exact
+  // input value), so no term carries an error proportional to max / T
+  const float mz = (float)rmax, kp = (float)(rlsum * 1.4426950408889634);
   asm volatile("" : "+v"(lse_q));  // every register load is consumed here, before the streams start
   __builtin_amdgcn_sched_barrier(0);
 
@@ -1582,16 +1604,17 @@ __global__ __launch_bounds__(512, 1) void gemm_residual_stream(GemmArgs a) {
     const uint32_t w = e < 8 ? w0[(e & 7) >> 1] : w1[(e & 7) >> 1];
     return (e & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
   };
+  // the accumulator starts at zero (the bias alone, at its own scale); the
+  // first stage of a tile sets ref
   auto seed = [&](int slot, bool first, f32x16& acc, float& ref) {
-    u32x4 w0, w1;
-    read16(slot, 0, w0, w1);
     if (first) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(ring + slot * SLOT_BYTES + xbase);
       float even, odd;
-      row_pair<32>(__uint_as_float(w0[0] << 16), even, odd);
+      row_pair<32>(__uint_as_float(w << 16), even, odd);
       ref = even;
     }
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[e] = unpack(w0, w1, e) - ref;
+    for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
   };
   auto rd = [&](int slot, int ks) {
     return *reinterpret_cast<const bf16x8*>(lds + slot * WL::BYTES + wbase + 32 * WL::RB * ks);
@@ -1609,7 +1632,7 @@ __global__ __launch_bounds__(512, 1) void gemm_residual_stream(GemmArgs a) {
       if (ks * n < 16) {
 #pragma unroll
         for (int j = ks * n; j < ks * n + n; ++j) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(z[j], cT, -kp));
+          const float p = __builtin_amdgcn_exp2f(fmaf(z[j] - mz, cT, -kp));
           const float q = __builtin_amdgcn_exp2f(fmaf(cur[j], cT, -kq));
           m += TV ? fminf(p, q) : fmaxf(p - q, 0.0f);
         }
@@ -1633,23 +1656,28 @@ __global__ __launch_bounds__(512, 1) void gemm_residual_stream(GemmArgs a) {
   wait_vmcnt_c<STAGE_LOADS>();  // stage 1 landed
   barrier_only();
 
-  // Iteration u (stage u in ring slot S = u % 3, its t values in `cur`):
-  //   seed `next` from stage u+1's backbone logits, take stage u's target
-  //   logits into registers, issue stage u+3 into slot S, run stage u+1's
+  // Iteration u (stage u in ring slot S = u % 3, its bias in `cur`):
+  //   take stage u's backbone and target logits into registers, seed `next`,
+  //   issue stage u+3 into slot S, run stage u+1's
   //   MFMAs with stage u's masses, on a tile's second stage store the tile's
   //   mass (residual draw), wait for stage u+2 (issued in iteration u-1, or
   //   the prologue), barrier.
   auto step = [&](auto S_, auto second_, f32x16& cur, f32x16& next, int u) {
     constexpr int S = decltype(S_)::value;
     constexpr bool second = decltype(second_)::value;
-    seed((S + 1) % kRStages, second, next, ref0);
-    u32x4 zw0, zw1;
+    u32x4 xw0, xw1, zw0, zw1;
+    read16(S, 0, xw0, xw1);
     read16(S, kXStageBytes, zw0, zw1);
-    float z[16];
+    seed((S + 1) % kRStages, second, next, ref0);
+    float z[16], x[16];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) z[e] = unpack(zw0, zw1, e);  // waits for the LDS reads: slot S is free
+    for (int e = 0; e < 16; ++e) z[e] = unpack(zw0, zw1, e), x[e] = unpack(xw0, xw1, e);
+    // slot S is rewritten below: its logits must have reached registers
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     dma_w(u + 3, S);
     dma_xz(u + 3, S);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) cur[e] = (x[e] - ref1) + cur[e];  // t = (x - ref) + bias, one rounding
     const int c0 = tile * kTile + (second ? kStageCols : 0);
     if (c0 + kStageCols > V) {  // a ragged stage: columns >= V do not exist
 #pragma unroll

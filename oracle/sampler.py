@@ -112,7 +112,7 @@ def tree_sample(scores, seed, streams, request, position, cond_mass=None):
     g = gumbel(uniforms(seed, streams[2], request, position, th - tl))
     cond = None
     if cond_mass is not None:
-        with np.errstate(divide="ignore", over="ignore"):
+        with np.errstate(divide="ignore", over="ignore", invalid="ignore"):
             cond = np.where(np.isfinite(s[tl:th]), cond_mass[tl:th] / np.exp(s[tl:th]), 0.0)
     e, m_leaf = pick(s[tl:th] - t_lam[t] + g, cond)
     return tl + e, min(m_top, m_mid, m_leaf)
