@@ -193,6 +193,30 @@ int dspark_schedule(const float* conf, const double* sps_B, const double* sps_va
                     void* workspace, void* stream);
 
 /*
+ * dspark_schedule_static -- dspark_schedule that allocates nothing and takes no
+ * workspace, for callers that cannot allocate device memory: code under HIP
+ * stream/graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Arithmetic, limits and budgets are exactly those of dspark_schedule.
+ *
+ *   conf, sps_B, sps_val, n_points, B, gamma, budget: as for dspark_schedule
+ *   status   device uint32 or NULL: the data-error bits of this call (scores
+ *            outside (0, 1), a bad table) are ORed into it, as into the
+ *            workspace's status word (the caller zeroes it); NULL drops them.
+ * Scratch: instead of a workspace the call uses one library-held device array
+ * of 98816 bytes per GPU (the largest scheduler workspace, B * gamma <= 8192),
+ * held until the process ends.  Its counters return to zero at the end of every
+ * call.  All calls on one GPU share it: calls that overlap on one GPU (another
+ * stream, another host thread) race and must not be made.  The call makes no
+ * hipMalloc / hipFree and calls no allocating library routine; the first call
+ * on a device looks up the array's address and enqueues one small clearing
+ * kernel on `stream`.
+ * Errors: DSPARK_EINVAL as for dspark_schedule (B * gamma > 8192 included);
+ * DSPARK_EHIP for a failed lookup or launch.
+ */
+int dspark_schedule_static(const float* conf, const double* sps_B, const double* sps_val, int n_points,
+                           int B, int gamma, int32_t* budget, uint32_t* status, void* stream);
+
+/*
  * dspark_schedule_ex -- dspark_schedule with Sequential Temperature Scaling and
  * a choice of rule ([P2], [P5]).
  *

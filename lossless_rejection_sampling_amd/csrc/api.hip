@@ -358,6 +358,25 @@ int dspark_schedule_ex(const float* conf, const float* tau, const double* sps_B,
   return DSPARK_OK;
 }
 
+int dspark_schedule_static(const float* conf, const double* sps_B, const double* sps_val, int n_points, int B,
+                           int gamma, int32_t* budget, uint32_t* status, void* stream) {
+  // arguments first: nothing is enqueued (not even the first call's clearing) for bad ones
+  int ok = schedule_args_ok(conf, sps_B, sps_val, n_points, B, gamma, DSPARK_SCHED_EARLY_STOP, 0.0, budget);
+  if (ok != DSPARK_OK) return ok;
+  if (dspark_schedule_workspace_bytes(B, gamma) > kStaticScheduleBytes) return DSPARK_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* scratch = nullptr;
+  DSPARK_TRY(static_schedule_scratch(&scratch, s));
+  ScheduleArgs a;
+  ok = schedule_args(conf, nullptr, sps_B, sps_val, n_points, B, gamma, DSPARK_SCHED_EARLY_STOP, 0.0, budget,
+                     scratch, a);
+  if (ok != DSPARK_OK) return ok;
+  if (status) a.status = status;
+  ProfileScope ps(kClsSchedule, s);
+  DSPARK_TRY(launch_schedule(a, s));
+  return DSPARK_OK;
+}
+
 int dspark_schedule(const float* conf, const double* sps_B, const double* sps_val, int n_points,
                     int B, int gamma, int32_t* budget, void* workspace, void* stream) {
   return dspark_schedule_ex(conf, nullptr, sps_B, sps_val, n_points, B, gamma, DSPARK_SCHED_EARLY_STOP, 0.0,

@@ -178,6 +178,14 @@ struct ScheduleArgs {
 };
 
 hipError_t launch_schedule(const ScheduleArgs& a, hipStream_t s);
+
+// The library-held scratch of dspark_schedule_static: the scheduler's workspace
+// layout (header, ranks, Theta) at its largest size, B gamma = 8192.
+constexpr size_t kStaticScheduleBytes = 256 + 8192 * 4 + 65792;
+// Device address of that scratch on the current device (looked up once per
+// device); the first call on a device also enqueues, on `s`, the clearing of
+// its header words.
+hipError_t static_schedule_scratch(void** ptr, hipStream_t s);
 int schedule_groups(const ScheduleArgs& a);        // workgroups of one scheduler launch
 size_t schedule_lds_bytes(const ScheduleArgs& a);  // its dynamic LDS
 

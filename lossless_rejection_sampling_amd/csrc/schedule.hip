@@ -22,6 +22,9 @@
 //      counter) finds the cut (first failure, or the first largest Theta), sets
 //      budget[b] = number of b's candidates ranked before it, and resets the
 //      counter and the failure word.
+#include <map>
+#include <mutex>
+
 #include "schedule_body.hpp"
 
 namespace dspark {
@@ -41,6 +44,45 @@ int schedule_groups(const ScheduleArgs& a) {
 
 size_t schedule_lds_bytes(const ScheduleArgs& a) {
   return (size_t)((a.B * a.gamma + 1) & ~1) * 8 + (size_t)a.n_points * 16;
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of dspark_schedule_static, for callers that cannot allocate device
+// memory: one array per GPU the library runs on, held until the process ends.
+// Host code never passes `scratch` itself to a kernel (on the host that name is
+// a stand-in, not a device address): it looks up the array's device address
+// once per device with hipGetSymbolAddress and uses that.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[kStaticScheduleBytes];
+
+__global__ void clear_header_kernel(uint32_t* words, int n) {
+  if ((int)threadIdx.x < n) words[threadIdx.x] = 0u;
+}
+
+hipError_t static_schedule_scratch(void** ptr, hipStream_t s) {
+  static std::mutex mu;
+  static std::map<int, void*> addr;  // device -> device address of `scratch`
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> g(mu);
+  auto it = addr.find(dev);
+  if (it != addr.end()) {
+    *ptr = it->second;
+    return hipSuccess;
+  }
+  void* p = nullptr;
+  e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  // the header words (status, ticket, first failure, ...) start at zero; every
+  // call leaves its counters at zero again.  A kernel, not a memset, so that a
+  // first call made under stream capture records no memset node.
+  clear_header_kernel<<<1, 64, 0, s>>>(static_cast<uint32_t*>(p), 64);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  addr.emplace(dev, p);
+  *ptr = p;
+  return hipSuccess;
 }
 
 hipError_t launch_schedule(const ScheduleArgs& a, hipStream_t s) {

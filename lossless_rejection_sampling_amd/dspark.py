@@ -48,6 +48,7 @@ _SIG = {
     "dspark_draft_schedule": (_I, [_P, _I, _P, _P, _I, _I, _P, _P, ctypes.c_uint64, _P, _I, _I, _I, _I, _P, _P,
                                    _P, _P, _P, _P, _P, _I, _I, ctypes.c_double, _P, _P, _P]),
     "dspark_schedule": (_I, [_P, _P, _P, _I, _I, _I, _P, _P, _P]),
+    "dspark_schedule_static": (_I, [_P, _P, _P, _I, _I, _I, _P, _P, _P]),
     "dspark_schedule_ex": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_double, _P, _P, _P]),
     "dspark_verify": (_I, [_P, _P, _I, _P, _P, _I, _I, _P, _P, _P, _P, _P, _P, ctypes.c_uint64, _P,
                            _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]),
@@ -204,6 +205,17 @@ def dspark_schedule(conf, sps_B, sps_val, budget, workspace, stream=None):
         _dev(sps_val, "sps_val", torch.float64), int(sps_B.numel()), B, gamma,
         _dev(budget, "budget", torch.int32), _dev(workspace, "workspace", torch.uint8), _stream(stream))
     _check("dspark_schedule", rc)
+
+
+def dspark_schedule_static(conf, sps_B, sps_val, budget, status=None, stream=None):
+    """dspark_schedule on the library's own scratch (no workspace, no allocation);
+    status: optional device uint32 [1] that receives the data-error bits."""
+    B, gamma = conf.shape
+    rc = lib().dspark_schedule_static(
+        _dev(conf, "conf", torch.float32), _dev(sps_B, "sps_B", torch.float64),
+        _dev(sps_val, "sps_val", torch.float64), int(sps_B.numel()), B, gamma,
+        _dev(budget, "budget", torch.int32), _dev(status, "status", optional=True), _stream(stream))
+    _check("dspark_schedule_static", rc)
 
 
 def dspark_schedule_ex(conf, tau, sps_B, sps_val, rule, param, budget, workspace, stream=None):
