@@ -42,6 +42,9 @@ def parse():
     p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--minimal", action="store_true",
+                   help="the timed rounds only (no reference rates, extras, per-round distribution or CPU "
+                        "baseline): for profiler runs")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain device copy of known size (counter calibration) and exit")
@@ -174,7 +177,7 @@ def main():
 
     # per-round distribution, after the timed region: ROUND_REPS rounds, each
     # between HIP events on the stream the rounds run on
-    round_ms = round_distribution(step, args.steps)
+    round_ms = None if args.minimal else round_distribution(step, args.steps)
 
     budgets = bufs[0].budget.cpu().numpy()
     verified = int(budgets.sum())
@@ -222,16 +225,19 @@ def main():
     if "overhead_bytes" in a:
         roof["overhead_bytes"] = a["overhead_bytes"]
     # the same achieved rate against what this device reaches in plain kernels
-    peaks = measure_peaks()
-    roof["measured_peak"] = peaks
-    roof["frac_of_measured"] = roof["achieved"] / (peaks["stream_read_GB_s"] if roof["unit"] == "GB/s"
-                                                   else peaks["mfma_bf16_TFLOP_s"])
+    if not args.minimal:
+        peaks = measure_peaks()
+        roof["measured_peak"] = peaks
+        roof["frac_of_measured"] = roof["achieved"] / (peaks["stream_read_GB_s"] if roof["unit"] == "GB/s"
+                                                       else peaks["mfma_bf16_TFLOP_s"])
 
-    extras = measure_extras(rounds[0], bufs[0])
-    extras["full_budget"] = full_budget_round(rounds, args.steps)
+    extras = None
+    if not args.minimal:
+        extras = measure_extras(rounds[0], bufs[0])
+        extras["full_budget"] = full_budget_round(rounds, args.steps)
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.minimal:
         cpu = cpu_baseline(base_round, budgets, args.cpu_seconds)
 
     line = {

@@ -105,9 +105,9 @@ def report(bench_fetch, bench_write, copy_fetch, copy_write, kernel, cls, comman
         "",
         "```",
         f"rocprofv3 --pmc FETCH_SIZE -d {_run_dir(bench_fetch)} -o run --output-format csv -- "
-        "python3 /root/repo/bench.py --steps 2 --warmup 1 --no-cpu-baseline",
+        "python3 /root/repo/bench.py --steps 2 --warmup 1 --minimal",
         f"rocprofv3 --pmc WRITE_SIZE -d {_run_dir(bench_write)} -o run --output-format csv -- "
-        "python3 /root/repo/bench.py --steps 2 --warmup 1 --no-cpu-baseline",
+        "python3 /root/repo/bench.py --steps 2 --warmup 1 --minimal",
         f"rocprofv3 --pmc FETCH_SIZE -d {_run_dir(copy_fetch)} -o run --output-format csv -- "
         "python3 /root/repo/bench.py --calibrate-copy",
         f"rocprofv3 --pmc WRITE_SIZE -d {_run_dir(copy_write)} -o run --output-format csv -- "
@@ -208,7 +208,7 @@ def mfma_report(path: str, kernel: str, cls: str, flops_per_launch: float) -> st
         "",
         "```",
         f"rocprofv3 --pmc {' '.join(MFMA_COUNTERS)} -d {_run_dir(path)} -o run --output-format csv -- "
-        "python3 /root/repo/bench.py --steps 2 --warmup 1 --no-cpu-baseline",
+        "python3 /root/repo/bench.py --steps 2 --warmup 1 --minimal",
         f"python3 -m lossless_rejection_sampling_amd.counters mfma {path} {kernel} {cls} {flops_per_launch:.0f}",
         "```",
         "",
@@ -221,10 +221,12 @@ def mfma_report(path: str, kernel: str, cls: str, flops_per_launch: float) -> st
         f"| raw means: SQ_VALU_MFMA_BUSY_CYCLES, SQ_BUSY_CYCLES, GRBM_GUI_ACTIVE | "
         f"{mean('SQ_VALU_MFMA_BUSY_CYCLES'):.0f}, {mean('SQ_BUSY_CYCLES'):.0f}, {mean('GRBM_GUI_ACTIVE'):.0f} |",
         "",
-        "The kernel is bound by the memory streams: its arithmetic intensity, about 120 flop/byte, is below the "
-        "312 flop/byte ridge of 2.5 PFLOP/s over 8 TB/s.  The executed flops exceed the algorithmic ones by "
-        f"{flops / flops_per_launch - 1:.1%}: every workgroup also runs the MFMAs of the one 32-column stage after "
-        "its last (the loop issues the same work every iteration; that stage's results are discarded).",
+        "The kernel is bound by the memory streams: its arithmetic intensity is about 213 flop/byte with W2 "
+        "counted once per round (19.9 GFLOP over 93.5 MB a step) and 128 flop/byte with W2 counted at every "
+        "step, both below the 312 flop/byte ridge of 2.5 PFLOP/s over 8 TB/s.  The executed flops exceed the "
+        f"algorithmic ones by {flops / flops_per_launch - 1:.1%}: every workgroup also runs the MFMAs of the one "
+        "32-column stage after its last (the loop issues the same work every iteration; that stage's results "
+        "are discarded).",
         "",
     ]
     return "\n".join(lines)
