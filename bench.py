@@ -90,6 +90,8 @@ def algorithmic(rnd, budgets, emitted, rejected):
                    (V r / gamma per step: the factor is the same at every block
                    position), the U rows of the previous tokens (B r); the
                    kernel's own tile records are overhead, reported apart;
+      draft round  the resident kernel (every position in one launch): gamma
+                   draft steps' rows and W2 once;
       verification target rows 0..n_b of request b (sum_b (n_b + 1) rows = the
                    emitted count: the rows up to the first rejection);
       residual     for every rejected request one target and one backbone row,
@@ -102,6 +104,8 @@ def algorithmic(rnd, budgets, emitted, rejected):
     return {
         "draft_gemm": dict(bytes=B * V * es + V * r * fs / g + B * r * fs,
                            overhead_bytes=B * n_tiles * 16, flops=2.0 * B * r * V, per="draft step"),
+        "draft_round": dict(bytes=g * (B * V * es + B * r * fs) + V * r * fs,
+                            overhead_bytes=g * B * n_tiles * 16, flops=2.0 * B * r * V * g, per="draft round"),
         "row_stats": dict(bytes=rows * V * es, flops=0.0, per="verify"),
         "residual_gemm": dict(bytes=rejected * 2 * V * es + V * r * fs, flops=2.0 * rejected * r * V,
                               per="verify"),
@@ -235,6 +239,7 @@ def main():
     if not args.minimal:
         extras = measure_extras(rounds[0], bufs[0])
         extras["full_budget"] = full_budget_round(rounds, args.steps)
+        extras["resident_draft"] = resident_draft_round(rounds, bufs, args.steps)
 
     cpu = None
     if not args.no_cpu_baseline and not args.minimal:
@@ -266,6 +271,40 @@ def main():
         "extras": extras,
     }
     print(json.dumps(line), flush=True)
+
+
+def resident_draft_round(rounds, bufs, steps):
+    """The same headline rounds with the draft round as one resident launch (W2
+    held on chip across the positions; dspark_set_draft_path): ms per round and
+    the resident kernel's time (events recorded around its cooperative launch,
+    so they include its dispatch), beside the per-position default."""
+    import torch
+
+    from lossless_rejection_sampling_amd import dspark as ds
+    from lossless_rejection_sampling_amd import round as rd
+
+    prev = ds.dspark_set_draft_path(ds.DSPARK_DRAFT_RESIDENT)
+    try:
+        step = lambda i: rd.run_round(rounds[i % N_SETS], bufs[i % N_SETS])
+        for i in range(3):
+            step(i)
+        torch.cuda.synchronize()
+        cls = ds.KERNEL_CLASSES["draft_round"]
+        ds.dspark_profile_enable(cls, True)
+        for i in range(N_SETS * 2):
+            step(i)
+        torch.cuda.synchronize()
+        n, kms = ds.dspark_profile_read(cls)
+        ds.dspark_profile_enable(cls, False)
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step(i)
+        torch.cuda.synchronize()
+        sec = (time.perf_counter() - t0) / steps
+        assert ds.dspark_status(bufs[0].workspace) == ds.DSPARK_OK
+    finally:
+        ds.dspark_set_draft_path(prev)
+    return {"ms_per_step": sec * 1e3, "draft_round_us": 1e3 * kms / max(n, 1), "launches_timed": n}
 
 
 def full_budget_round(rounds, steps):

@@ -99,6 +99,13 @@ enum dspark_schedule_rule {
   DSPARK_SCHED_THRESHOLD = 3   /* baseline: verify while the score exceeds param */
 };
 
+/* Implementations of the draft round (dspark_set_draft_path). */
+enum dspark_draft_path {
+  DSPARK_DRAFT_PER_POSITION = 0, /* one contraction and one draw launch per position (default) */
+  DSPARK_DRAFT_RESIDENT = 1      /* one cooperative launch for the whole round, W2 held on chip,
+                                    where it fits (else per position) */
+};
+
 /* Version of this ABI (DSPARK_ABI_VERSION of the built library). */
 int dspark_abi_version(void);
 
@@ -129,6 +136,15 @@ size_t dspark_schedule_workspace_bytes(int B, int gamma);
  */
 int dspark_pack_w2(const void* W, int factor_dtype, int V, int r, void* W_packed, void* stream);
 
+/* Selects the implementation dspark_draft_round and dspark_draft_schedule use
+ * from now on, process-wide (a dspark_draft_path value); returns the previous
+ * one, or DSPARK_EINVAL for an unknown value.  Both implementations compute
+ * the same draft round ([P1] eq. p_k) with the same arithmetic.  On MI355X the
+ * per-position launches are the faster ones at the sizes measured (the
+ * resident round's two device-wide waits per position cost more than the
+ * kernel boundaries they replace), so they are the default. */
+int dspark_set_draft_path(int path);
+
 /*
  * dspark_draft_round -- [P1] eq. p_k with the Markov head.
  *
@@ -156,6 +172,12 @@ int dspark_pack_w2(const void* W, int factor_dtype, int V, int r, void* W_packed
  *   draft_lse    [B, gamma] float64 ln sum_v exp(d_k(v) / T_b) (for greedy
  *                                   requests: max_v d_k(v)); kept in fp64 so
  *                                   that dspark_verify can rebuild q_k exactly
+ * The round runs as one contraction launch and one draw launch per position.
+ * After dspark_set_draft_path(DSPARK_DRAFT_RESIDENT) it runs instead, where it
+ * fits (bf16 logits and factors, r = 256, V a multiple of 8 with at most
+ * 20 x 64 columns per CU: V <= 163840 on a 256-CU MI355X, B <= 2048), as one
+ * cooperative launch that keeps W2 in registers across the gamma positions
+ * (every CU takes part).  Both give the same results, bit for bit.
  */
 int dspark_draft_round(const void* base_logits, int logits_dtype,
                        const void* U, const void* W, int factor_dtype, int w_layout,
@@ -344,7 +366,9 @@ int dspark_status(void* workspace, void* stream);
  * ms, then clears the record.  Classes: 0 draft GEMM + softmax statistics, 1 draft
  * sample, 2 verification pass (target row statistics up to the first
  * rejection, accept tests, bonus and greedy tokens), 3 unused, 4 residual
- * statistics, 5 residual sample, 6 scheduler, 7 acceptance-pass GEMM. */
+ * statistics, 5 residual sample, 6 scheduler, 7 acceptance-pass GEMM, 8 the
+ * resident draft round (a cooperative launch: its events are recorded on the
+ * stream around the launch, so they include its dispatch). */
 int dspark_profile_enable(int kernel_class, int enabled);
 int dspark_profile_read(int kernel_class, int* launches, double* total_ms);
 

@@ -24,6 +24,12 @@ HIPCC_FLAGS = [
 ]
 
 
+# Per-source flags.  draft.hip: MFMA accumulators in vector registers, so that
+# the resident draft kernel has all 256 accumulation registers for its W2
+# operands (the MFMAs read them there).
+SOURCE_FLAGS = {"draft.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if cand and os.path.exists(cand):
@@ -39,7 +45,8 @@ def build(verbose: bool = False) -> str:
 
     def compile_one(src):
         obj = os.path.join(obj_dir, os.path.splitext(src)[0] + ".o")
-        cmd = [cc, *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *HIPCC_FLAGS, *SOURCE_FLAGS.get(src, []), "-I", INCLUDE, "-I", CSRC, "-c",
+               os.path.join(CSRC, src), "-o", obj]
         res = subprocess.run(cmd, capture_output=True, text=True)
         if res.returncode != 0:
             raise RuntimeError(f"hipcc failed on {src}:\n{res.stdout}\n{res.stderr}")

@@ -3,6 +3,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
 #include <map>
 #include <mutex>
 #include <vector>
@@ -18,12 +19,13 @@ inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // Workspace: [header | scheduler ranks | tile stats (B + 1 rows) | block stats | request state | slot list |
 // residual tile mass | U rows of the last drawn tokens | acceptance pass: row
-// statistics, row argmax, tile masses | lazy verification: row counters, request progress].  Header words: 0 status, 1 residual slot count, 2 scheduler
+// statistics, row argmax, tile masses | lazy verification: row counters, request progress |
+// resident draft round: phase flags, exit counter].  Header words: 0 status, 1 residual slot count, 2 scheduler
 // ticket, 3 scheduler first failure.  The header and the scheduler ranks are all
 // that dspark_schedule touches, at offsets that do not depend on V and r.
 constexpr size_t kHeaderBytes = 256;
 struct Layout {
-  size_t header, sched, tstat, bstat, req, slots, rsum, hrows, rowinfo, rowarg, tmass, vsync, total;
+  size_t header, sched, tstat, bstat, req, slots, rsum, hrows, rowinfo, rowarg, tmass, vsync, grid, total;
   int n_tiles, n_blk;
 };
 
@@ -67,6 +69,8 @@ Layout layout(int B, int gamma, int V, int r) {
   off = align_up(off + (size_t)B * gamma * L.n_tiles * sizeof(float));
   L.vsync = off;  // lazy verification: blocks done per target row, then the decided positions per request
   off = align_up(off + ((size_t)B * (gamma + 1) + B) * sizeof(uint32_t));
+  L.grid = off;  // resident draft round: phase flags of the workgroups and the exit counter
+  off = align_up(off + (size_t)kResidentGridWords * sizeof(uint32_t));
   L.total = off;
   return L;
 }
@@ -230,8 +234,16 @@ int draft_args_ok(const void* base_logits, int logits_dtype, const void* U, cons
   return DSPARK_OK;
 }
 
-// The draft round on validated arguments; with `sched`, the scheduler too: in
-// the launch of the last draw when that draw uses the fast kernel, else after it.
+// Which implementation of the draft round runs (dspark_set_draft_path).
+std::atomic<int>& draft_path() {
+  static std::atomic<int> p{DSPARK_DRAFT_PER_POSITION};
+  return p;
+}
+
+// The draft round on validated arguments; with `sched`, the scheduler too: one
+// GEMM and one draw per position, the scheduler in the launch of the last draw
+// when that draw uses the fast kernel, else after it.  On the resident path
+// (when it fits) one launch runs the whole round and the scheduler follows it.
 int draft_round(const void* base_logits, int logits_dtype, const void* U, const void* W, int factor_dtype,
                 const int32_t* prev0, const float* temperature, uint64_t seed, const int32_t* pos_offset, int B,
                 int gamma, int V, int r, int32_t* draft_tokens, float* draft_logq, double* draft_lse,
@@ -253,6 +265,23 @@ int draft_round(const void* base_logits, int logits_dtype, const void* U, const 
   d.draft = draft_tokens, d.logq = draft_logq, d.lse = draft_lse, d.status = status;
   // the streaming GEMM takes the U rows of the previous tokens from this table
   // (filled by the draw of the previous position) instead of gathering them
+  if (draft_path().load(std::memory_order_relaxed) == DSPARK_DRAFT_RESIDENT) {
+    // the whole round in one launch, W2 kept on chip
+    hipError_t e;
+    {
+      ProfileScope ps(kClsDraftRound, s);
+      e = launch_draft_resident(d, logits_dtype, factor_dtype, at<uint32_t>(workspace, L.grid), s);
+    }
+    if (e == hipSuccess) {
+      if (sched) {
+        ProfileScope ps(kClsSchedule, s);
+        DSPARK_TRY(launch_schedule(*sched, s));
+      }
+      return DSPARK_OK;
+    }
+    if (e != hipErrorNotSupported) return DSPARK_EHIP;
+  }
+
   const bool table = factor_dtype == DSPARK_BF16 && (r == 128 || r == 256);
   d.hrows = table ? at<void>(workspace, L.hrows) : nullptr;
 
@@ -315,6 +344,11 @@ int dspark_pack_w2(const void* W, int factor_dtype, int V, int r, void* W_packed
   const int es = factor_dtype == DSPARK_BF16 ? 2 : 4;
   DSPARK_TRY(launch_pack_w2(W, W_packed, es, V, r, static_cast<hipStream_t>(stream)));
   return DSPARK_OK;
+}
+
+int dspark_set_draft_path(int path) {
+  if (path != DSPARK_DRAFT_PER_POSITION && path != DSPARK_DRAFT_RESIDENT) return DSPARK_EINVAL;
+  return draft_path().exchange(path);
 }
 
 int dspark_draft_round(const void* base_logits, int logits_dtype, const void* U, const void* W,

@@ -20,9 +20,11 @@ enum : uint32_t {
   kFinalTop = 4, kFinalMid = 5, kFinalLeaf = 6,
 };
 
-// Bits of the workspace status word.
+// Bits of the workspace status word.  kStall: a device-wide wait of the
+// resident draft round passed its time bound (its results are then unspecified).
 enum : uint32_t {
   kBadPrev = 1u, kBadDraft = 2u, kBadBudget = 4u, kBadTemp = 8u, kBadConf = 16u, kBadTable = 32u,
+  kStall = 64u,
 };
 
 // Softmax statistics of one 64-column tile of one draft row:

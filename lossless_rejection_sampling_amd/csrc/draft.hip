@@ -789,16 +789,51 @@ __global__ __launch_bounds__(256) void draft_select_kernel(DraftSelectArgs a) {
 //      wavefronts), the column drawn, and U[x] copied for the next position.
 // The arithmetic of every value that decides a draw is that of
 // draft_select_kernel.
-template <typename TL, typename TF>
-__device__ __forceinline__ void draft_select_block(const DraftSelectArgs& a, int b) {
-  constexpr int kMaxTiles = kTilesPerBlock * 64;
-  __shared__ double s_d[kMaxTiles];     // ref + mx of every tile
-  __shared__ float s_sum[kMaxTiles];    // exp-sum of every tile
-  __shared__ double s_g[3][64];         // Gumbel values: block, tile, column level
-  __shared__ double s_bm[64], s_part[4][64];
-  __shared__ float s_be[64];
-  __shared__ double s_val[4], s_lse;
-  __shared__ int s_idx[4], s_tile;
+constexpr int kDrawMaxTiles = kTilesPerBlock * 64;
+struct DrawShared {
+  double d[kDrawMaxTiles];   // ref + mx of every tile
+  float sum[kDrawMaxTiles];  // exp-sum of every tile
+  double g[3][64];           // Gumbel values: block, tile, column level
+  double bm[64], part[4][64];
+  float be[64];
+  double val[4], lse;
+  int idx[4], tile;
+};
+
+// Accesses to data that other workgroups of the same launch write or read
+// (agent-scope relaxed atomics: coherent across the XCDs' L2 caches).
+__device__ __forceinline__ float4 load_rec_coherent(const TileStat* p) {
+  const uint64_t* q = reinterpret_cast<const uint64_t*>(p);
+  const uint64_t lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return make_float4(__uint_as_float((uint32_t)lo), __uint_as_float((uint32_t)(lo >> 32)),
+                     __uint_as_float((uint32_t)hi), __uint_as_float((uint32_t)(hi >> 32)));
+}
+__device__ __forceinline__ void store_rec_coherent(TileStat* p, float ref, float mx, float sum) {
+  uint64_t* q = reinterpret_cast<uint64_t*>(p);
+  __hip_atomic_store(q, (uint64_t)__float_as_uint(ref) | ((uint64_t)__float_as_uint(mx) << 32), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(q + 1, (uint64_t)__float_as_uint(sum), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int load_coherent(const int32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// COHERENT: the tile records and the previous position's token were written by
+// other workgroups of the same launch, and the token drawn here is read by them.
+template <typename TL, typename TF, bool COHERENT = false>
+__device__ __forceinline__ void draft_select_block(const DraftSelectArgs& a, int b, DrawShared& sh) {
+
+  auto& s_d = sh.d;
+  auto& s_sum = sh.sum;
+  auto& s_g = sh.g;
+  auto& s_bm = sh.bm;
+  auto& s_part = sh.part;
+  auto& s_be = sh.be;
+  auto& s_val = sh.val;
+  auto& s_lse = sh.lse;
+  auto& s_idx = sh.idx;
+  auto& s_tile = sh.tile;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int V = a.V, r = a.r, gamma = a.gamma, nt = a.n_tiles, pos = a.pos;
   const int nblk = (nt + kTilesPerBlock - 1) / kTilesPerBlock;
@@ -806,13 +841,18 @@ __device__ __forceinline__ void draft_select_block(const DraftSelectArgs& a, int
 
   // 1. every load of the draw's first phase at once
   const float T_raw = a.temperature[b];
-  const int prev_raw = pos == 0 ? a.prev0[b] : a.draft[(size_t)b * gamma + pos - 1];
+  const int prev_raw = pos == 0                 ? a.prev0[b]
+                       : COHERENT               ? load_coherent(a.draft + (size_t)b * gamma + pos - 1)
+                                                : a.draft[(size_t)b * gamma + pos - 1];
   const uint32_t off = a.pos_offset ? (uint32_t)a.pos_offset[b] : 0u;
   float4 rec[4][4];  // tiles 1024 q + 4 tid + k (unconditional loads, so that they all go out at once)
 #pragma unroll
   for (int q = 0; q < 4; ++q)
 #pragma unroll
-    for (int k = 0; k < 4; ++k) rec[q][k] = *reinterpret_cast<const float4*>(ts + min(1024 * q + 4 * tid + k, nt - 1));
+    for (int k = 0; k < 4; ++k) {
+      const TileStat* p = ts + min(1024 * q + 4 * tid + k, nt - 1);
+      rec[q][k] = COHERENT ? load_rec_coherent(p) : *reinterpret_cast<const float4*>(p);
+    }
 #pragma unroll
   for (int q = 0; q < 4; ++q)
 #pragma unroll
@@ -924,7 +964,10 @@ __device__ __forceinline__ void draft_select_block(const DraftSelectArgs& a, int
     const int x = index_or(vi, min(V, (tile + 1) * kTile), tile * kTile);
     const double sx = __shfl(sv, x - tile * kTile);
     if (lane == 0) {
-      a.draft[(size_t)b * gamma + pos] = x;
+      if (COHERENT)
+        __hip_atomic_store(a.draft + (size_t)b * gamma + pos, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else
+        a.draft[(size_t)b * gamma + pos] = x;
       a.logq[(size_t)b * gamma + pos] = Tf > 0.0f ? (float)(sx - lse) : 0.0f;
       a.lse[(size_t)b * gamma + pos] = Tf > 0.0f ? lse : sx;
     }
@@ -939,7 +982,8 @@ __device__ __forceinline__ void draft_select_block(const DraftSelectArgs& a, int
 
 template <typename TL, typename TF>
 __global__ __launch_bounds__(256) void draft_select_fast(DraftSelectArgs a) {
-  draft_select_block<TL, TF>(a, blockIdx.x);
+  __shared__ DrawShared sh;
+  draft_select_block<TL, TF>(a, blockIdx.x, sh);
 }
 
 // The last draw of a round and the scheduler (independent of each other, both
@@ -953,7 +997,8 @@ struct SelectScheduleArgs {
 template <typename TL, typename TF>
 __global__ __launch_bounds__(256) void draft_select_schedule(SelectScheduleArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  if ((int)blockIdx.x < a.d.B) draft_select_block<TL, TF>(a.d, blockIdx.x);
+  __shared__ DrawShared sh;
+  if ((int)blockIdx.x < a.d.B) draft_select_block<TL, TF>(a.d, blockIdx.x, sh);
   else schedule_block(a.s, (int)blockIdx.x - a.d.B, (int)gridDim.x - a.d.B, smem);
 }
 
@@ -1268,6 +1313,356 @@ hipError_t launch_draft_stream(const GemmArgs& a, hipStream_t s) {
   const int wg_x = max(1, min(a.n_tiles, max_wg / groups));
   launch(&gemm_draft_stream<R>, dim3(wg_x, groups), 512, lds, s, a);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Resident draft round (bf16 logits, bf16 factors, r = 256): one cooperative
+// launch of one workgroup per CU runs every block position of the round, so
+// that W2 crosses the memory system once per round instead of once per
+// position.
+//
+//  * Ownership.  Workgroup c owns the contiguous tiles [c nt / G, (c+1) nt / G)
+//    for the whole round; their 2 x (tiles) 32-column stages are split into
+//    contiguous runs over the 4 wavefronts (one per SIMD, 512 registers each),
+//    at most kResStagesPerWave = 5 a wavefront.  A wavefront's W2 stages stay
+//    in registers (AGPRs and VGPRs) as MFMA A operands: 5 x 16 k-steps x 4 =
+//    320 registers; MFMA row i of a stage stands for column col_of_row(i), as
+//    in the streaming kernel, so a lane's 16 accumulators are 16 consecutive
+//    columns of its slot.
+//  * A position.  Slot groups of 32 requests in turn: the U rows of the group
+//    (gathered through the previous tokens) and each wavefront's backbone rows
+//    of its stages arrive in LDS by direct loads two groups ahead; per stage
+//    16 MFMAs with the U rows as B operand, then the tile statistics exactly as
+//    in the streaming kernel (t = (x - ref) + bias, max, exp2-sum).  Stage
+//    statistics meet in LDS, where the workgroup merges the two stages of each
+//    tile into the tile's record.
+//  * Between phases.  The records of a position (all workgroups) feed the
+//    draws; the tokens drawn feed the next position's gather.  Both cross
+//    workgroups as agent-scope relaxed atomics (coherent across the XCDs' L2
+//    caches without write-back or invalidation of the caches), and each phase
+//    ends with a device-wide wait: every wavefront waits for its own stores
+//    (vmcnt(0)), the workgroup raises its flag to the phase number, and one
+//    wavefront polls all flags.  The poll is bounded in time; when the bound
+//    passes (only if the workgroups were not all resident) the kStall bit is
+//    set and the kernel runs on to its end.  The last workgroup out resets the
+//    flags, so they are zero between calls.
+//  * The draw of request b runs in workgroup b mod G with draft_select_block's
+//    arithmetic, so the round's results are those of the per-position launches.
+// ---------------------------------------------------------------------------
+constexpr int kResWaves = 4;
+constexpr int kResStagesPerWave = 5;  // W2 stages (32 columns x 256) held in registers per wavefront
+constexpr int kResMaxB = 2048;        // requests (their tokens and temperatures live in LDS)
+constexpr int kResMaxGrid = 1024;     // workgroups (phase flags in the workspace)
+// Backbone rows of a slot group: the workgroup's 32 rows x (8 x tiles) 16-byte
+// chunks, row-major with rows padded to an odd number of chunks (so that the
+// reads of 16 consecutive rows at one column fall in distinct banks), loaded by
+// row-contiguous direct loads (each 1 KB instruction covers one or two rows).
+constexpr int kResXInstr = 11;  // direct loads per wavefront and slot group: 4 x 11 KB >= 32 x 81 chunks
+constexpr int kResXBufBytes = kResWaves * kResXInstr * 1024;
+constexpr int kResRingBytes = 2 * kResXBufBytes;  // two slot groups
+
+struct ResidentGemmShared {
+  uint4 urows[2][32 * 32];                          // U rows of two slot groups, 16-byte chunks swizzled
+  float2 st[2][kResWaves * kResStagesPerWave + 1][32];  // (max, exp-sum) per stage and slot; the last row is a sink
+  float ref[2][2 * kResStagesPerWave + 1][32];         // tile reference logit per tile and slot; last row a sink
+  int32_t tok[kResMaxB];                             // previous token of every request
+};
+constexpr size_t kResUnionBytes =
+    sizeof(ResidentGemmShared) > sizeof(DrawShared) ? sizeof(ResidentGemmShared) : sizeof(DrawShared);
+constexpr size_t kResLdsBytes = kResRingBytes + ((kResUnionBytes + 15) & ~(size_t)15) + kResMaxB * sizeof(float);
+
+// Eight bf16 -inf values: the backbone chunks past V load this instead, so the
+// columns that do not exist enter the statistics as t = -inf with no masking.
+__device__ const uint4 kNegInfChunk = {0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u};
+
+struct ResidentArgs {
+  DraftSelectArgs d;
+  uint32_t* flags;      // [gridDim.x] phase reached by each workgroup (zero between calls)
+  uint32_t* exits;      // workgroups finished (zero between calls)
+  uint64_t spin_limit;  // bound of a device-wide wait, in s_memrealtime ticks (100 MHz)
+};
+
+// LDS stores written as instructions of their own: the compiler would otherwise
+// wait for every direct-to-LDS load in flight (vmcnt(0)) before a store that it
+// cannot prove disjoint from their targets.  Only for LDS that no direct load
+// writes; completion is covered by the caller's lgkmcnt wait.
+__device__ __forceinline__ void lds_store_f32x2(float2* p, float x, float y) {
+  const uint32_t a = (uint32_t)reinterpret_cast<uintptr_t>(p);
+  asm volatile("ds_write_b64 %0, %1" ::"v"(a), "v"(make_float2(x, y)) : "memory");
+}
+__device__ __forceinline__ void lds_store_f32(float* p, float x) {
+  const uint32_t a = (uint32_t)reinterpret_cast<uintptr_t>(p);
+  asm volatile("ds_write_b32 %0, %1" ::"v"(a), "v"(x) : "memory");
+}
+
+// The LDS reads of one tile record's merge (two stage statistics, the slot's
+// exp2 scale, the tile reference), issued together and waited for in the same
+// block, likewise without the compiler's wait for direct loads in flight.
+__device__ __forceinline__ void lds_load_record_parts(const float2* p0, const float2* p1, const float* pc,
+                                                      const float* pr, float2& s0, float2& s1, float& c, float& r) {
+  const uint32_t a0 = (uint32_t)reinterpret_cast<uintptr_t>(p0), a1 = (uint32_t)reinterpret_cast<uintptr_t>(p1);
+  const uint32_t ac = (uint32_t)reinterpret_cast<uintptr_t>(pc), ar = (uint32_t)reinterpret_cast<uintptr_t>(pr);
+  asm volatile(
+      "ds_read_b64 %0, %4\n\t"
+      "ds_read_b64 %1, %5\n\t"
+      "ds_read_b32 %2, %6\n\t"
+      "ds_read_b32 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(s0), "=&v"(s1), "=&v"(c), "=&v"(r)
+      : "v"(a0), "v"(a1), "v"(ac), "v"(ar)
+      : "memory");
+}
+
+// Device-wide wait for phase `phase`.  The caller has waited for its own stores.
+__device__ __forceinline__ void grid_phase(const ResidentArgs& ra, uint32_t phase) {
+  __syncthreads();
+  if (threadIdx.x == 0)
+    __hip_atomic_store(ra.flags + blockIdx.x, phase, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x < 64) {
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    for (;;) {
+      int done = 1;
+      for (int i = threadIdx.x; i < (int)gridDim.x; i += 64)
+        done &= __hip_atomic_load(ra.flags + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= phase;
+      if (__all(done)) break;
+      if (__builtin_amdgcn_s_memrealtime() - t0 > ra.spin_limit) {
+        if (threadIdx.x == 0) flag_status(ra.d.status, kStall);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(256, 1) void draft_round_resident(ResidentArgs ra) {
+  constexpr int R = 256, KS = R / 16, KW = kResStagesPerWave;
+  constexpr int X_DMA = kResXInstr;  // direct loads of backbone rows per wavefront and slot group
+  constexpr int U_DMA = 4;       // and of U rows (16 KB per group over 4 wavefronts)
+  const DraftSelectArgs& a = ra.d;
+  extern __shared__ __attribute__((aligned(1024))) char lds[];
+  ResidentGemmShared& gs = *reinterpret_cast<ResidentGemmShared*>(lds + kResRingBytes);
+  DrawShared& dsh = *reinterpret_cast<DrawShared*>(lds + kResRingBytes);
+  float* const cTs = reinterpret_cast<float*>(lds + kResRingBytes + ((kResUnionBytes + 15) & ~(size_t)15));
+  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: everything derived from it is scalar
+  const int G = gridDim.x, cu = blockIdx.x;
+  const int B = a.B, gamma = a.gamma, V = a.V, nt = a.n_tiles;
+  const int NG = (B + 31) / 32;
+  const int T0 = (int)((long long)cu * nt / G), T1 = (int)((long long)(cu + 1) * nt / G);
+  const int ntl = T1 - T0, ns = 2 * ntl;
+  const int S0 = wave * ns / kResWaves, S1 = (wave + 1) * ns / kResWaves, nsw = S1 - S0;
+  // backbone buffer rows: 8 ntl chunks and one of padding
+  const uint32_t nch = 8u * (uint32_t)ntl, rs = nch + 1u, rs_magic = 0xFFFFFFFFu / rs + 1u;
+  const char* const Wb = static_cast<const char*>(a.Wt);
+  const char* const Xb = static_cast<const char*>(a.base);
+  const char* const Ub = static_cast<const char*>(a.U);
+
+  for (int b = tid; b < B; b += 256) {
+    const float T = effective_temp(a.temperature[b]);
+    cTs[b] = T > 0.0f ? kLog2e / T : 0.0f;
+  }
+
+  // W2 stages into registers (rows >= V read row V - 1: their columns are masked)
+  bf16x8 Wr[KW][KS];
+#pragma unroll
+  for (int i = 0; i < KW; ++i) {
+    const int c0 = (2 * T0 + S0 + min(i, max(nsw - 1, 0))) * kStageCols;
+    const int v = max(min(c0 + col_of_row(l32), V - 1), 0);
+    const char* p = Wb + (size_t)v * (R * 2) + half * 16;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      Wr[i][ks] = *reinterpret_cast<const bf16x8*>(p + ks * 32);
+      // home: four stages in the 256 accumulation registers (MFMA operands read
+      // them there), the fifth in vector registers
+      if (i < 4) asm volatile("" : "+a"(Wr[i][ks]));
+      else asm volatile("" : "+v"(Wr[i][ks]));
+    }
+  }
+
+  // backbone rows of slot group g: 16-byte chunk p of the buffer (p = 64 j +
+  // lane for instruction j) is chunk c = p mod rs of row p / rs; padding chunks
+  // and rows past the batch load a valid chunk that is never read; chunks past
+  // V (in the last tile) load kNegInfChunk.
+  // Addresses are a uniform base (the group's first row) plus a 32-bit lane
+  // offset (the launcher checks that 32 rows fit).
+  auto dma_x = [&](int pos, int g) {
+    const char* gbase = Xb + ((size_t)g * 32 * gamma + pos) * (size_t)V * 2;
+    const uint32_t rows = (uint32_t)min(32, B - g * 32), rowb = (uint32_t)gamma * (uint32_t)V * 2u;
+    uint32_t ln = (uint32_t)lane;
+    asm volatile("" : "+v"(ln));  // computed here, not kept live across the loop
+#pragma unroll
+    for (int m = 0; m < kResXInstr; ++m) {
+      const uint32_t j = (uint32_t)(wave * kResXInstr + m);
+      const uint32_t p = j * 64u + ln;
+      uint32_t row = __umulhi(p, rs_magic);
+      uint32_t c = p - row * rs;
+      if (row >= rows || c >= nch) row = 0, c = 0;
+      const uint32_t col = (uint32_t)T0 * 64u + c * 8u;
+      const void* src = col < (uint32_t)V ? static_cast<const void*>(gbase + (row * rowb + col * 2u))
+                                          : static_cast<const void*>(&kNegInfChunk);
+      __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(lds + (g & 1) * kResXBufBytes + j * 1024), 16, 0, 0);
+    }
+  };
+  // U rows of slot group g: chunk c of slot s at 16-byte position 32 s + (c ^ s),
+  // so that the B-operand reads of 16 consecutive slots hit distinct banks
+  auto dma_u = [&](int g) {
+    int hv = half;
+    asm volatile("" : "+v"(hv));  // computed here, not kept live across the loop
+#pragma unroll
+    for (int m = 0; m < U_DMA; ++m) {
+      const int j = wave * U_DMA + m;
+      const int s = 2 * j + hv;
+      const uint32_t tk = (uint32_t)gs.tok[min(g * 32 + s, B - 1)];
+      __builtin_amdgcn_global_load_lds(Ub + (tk * (uint32_t)(R * 2) + (uint32_t)((l32 ^ s) * 16)),
+                                       (lds_ptr_t)(reinterpret_cast<char*>(gs.urows[g & 1]) + j * 1024), 16, 0, 0);
+    }
+  };
+
+  // the tile records of slot group g: merge the two stages of each tile.  The
+  // stores (write-through, slow to complete) count in vmcnt with the direct
+  // loads, so they are issued one group after the statistics, right after a
+  // group's wait: they then have a group's work to complete before the next
+  // wait, which could otherwise only pass after loads issued just before it.
+  auto records = [&](int g) {
+    for (int q = tid; q < 32 * ntl; q += 256) {
+      const int sl = q / ntl, t = q - sl * ntl;
+      const int b = g * 32 + sl;
+      if (b < B) {
+        float2 f, s2;
+        float c, rf;
+        lds_load_record_parts(&gs.st[g & 1][2 * t][sl], &gs.st[g & 1][2 * t + 1][sl], &cTs[b], &gs.ref[g & 1][t][sl],
+                              f, s2, c, rf);
+        const float m = fmaxf(f.x, s2.x);
+        float s = f.y * __builtin_amdgcn_exp2f((f.x - m) * c);
+        if (s2.y > 0.0f) s += s2.y * __builtin_amdgcn_exp2f((s2.x - m) * c);
+        store_rec_coherent(const_cast<TileStat*>(a.tstat) + (size_t)b * nt + T0 + t, rf, m, s);
+      }
+    }
+  };
+
+  uint32_t phase = 0;
+  for (int pos = 0; pos < gamma; ++pos) {
+    // previous tokens: prev0 at position 0, else the draws of this launch
+    // (clamped into [0, V): a draw that never ran, after a stalled wait, leaves
+    // whatever the output held)
+    for (int b = tid; b < B; b += 256)
+      gs.tok[b] = pos == 0 ? checked_token(a.prev0[b], V, a.status, kBadPrev)
+                           : min(max(load_coherent(a.draft + (size_t)b * gamma + pos - 1), 0), V - 1);
+    __syncthreads();
+    dma_x(pos, 0);
+    if (NG > 1) dma_x(pos, 1);
+    dma_u(0);
+    if (NG > 1) dma_u(1);
+
+    for (int g = 0; g < NG; ++g) {
+      // group g's loads have landed in every wavefront (the next group's may be
+      // in flight; record stores are counted too, which only waits longer)
+      if (g + 1 >= NG) wait_vmcnt_c<0>();
+      else if (g == 0) wait_vmcnt_c<U_DMA>();
+      else wait_vmcnt_c<X_DMA + U_DMA>();
+      barrier_only();
+      if (g > 0) records(g - 1);
+
+      bf16x8 H[KS];
+      {
+        // chunk 2 ks + half of slot l32: byte (32 ks) ^ sw past the slot's row
+        uint32_t sw = (uint32_t)(half ^ l32) * 16u;
+        asm volatile("" : "+v"(sw));  // computed here, not kept live across the loop
+        const char* ub = reinterpret_cast<const char*>(gs.urows[g & 1]) + l32 * 512;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          H[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(ub + ((uint32_t)(32 * ks) ^ sw)));
+      }
+      const float cT = cTs[min(g * 32 + l32, B - 1)];
+      const char* const xrow = lds + (g & 1) * kResXBufBytes + (uint32_t)l32 * rs * 16u;  // this lane's slot
+      // Stage i's statistics run interleaved with the MFMAs of stage i + 1
+      // (one wavefront per SIMD: the matrix core works while the vector unit
+      // forms t, its maximum and its exp2-sum): per k-step, the first quarter
+      // forms t = (x - ref) + bias for 4 columns, the second takes their
+      // maximum, the second half adds 2 exp2 terms.
+      const f32x16 zero = {};
+      f32x16 acc[2];
+      acc[0] = zero;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Wr[0][ks], H[ks], acc[0], 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < KW; ++i) {
+        f32x16& cur = acc[i & 1];
+        f32x16& nxt = acc[(i + 1) & 1];
+        const int cs = S0 + i;  // stage index within the workgroup
+        // columns 16 half .. + 15 of the stage, and the tile's first column
+        const u32x4 w0 = *reinterpret_cast<const u32x4*>(xrow + (cs * 4 + 2 * half) * 16);
+        const u32x4 w1 = *reinterpret_cast<const u32x4*>(xrow + (cs * 4 + 2 * half) * 16 + 16);
+        const float ref = bf16_bits_to_f32(*reinterpret_cast<const uint16_t*>(xrow + (cs & ~1) * 64));
+        float tmax = -INFINITY, sum = 0.0f, mc = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          if (i + 1 < KW)
+            nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Wr[i + 1 < KW ? i + 1 : i][ks], H[ks], ks == 0 ? zero : nxt,
+                                                          0, 0, 0);
+          if (ks < 4) {
+#pragma unroll
+            for (int e = 4 * ks; e < 4 * ks + 4; ++e) {
+              const uint32_t w = e < 8 ? w0[(e & 7) >> 1] : w1[(e & 7) >> 1];
+              const float x = (e & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
+              cur[e] = (x - ref) + cur[e];  // columns past V: x = -inf
+            }
+          } else if (ks < 8) {
+#pragma unroll
+            for (int e = 4 * (ks - 4); e < 4 * (ks - 4) + 4; ++e) tmax = fmaxf(tmax, cur[e]);
+            if (ks == 7) tmax = pair_max(tmax), mc = tmax * cT;
+          } else {
+#pragma unroll
+            for (int e = 2 * (ks - 8); e < 2 * (ks - 8) + 2; ++e) sum += __builtin_amdgcn_exp2f(fmaf(cur[e], cT, -mc));
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        sum = pair_sum(sum);
+        const bool mine = i < nsw;
+        if (half == 0) {
+          // LDS that no direct load targets: written without the compiler's wait
+          // for the direct loads in flight (the waits before the barrier cover it)
+          lds_store_f32x2(&gs.st[g & 1][mine ? cs : kResWaves * KW][l32], tmax, sum);
+          if ((cs & 1) == 0) lds_store_f32(&gs.ref[g & 1][mine ? cs >> 1 : 2 * KW][l32], ref);
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      barrier_only();  // statistics complete; ring slot g & 1 and U rows g & 1 free again
+      // (stage statistics of g stay until the records of g are made at the top of
+      // group g + 1: group g + 2, the next to write them, starts after that)
+      if (g + 2 < NG) {
+        dma_x(pos, g + 2);
+        dma_u(g + 2);
+      }
+    }
+    records(NG - 1);
+
+    // every record of this position is written: draw
+    wait_vmcnt_c<0>();
+    grid_phase(ra, ++phase);
+    DraftSelectArgs d = a;
+    d.pos = pos;
+    for (int b = cu; b < B; b += G) {
+      draft_select_block<uint16_t, uint16_t, true>(d, b, dsh);
+      __syncthreads();
+    }
+    if (pos + 1 < gamma) {
+      wait_vmcnt_c<0>();
+      grid_phase(ra, ++phase);
+    }
+  }
+
+  // the last workgroup out leaves the flags at zero
+  wait_vmcnt_c<0>();
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t done = __hip_atomic_fetch_add(ra.exits, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (done == (uint32_t)G - 1) {
+      for (int i = 0; i < G; ++i) __hip_atomic_store(ra.flags + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(ra.exits, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1828,6 +2223,41 @@ hipError_t launch_draft_select_schedule(const DraftSelectArgs& d, const Schedule
                                        : launch_select_schedule_t<uint16_t, float>(d, sa, stream);
   return factor_dtype == DSPARK_BF16 ? launch_select_schedule_t<float, uint16_t>(d, sa, stream)
                                      : launch_select_schedule_t<float, float>(d, sa, stream);
+}
+
+hipError_t launch_draft_resident(const DraftSelectArgs& d, int logits_dtype, int factor_dtype,
+                                 uint32_t* grid_words, hipStream_t s) {
+  static_assert(kResMaxGrid + 1 <= kResidentGridWords, "phase flags and exit counter");
+  // lane offsets within a slot group's 32 rows and within U are 32-bit
+  const bool fits = (size_t)32 * d.gamma * d.V * 2 < (1ull << 32) && (size_t)d.V * d.r * 2 < (1ull << 32);
+  if (logits_dtype != DSPARK_BF16 || factor_dtype != DSPARK_BF16 || d.r != 256 || d.V % 8 != 0 || d.V < 64 ||
+      d.B > kResMaxB || d.n_tiles > kDrawMaxTiles || d.hrows || !fits)
+    return hipErrorNotSupported;
+  int dev = 0, cus = 0, coop = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev);
+  if (e != hipSuccess) return e;
+  // W2 must fit: at most 2 kResStagesPerWave tiles per workgroup
+  if (!coop || cus < 1 || cus > kResMaxGrid || (d.n_tiles + cus - 1) / cus > 2 * kResStagesPerWave)
+    return hipErrorNotSupported;
+  int groups = 0;
+  e = kernel_setup(reinterpret_cast<const void*>(&draft_round_resident), 256, kResLdsBytes, &groups);
+  if (e != hipSuccess) return e;
+  if (groups < cus) return hipErrorNotSupported;
+  ResidentArgs ra{};
+  ra.d = d;
+  ra.flags = grid_words;
+  ra.exits = grid_words + kResMaxGrid;
+  ra.spin_limit = 20000000ull;  // 0.2 s
+  void* args[] = {&ra};
+  KernelEvents* ev = kernel_events();
+  if (ev && ev->launches == 0) (void)hipEventRecord(ev->start, s);
+  e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&draft_round_resident), dim3(cus), dim3(256), args,
+                                 (unsigned)kResLdsBytes, s);
+  if (e != hipSuccess) return e;
+  if (ev && hipEventRecord(ev->stop, s) == hipSuccess) ++ev->launches;
+  return hipSuccess;
 }
 
 hipError_t launch_draft_select(const DraftSelectArgs& a, int logits_dtype, int factor_dtype,

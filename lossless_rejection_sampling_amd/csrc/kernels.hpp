@@ -11,7 +11,8 @@ namespace dspark {
 
 enum KernelClass : int {
   kClsDraftGemm = 0, kClsDraftSelect = 1, kClsRowStats = 2, kClsAccept = 3,
-  kClsResidualGemm = 4, kClsResidualSelect = 5, kClsSchedule = 6, kClsAcceptance = 7, kNumClasses = 8,
+  kClsResidualGemm = 4, kClsResidualSelect = 5, kClsSchedule = 6, kClsAcceptance = 7, kClsDraftRound = 8,
+  kNumClasses = 9,
 };
 
 // Kernel timing (measurement support).  While a ProfileScope of an enabled
@@ -107,6 +108,15 @@ struct DraftSelectArgs {
 
 hipError_t launch_draft_select(const DraftSelectArgs& a, int logits_dtype, int factor_dtype,
                                hipStream_t s);
+
+// The whole draft round (every position: contraction, statistics, draw) in one
+// cooperative launch that keeps W2 on chip; hipErrorNotSupported when the sizes,
+// types or the device do not fit it (the caller then launches per position).
+// `grid_words` (kResidentGridWords words of the workspace, zero between calls)
+// holds the launch's phase flags.
+constexpr int kResidentGridWords = 1024 + 64;
+hipError_t launch_draft_resident(const DraftSelectArgs& d, int logits_dtype, int factor_dtype,
+                                 uint32_t* grid_words, hipStream_t s);
 
 struct VerifyArgs {
   const void* target;

@@ -25,7 +25,9 @@ DSPARK_OK, DSPARK_EINVAL, DSPARK_EHIP, DSPARK_EDATA = 0, -1, -2, -3
 DSPARK_W_VOCAB_MAJOR, DSPARK_W_RANK_MAJOR = 0, 1
 SCHED_RULES = {"early_stop": 0, "argmax": 1, "fixed": 2, "threshold": 3}
 KERNEL_CLASSES = {"draft_gemm": 0, "draft_select": 1, "row_stats": 2, "accept": 3,
-                  "residual_gemm": 4, "residual_select": 5, "schedule": 6, "acceptance": 7}
+                  "residual_gemm": 4, "residual_select": 5, "schedule": 6, "acceptance": 7,
+                  "draft_round": 8}
+DSPARK_DRAFT_PER_POSITION, DSPARK_DRAFT_RESIDENT = 0, 1
 
 
 class DsparkError(RuntimeError):
@@ -43,6 +45,7 @@ _SIG = {
     "dspark_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
     "dspark_schedule_workspace_bytes": (ctypes.c_size_t, [_I, _I]),
     "dspark_pack_w2": (_I, [_P, _I, _I, _I, _P, _P]),
+    "dspark_set_draft_path": (_I, [_I]),
     "dspark_draft_round": (_I, [_P, _I, _P, _P, _I, _I, _P, _P, ctypes.c_uint64, _P,
                                 _I, _I, _I, _I, _P, _P, _P, _P, _P]),
     "dspark_draft_schedule": (_I, [_P, _I, _P, _P, _I, _I, _P, _P, ctypes.c_uint64, _P, _I, _I, _I, _I, _P, _P,
@@ -155,6 +158,15 @@ def dspark_pack_w2(W, W_packed, stream=None):
         raise ValueError("W_packed must be [V, r] with the dtype of W")
     _check("dspark_pack_w2", lib().dspark_pack_w2(_dev(W, "W"), _dtype_code(W), V, r,
                                                   _dev(W_packed, "W_packed"), _stream(stream)))
+
+
+def dspark_set_draft_path(path):
+    """Selects the draft-round implementation (DSPARK_DRAFT_PER_POSITION, the
+    default, or DSPARK_DRAFT_RESIDENT) process-wide; returns the previous one."""
+    res = lib().dspark_set_draft_path(int(path))
+    if res < 0:
+        _check("dspark_set_draft_path", res)
+    return res
 
 
 def dspark_draft_round(base_logits, U, W, prev0, temperature, seed, pos_offset,

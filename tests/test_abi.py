@@ -112,6 +112,15 @@ def test_host_argument_checks_return_einval(lib):
     assert lib.dspark_profile_enable(99, 1) == ds.DSPARK_EINVAL
 
 
+def test_draft_path_switch(lib):
+    # no device work: the switch is process state of the library
+    prev = lib.dspark_set_draft_path(1)
+    assert prev == 0  # per-position launches are the default
+    assert lib.dspark_set_draft_path(0) == 1
+    assert lib.dspark_set_draft_path(2) == -1 and lib.dspark_set_draft_path(-1) == -1
+    assert lib.dspark_set_draft_path(0) == 0
+
+
 def test_binding_reads_the_layout_from_the_shape():
     import torch
     U = torch.zeros((100, 16))
