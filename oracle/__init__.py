@@ -25,6 +25,9 @@ Modules:
   philox   -- Philox4x32-10 counter-based generator and the uniform/Gumbel maps
   sampler  -- the three-level Gumbel-max categorical sampler
   dspark   -- draft round, verify, scheduler, and probability helpers
+  ref      -- ctypes binding of the C oracle (dspark_ref.c: the ref_ entry
+              points, the same round as plain fp64 loops with OpenMP over
+              requests; compiled by build.py), pinned against dspark
 """
 
 from . import philox, sampler, dspark  # noqa: F401
