@@ -489,65 +489,49 @@ def _cpu_model():
 
 
 def cpu_baseline(rnd, budgets, seconds, threads=None):
-    """The oracle, as it stands, on a bounded sample of the same round: whole
-    requests (draft of every position, verify with the GPU-granted budgets),
-    spread over a pool of host threads (one BLAS thread each; numpy releases
-    the interpreter lock inside its array operations), until about ``seconds``
-    of wall time; the scheduler runs over the full batch once.  Reported as
-    verified draft tokens per second, extrapolated per request to the batch."""
-    import concurrent.futures as cf
-
+    """The C oracle (plain fp64 loops, OpenMP over requests), as it stands, on a
+    bounded sample of the same round: chunks of whole requests (draft of every
+    position, then verification with the GPU-granted budgets), one request per
+    thread, until about ``seconds`` of wall time; the scheduler runs over the
+    full batch once.  Reported as verified draft tokens per second,
+    extrapolated per request to the batch; the same at one thread beside it."""
     import numpy as np
 
     from lossless_rejection_sampling_amd import workloads as wl
-    from oracle import dspark as od
+    from oracle import ref
 
-    threads = threads or max(1, min(16, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity")
-                                  else (os.cpu_count() or 1)))
+    if not os.path.exists(ref.LIB):
+        from oracle import build as ob
+        ob.build()
+    avail = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    threads = threads or max(1, min(16, avail))
     h = wl.to_host
-    U, W = h(rnd.U), h(rnd.W)
-    conf = h(rnd.conf)
-    t_start = time.perf_counter()
-    sched = od.schedule(conf, rnd.sps_B, rnd.sps_val)
-    t_sched = time.perf_counter() - t_start
-
-    def one(b):
-        idx = [b]
-        base, target = h(rnd.base[b:b + 1]), h(rnd.target[b:b + 1])
-        prev0, T = h(rnd.prev0[b:b + 1]), h(rnd.temperature[b:b + 1])
-        dr = od.draft_round(base, U, W, prev0, T, rnd.seed, req_ids=idx)
-        od.verify(target, base, U, W, prev0, dr.tokens, T, rnd.seed, sched.budget[idx], req_ids=idx)
-        return b
+    U, W = np.ascontiguousarray(h(rnd.U), np.float32), np.ascontiguousarray(h(rnd.W), np.float32)
+    base, target = h(rnd.base), h(rnd.target)
+    prev0, T = h(rnd.prev0), h(rnd.temperature)
+    budgets = np.asarray(budgets, dtype=np.int32)
+    before = ref.threads()
+    t0 = time.perf_counter()
+    if rnd.scheduled:
+        ref.schedule(h(rnd.conf), rnd.sps_B, rnd.sps_val)
+    t_sched = time.perf_counter() - t0
 
     def run(n_threads, budget_s):
-        done = 0
-        t0 = time.perf_counter()
-        with cf.ThreadPoolExecutor(n_threads) as ex:
-            futs = []
-            nxt = 0
-            while nxt < min(rnd.B, n_threads):
-                futs.append(ex.submit(one, nxt))
-                nxt += 1
-            while futs:
-                f = futs.pop(0)
-                f.result()
-                done += 1
-                if time.perf_counter() - t0 < budget_s and nxt < rnd.B:
-                    futs.append(ex.submit(one, nxt))
-                    nxt += 1
+        ref.threads(n_threads)
+        done, t0 = 0, time.perf_counter()
+        while done < rnd.B and (done == 0 or time.perf_counter() - t0 < budget_s):
+            idx = np.arange(done, min(rnd.B, done + n_threads), dtype=np.int32)
+            sl = slice(int(idx[0]), int(idx[-1]) + 1)
+            dr = ref.draft_round(base[sl], U, W, prev0[sl], T[sl], rnd.seed, req_ids=idx)
+            ref.verify(target[sl], base[sl], U, W, prev0[sl], dr.tokens, T[sl], rnd.seed, budgets[sl], req_ids=idx)
+            done += len(idx)
         return done, time.perf_counter() - t0
 
-    try:
-        from threadpoolctl import threadpool_limits
-        limit = threadpool_limits(limits=1)
-    except Exception:
-        limit = None
     try:
         done, wall = run(threads, seconds)
         d1, w1 = run(1, seconds / 4)
     finally:
-        if limit is not None:
-            limit.restore_original_limits()
+        ref.threads(before)
     verified = float(np.sum(budgets))
     round_s = wall / done * rnd.B + t_sched
     single = {"value": verified / (w1 / d1 * rnd.B + t_sched), "cores": 1,
@@ -557,11 +541,12 @@ def cpu_baseline(rnd, budgets, seconds, threads=None):
         "unit": "verified draft tokens/s",
         "cores": threads,
         "kind": "oracle",
+        "implementation": "C oracle (oracle/dspark_ref.c), fp64, OpenMP over requests",
         "cpu_model": _cpu_model(),
         "host_cpus_visible": os.cpu_count(),
-        "sample": f"{done} of {rnd.B} requests timed whole (draft + verify) on {threads} threads in "
-                  f"{wall:.1f} s, plus the scheduler over all {rnd.B} ({t_sched:.2f} s), extrapolated per "
-                  f"request to the batch",
+        "sample": f"{done} of {rnd.B} requests timed whole (draft + verify) in chunks of {threads}, one request "
+                  f"per thread, in {wall:.1f} s, plus the scheduler over all {rnd.B} ({t_sched:.2f} s), "
+                  f"extrapolated per request to the batch",
         "single_thread": single,
     }
 
