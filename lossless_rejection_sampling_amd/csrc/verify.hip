@@ -267,9 +267,9 @@ __device__ int sample_row(const TL* row, const BlockStat* bs, int nb, int V, dou
 }
 
 // ---------------------------------------------------------------------------
-// Lazy verification: a target row is skipped once its request is known to be
-// decided, so the rows read are 0..n_b plus the few read before the decision
-// was known (instead of 0..L_b).  One workgroup of 4 wavefronts per work item
+// Lazy verification: a target row from row 2 on is skipped once its request is
+// known to be decided, so the rows read are 0..max(n_b, 1) plus the few read
+// before the decision was known (instead of 0..L_b).  One workgroup of 4 wavefronts per work item
 // (target row j, request b, 4 consecutive 4096-column blocks, one per
 // wavefront) in position-major order,
 //   item = (j B + b) ceil(n_blk / 4) + chunk,
@@ -320,7 +320,10 @@ __global__ __launch_bounds__(256) void verify_lazy_kernel(VerifyArgs a) {
   if (j == 0 && ch == 0 && tid == 0 && a.budget && (a.budget[b] < 0 || a.budget[b] > gamma))
     flag_status(a.status, kBadBudget);
   uint32_t* const vw = a.vstate + b;
-  if (j > 0) {
+  // Rows 0 and 1 are read without asking: row 0 is always needed and row 1
+  // whenever position 1 is accepted, the common case, while the question costs
+  // a memory round trip before the item's loads can go out.
+  if (j > 1) {
     if (tid == 0) s_word = __hip_atomic_load(vw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     if (s_word & kVerifyDone) return;  // decided at an earlier position: row j is not needed
