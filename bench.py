@@ -100,12 +100,13 @@ def algorithmic(rnd, budgets, emitted, rejected):
     es = rnd.base.element_size()
     fs = rnd.U.element_size()
     n_tiles = -(-V // 64)
+    rec = 8 if es == 2 else 16  # bytes of a tile record: (max, exp-sum), plus the shift for fp32 logits
     rows = int(sum(int(e) for e in emitted))
     return {
         "draft_gemm": dict(bytes=B * V * es + V * r * fs / g + B * r * fs,
-                           overhead_bytes=B * n_tiles * 16, flops=2.0 * B * r * V, per="draft step"),
+                           overhead_bytes=B * n_tiles * rec, flops=2.0 * B * r * V, per="draft step"),
         "draft_round": dict(bytes=g * (B * V * es + B * r * fs) + V * r * fs,
-                            overhead_bytes=g * B * n_tiles * 16, flops=2.0 * B * r * V * g, per="draft round"),
+                            overhead_bytes=g * B * n_tiles * rec, flops=2.0 * B * r * V * g, per="draft round"),
         "row_stats": dict(bytes=rows * V * es, flops=0.0, per="verify"),
         "residual_gemm": dict(bytes=rejected * 2 * V * es + V * r * fs, flops=2.0 * rejected * r * V,
                               per="verify"),

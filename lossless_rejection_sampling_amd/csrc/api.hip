@@ -49,7 +49,7 @@ Layout layout(int B, int gamma, int V, int r) {
   off = align_up(off + (size_t)B * gamma * sizeof(int32_t));
   off = align_up(off + ((size_t)B * gamma + 1) * sizeof(double));
   L.tstat = off;  // one spare row (B) takes the records of padding slots
-  off = align_up(off + (size_t)(B + 1) * L.n_tiles * sizeof(TileStat));
+  off = align_up(off + (size_t)(B + 1) * L.n_tiles * sizeof(TileStatRef));  // the larger record (fp32 logits)
   L.bstat = off;
   off = align_up(off + (size_t)B * (gamma + 1) * L.n_blk * sizeof(BlockStat));
   L.req = off;
@@ -255,7 +255,7 @@ int draft_round(const void* base_logits, int logits_dtype, const void* U, const 
   g.base = base_logits, g.U = U, g.Wt = W, g.prev0 = prev0, g.draft = draft_tokens;
   g.temperature = temperature;
   g.B = B, g.gamma = gamma, g.V = V, g.r = r, g.n_tiles = L.n_tiles;
-  g.tstat = at<TileStat>(workspace, L.tstat);
+  g.tstat = at<TileStatRef>(workspace, L.tstat);
   g.status = status;
 
   DraftSelectArgs d{};

@@ -27,12 +27,25 @@ enum : uint32_t {
   kStall = 64u,
 };
 
-// Softmax statistics of one 64-column tile of one draft row:
-//   d(v) = ref + t(v) with ref an exact input value (the tile's largest backbone
-//   logit), mx = max_v t(v), sum = sum_v exp((t(v) - mx) / T).
+// Softmax statistics of one 64-column tile of one draft row, d(v) being the
+// draft logit (backbone logit x(v) plus Markov bias) and T the temperature.
+// bf16 logits: t(v) = x(v) + bias(v) with one rounding (x is exact in fp32),
+//   mx = max_v t(v), sum = sum_v exp((t(v) - mx) / T); d(v) = t(v).
 struct TileStat {
+  float mx, sum;
+};
+// fp32 logits: the same with t(v) = (x(v) - ref) + bias(v), ref the tile's
+// largest backbone logit, so that the terms near the maximum carry no rounding
+// proportional to |ref| / T; d(v) = ref + t(v).
+struct TileStatRef {
   float ref, mx, sum, pad;
 };
+template <typename TL> struct TileRecOf { using type = TileStatRef; };
+template <> struct TileRecOf<uint16_t> { using type = TileStat; };
+template <typename TL> using TileRec = typename TileRecOf<TL>::type;
+// the tile's largest draft logit (exact: a sum of two fp32 values in fp64)
+__device__ __forceinline__ double rec_top(const TileStat& r) { return (double)r.mx; }
+__device__ __forceinline__ double rec_top(const TileStatRef& r) { return (double)r.ref + (double)r.mx; }
 
 // Statistics of one 4096-column block of one target row:
 //   mx = max z (an input value), sum = sum exp((z - mx) / T), arg = lowest index

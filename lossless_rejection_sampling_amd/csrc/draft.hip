@@ -74,6 +74,21 @@ __device__ __forceinline__ void slot_info(const GemmArgs& a, int s, int nslots, 
   prev = valid ? checked_token(pv, a.V, a.status, pos == 0 ? kBadPrev : kBadDraft) : 0;
 }
 
+// The draft tile record of the logit type (8 bytes for bf16 logits, whose t
+// carries no shift; 16 for fp32, shifted by the tile's largest backbone logit).
+template <typename TL>
+__device__ __forceinline__ void put_rec(void* ts, size_t i, float ref, float mx, float sum) {
+  if constexpr (sizeof(TL) == 2) {
+    static_cast<TileStat*>(ts)[i] = TileStat{mx, sum};
+  } else {
+    static_cast<TileStatRef*>(ts)[i] = TileStatRef{ref, mx, sum, 0.0f};
+  }
+}
+// Whether the draft statistics shift t by the tile's largest backbone logit
+// (fp32 logits; the residual masses always do, since any shift serves them).
+template <typename TL, bool RESIDUAL>
+constexpr bool kShiftByTileMax = RESIDUAL || sizeof(TL) != 2;
+
 // Four consecutive logits [v, v+4) of one row; missing columns read as -inf.
 template <typename TL, bool VEC>
 __device__ __forceinline__ void load4(const TL* row, int v, int V, float out[4]) {
@@ -172,7 +187,7 @@ __global__ __launch_bounds__(256) void gemm_stats_mfma(GemmArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) ref = fmaxf(ref, x[vb][g * 4 + e]);
       }
-    ref = fmaxf(ref, __shfl_xor(ref, 32));
+    ref = kShiftByTileMax<TL, RESIDUAL> ? fmaxf(ref, __shfl_xor(ref, 32)) : 0.0f;  // the shift of t
     float tmax = -INFINITY;
 #pragma unroll
     for (int vb = 0; vb < 2; ++vb)
@@ -190,11 +205,7 @@ __global__ __launch_bounds__(256) void gemm_stats_mfma(GemmArgs a) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) s += exp2f((x[vb][e] - tmax) * c);
       s += __shfl_xor(s, 32);
-      if (half == 0 && valid[bb]) {
-        TileStat st;
-        st.ref = ref, st.mx = tmax, st.sum = s, st.pad = 0.0f;
-        a.tstat[(size_t)rq * a.n_tiles + tile] = st;
-      }
+      if (half == 0 && valid[bb]) put_rec<TL>(a.tstat, (size_t)rq * a.n_tiles + tile, ref, tmax, s);
     } else {
       // r(v) = max(0, p(v) - q(v)) with p from the target row and q rebuilt from
       // the draft statistics of the same position.
@@ -311,12 +322,15 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const f32x16 (&
       for (int e = 0; e < 16; ++e)
         if (acc_col(tile * kTile, vb, e, half) >= a.V) xv[vb][e] = -INFINITY;
   }
-  float ref = -INFINITY;
+  float ref = 0.0f;  // the shift of t
+  if constexpr (kShiftByTileMax<TL, RESIDUAL>) {
+    ref = -INFINITY;
 #pragma unroll
-  for (int vb = 0; vb < 2; ++vb)
+    for (int vb = 0; vb < 2; ++vb)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) ref = fmaxf(ref, xv[vb][e]);
-  ref = fmaxf(ref, __shfl_xor(ref, 32));
+      for (int e = 0; e < 16; ++e) ref = fmaxf(ref, xv[vb][e]);
+    ref = fmaxf(ref, __shfl_xor(ref, 32));
+  }
   float t[2][16];
   float tmax = -INFINITY;
 #pragma unroll
@@ -336,11 +350,7 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const f32x16 (&
 #pragma unroll
       for (int e = 0; e < 16; ++e) s += __builtin_amdgcn_exp2f(fmaf(t[vb][e], c, -mc));
     s += __shfl_xor(s, 32);
-    if (half == 0 && valid) {
-      TileStat st;
-      st.ref = ref, st.mx = tmax, st.sum = s, st.pad = 0.0f;
-      a.tstat[(size_t)rq * a.n_tiles + tile] = st;
-    }
+    if (half == 0 && valid) put_rec<TL>(a.tstat, (size_t)rq * a.n_tiles + tile, ref, tmax, s);
   } else {
     TileBuf<TL> z;
     load_tile<TL>(trow, tile * kTile, half, a.V, z);
@@ -536,18 +546,14 @@ __global__ __launch_bounds__(64) void gemm_stats_valu(GemmArgs a) {
   for (int k = 0; k < r; ++k) bias = fmaf(load_logit(h + k), load_logit(w + k), bias);
   const TL* brow = static_cast<const TL*>(a.base) + ((size_t)b * a.gamma + pos) * V;
   const float x = ok ? load_logit(brow + v) : -INFINITY;
-  const float ref = wave_max(x);
+  const float ref = kShiftByTileMax<TL, RESIDUAL> ? wave_max(x) : 0.0f;  // the shift of t
   const float t = ok ? (x - ref) + bias : -INFINITY;
   const float tmax = wave_max(t);
   const float T = effective_temp(a.temperature[b]);
   if constexpr (!RESIDUAL) {
     const float c = T > 0.0f ? kLog2e / T : 0.0f;
     const float sum = wave_sum(ok ? exp2f((t - tmax) * c) : 0.0f);
-    if (lane == 0) {
-      TileStat st;
-      st.ref = ref, st.mx = tmax, st.sum = sum, st.pad = 0.0f;
-      a.tstat[(size_t)b * a.n_tiles + tile] = st;
-    }
+    if (lane == 0) put_rec<TL>(a.tstat, (size_t)b * a.n_tiles + tile, ref, tmax, sum);
   } else {
     double rmax, rlsum;
     residual_rowstats(a, b, pos, rmax, rlsum);
@@ -588,7 +594,8 @@ __device__ __forceinline__ void block_mass(const double (&d)[4], const float (&s
 // One draw per request at block position pos+1 (a workgroup of 4 wavefronts
 // per request): three-level Gumbel-max over blocks of 64 tiles, tiles of 64
 // columns, and columns.  Block and tile levels use the tile statistics (one
-// coalesced 1 KB read per block); the chosen tile is recomputed in fp64 with
+// coalesced 512-byte read per block for bf16 logits, 1 KB for fp32); the chosen
+// tile is recomputed in fp64 with
 // the rank split over the four wavefronts.  Greedy requests take the tile with
 // the largest logit and its argmax (lowest index on ties).
 // ---------------------------------------------------------------------------
@@ -641,7 +648,7 @@ __global__ __launch_bounds__(256) void draft_select_kernel(DraftSelectArgs a) {
   const float Tf = checked_temp(a.temperature[b], a.status);
   int prev = pos == 0 ? a.prev0[b] : a.draft[(size_t)b * gamma + pos - 1];
   prev = checked_token(prev, V, a.status, pos == 0 ? kBadPrev : kBadDraft);
-  const TileStat* ts = a.tstat + (size_t)b * nt;
+  const TileRec<TL>* ts = static_cast<const TileRec<TL>*>(a.tstat) + (size_t)b * nt;
   const TL* brow = static_cast<const TL*>(a.base) + ((size_t)b * gamma + pos) * V;
   const TF* h = static_cast<const TF*>(a.U) + (size_t)prev * r;
   const TF* Wt = static_cast<const TF*>(a.Wt);
@@ -651,7 +658,7 @@ __global__ __launch_bounds__(256) void draft_select_kernel(DraftSelectArgs a) {
   double invT = 0.0, lse = 0.0;
   if (Tf > 0.0f) {
     invT = 1.0 / (double)Tf;
-    const double mref = (double)ts[0].ref + (double)ts[0].mx;
+    const double mref = rec_top(ts[0]);
     // wavefront 0, lane j: running choice and log-sum-exp over the groups
     double best = -INFINITY, row_m = -INFINITY, row_s = 0.0;
     int best_blk = 0x7fffffff;
@@ -668,8 +675,8 @@ __global__ __launch_bounds__(256) void draft_select_kernel(DraftSelectArgs a) {
         for (int k = 0; k < 4; ++k) {
           const int t = (g0 + 16 * q) * kTilesPerBlock + 4 * tid + k;
           if (t < nt) {
-            const TileStat st = ts[t];
-            d[q][k] = (double)st.ref + (double)st.mx, sm[q][k] = st.sum;
+            const TileRec<TL> st = ts[t];
+            d[q][k] = rec_top(st), sm[q][k] = st.sum;
           } else {
             d[q][k] = -INFINITY, sm[q][k] = 0.0f;
           }
@@ -712,9 +719,8 @@ __global__ __launch_bounds__(256) void draft_select_kernel(DraftSelectArgs a) {
       double val = -INFINITY;
       int ti = 0x7fffffff;
       if (t0 + lane < t1) {
-        const TileStat st = ts[t0 + lane];
-        val = ((double)st.ref + (double)st.mx - mref) * invT + log((double)st.sum) +
-              gumbel(a.seed, kDraftMid, b, rpos, lane);
+        const TileRec<TL> st = ts[t0 + lane];
+        val = (rec_top(st) - mref) * invT + log((double)st.sum) + gumbel(a.seed, kDraftMid, b, rpos, lane);
         ti = t0 + lane;
       }
       wave_argmax(val, ti);
@@ -726,7 +732,7 @@ __global__ __launch_bounds__(256) void draft_select_kernel(DraftSelectArgs a) {
     double best = -INFINITY;
     int bt = 0x7fffffff;
     for (int t = tid; t < nt; t += 256) {
-      const double d = (double)ts[t].ref + (double)ts[t].mx;
+      const double d = rec_top(ts[t]);
       if (d > best) best = d, bt = t;
     }
     wave_argmax(best, bt);
@@ -791,7 +797,7 @@ __global__ __launch_bounds__(256) void draft_select_kernel(DraftSelectArgs a) {
 // draft_select_kernel.
 constexpr int kDrawMaxTiles = kTilesPerBlock * 64;
 struct DrawShared {
-  double d[kDrawMaxTiles];   // ref + mx of every tile
+  double d[kDrawMaxTiles];   // largest draft logit of every tile
   float sum[kDrawMaxTiles];  // exp-sum of every tile
   double g[3][64];           // Gumbel values: block, tile, column level
   double bm[64], part[4][64];
@@ -802,18 +808,14 @@ struct DrawShared {
 
 // Accesses to data that other workgroups of the same launch write or read
 // (agent-scope relaxed atomics: coherent across the XCDs' L2 caches).
-__device__ __forceinline__ float4 load_rec_coherent(const TileStat* p) {
-  const uint64_t* q = reinterpret_cast<const uint64_t*>(p);
-  const uint64_t lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const uint64_t hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return make_float4(__uint_as_float((uint32_t)lo), __uint_as_float((uint32_t)(lo >> 32)),
-                     __uint_as_float((uint32_t)hi), __uint_as_float((uint32_t)(hi >> 32)));
+__device__ __forceinline__ TileStat load_rec_coherent(const TileStat* p) {
+  const uint64_t w = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  return TileStat{__uint_as_float((uint32_t)w), __uint_as_float((uint32_t)(w >> 32))};
 }
-__device__ __forceinline__ void store_rec_coherent(TileStat* p, float ref, float mx, float sum) {
-  uint64_t* q = reinterpret_cast<uint64_t*>(p);
-  __hip_atomic_store(q, (uint64_t)__float_as_uint(ref) | ((uint64_t)__float_as_uint(mx) << 32), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(q + 1, (uint64_t)__float_as_uint(sum), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void store_rec_coherent(TileStat* p, float mx, float sum) {
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), (uint64_t)__float_as_uint(mx) | ((uint64_t)__float_as_uint(sum) << 32),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ int load_coherent(const int32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -837,7 +839,9 @@ __device__ __forceinline__ void draft_select_block(const DraftSelectArgs& a, int
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int V = a.V, r = a.r, gamma = a.gamma, nt = a.n_tiles, pos = a.pos;
   const int nblk = (nt + kTilesPerBlock - 1) / kTilesPerBlock;
-  const TileStat* ts = a.tstat + (size_t)b * nt;
+  using Rec = TileRec<TL>;
+  static_assert(!COHERENT || sizeof(TL) == 2, "coherent records are the bf16 kind");
+  const Rec* ts = static_cast<const Rec*>(a.tstat) + (size_t)b * nt;
 
   // 1. every load of the draw's first phase at once
   const float T_raw = a.temperature[b];
@@ -845,19 +849,20 @@ __device__ __forceinline__ void draft_select_block(const DraftSelectArgs& a, int
                        : COHERENT               ? load_coherent(a.draft + (size_t)b * gamma + pos - 1)
                                                 : a.draft[(size_t)b * gamma + pos - 1];
   const uint32_t off = a.pos_offset ? (uint32_t)a.pos_offset[b] : 0u;
-  float4 rec[4][4];  // tiles 1024 q + 4 tid + k (unconditional loads, so that they all go out at once)
+  Rec rec[4][4];  // tiles 1024 q + 4 tid + k (unconditional loads, so that they all go out at once)
 #pragma unroll
   for (int q = 0; q < 4; ++q)
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const TileStat* p = ts + min(1024 * q + 4 * tid + k, nt - 1);
-      rec[q][k] = COHERENT ? load_rec_coherent(p) : *reinterpret_cast<const float4*>(p);
+      const Rec* p = ts + min(1024 * q + 4 * tid + k, nt - 1);
+      if constexpr (COHERENT) rec[q][k] = load_rec_coherent(p);
+      else rec[q][k] = *p;
     }
 #pragma unroll
   for (int q = 0; q < 4; ++q)
 #pragma unroll
     for (int k = 0; k < 4; ++k)
-      if (1024 * q + 4 * tid + k >= nt) rec[q][k] = make_float4(0.0f, -INFINITY, 0.0f, 0.0f);
+      if (1024 * q + 4 * tid + k >= nt) rec[q][k].mx = -INFINITY, rec[q][k].sum = 0.0f;
   const uint32_t rpos = (uint32_t)(pos + 1) + off;
   if (wave < 3 && (wave != 0 || lane < nblk)) s_g[wave][lane] = gumbel(a.seed, kDraftTop + wave, b, rpos, lane);
   const float Tf = checked_temp(T_raw, a.status);
@@ -869,7 +874,7 @@ __device__ __forceinline__ void draft_select_block(const DraftSelectArgs& a, int
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int t = 1024 * q + 4 * tid + k;
-      if (t < nt) s_d[t] = (double)rec[q][k].x + (double)rec[q][k].y, s_sum[t] = rec[q][k].z;
+      if (t < nt) s_d[t] = rec_top(rec[q][k]), s_sum[t] = rec[q][k].sum;
     }
   int tile;
   double lse = 0.0;
@@ -880,7 +885,7 @@ __device__ __forceinline__ void draft_select_block(const DraftSelectArgs& a, int
       double d[4], m;
       float sm[4], e;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) d[k] = (double)rec[q][k].x + (double)rec[q][k].y, sm[k] = rec[q][k].z;
+      for (int k = 0; k < 4; ++k) d[k] = rec_top(rec[q][k]), sm[k] = rec[q][k].sum;
       block_mass(d, sm, invT * kLog2eD, m, e);
       const int j = 16 * q + 4 * wave + (lane >> 4);
       if ((lane & 15) == 0 && j < nblk) s_bm[j] = m, s_be[j] = e;
@@ -926,7 +931,7 @@ __device__ __forceinline__ void draft_select_block(const DraftSelectArgs& a, int
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int t = 1024 * q + 4 * tid + k;
-        const double d = (double)rec[q][k].x + (double)rec[q][k].y;
+        const double d = rec_top(rec[q][k]);
         if (t < nt && d > best) best = d, bt = t;
       }
     wave_argmax(best, bt);
@@ -1019,9 +1024,9 @@ __global__ __launch_bounds__(256) void draft_select_schedule(SelectScheduleArgs 
 //    register is ever the target of an outstanding load inside the loop, and
 //    every wait is explicit.
 //  * The accumulator sums the bias alone (it starts at zero, so its roundings
-//    are at the bias's scale); the epilogue forms t = (x - ref) + bias with one
-//    rounding, ref being the slot's logit at the tile's first column (an exact
-//    input value, so x - ref is exact).
+//    are at the bias's scale); the epilogue forms t = x + bias with one
+//    rounding (a bf16 logit is exact in fp32).  With no shift to carry, a tile
+//    record is (max t, exp-sum): 8 bytes.
 //  * Iteration u issues the MFMAs of stage u+1 interleaved with the
 //    statistics of stage u; the two stages of a tile are merged into one
 //    record; the wait at the end covers only the loads of stage u+2.
@@ -1134,11 +1139,11 @@ __global__ __launch_bounds__(512, 1) void gemm_draft_stream(GemmArgs a) {
   };
   const uint32_t st_spare = (uint32_t)nslots * (uint32_t)nt;
   const uint32_t st_base = valid ? (uint32_t)rq * (uint32_t)nt : st_spare;
-  auto store_rec = [&](uint32_t at, float ref, float mx, float sum) {
-    const f32x4 rec = {ref, mx, sum, 0.0f};
+  auto store_rec = [&](uint32_t at, float mx, float sum) {
+    const float2 rec = {mx, sum};  // TileStat
     // an ordinary store: the line stays in L2 until the neighbouring records
     // of the same XCD's run have joined it, and leaves as a whole line
-    *reinterpret_cast<f32x4*>(reinterpret_cast<char*>(a.tstat) + at * 16u) = rec;
+    *reinterpret_cast<float2*>(reinterpret_cast<char*>(a.tstat) + at * 8u) = rec;
   };
 
   // The temperature and the U rows of the previous tokens (from the table the
@@ -1177,16 +1182,9 @@ __global__ __launch_bounds__(512, 1) void gemm_draft_stream(GemmArgs a) {
   const int wbase = WL::at(l32, half);          // operand base: storage row l32, chunk half
   const int xbase = half * 1024 + l32 * 16;     // this lane's first logit chunk in a stage
 
-  // the accumulator of a stage starts at zero (it sums the bias alone, at the
-  // bias's own scale); the first stage of a tile also sets ref (its column 0,
-  // held by lane l32 of half 0)
-  auto seed = [&](int slot, bool first, f32x16& acc, float& ref) {
-    if (first) {
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(xring + slot * kXStageBytes + xbase);
-      float even, odd;
-      row_pair<32>(__uint_as_float(w << 16), even, odd);
-      ref = even;
-    }
+  // the accumulator of a stage starts at zero: it sums the bias alone, at the
+  // bias's own scale
+  auto seed = [&](f32x16& acc) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
   };
@@ -1237,7 +1235,7 @@ __global__ __launch_bounds__(512, 1) void gemm_draft_stream(GemmArgs a) {
 
   // Iteration u (stage u in ring slot S = u % 4 has its bias in `cur`; stage
   // u+1 in slot S+1 has landed):
-  //   take stage u's backbone logits from slot S (t = (x - ref) + bias, one
+  //   take stage u's backbone logits from slot S (t = x + bias, one
   //   rounding); seed `next` for stage u+1; issue stage u+4 into slot S; run the
   //   MFMAs of stage u+1 with the statistics of stage u; on a tile's second
   //   stage (odd u) merge with the first and store the record; wait for stage
@@ -1247,20 +1245,19 @@ __global__ __launch_bounds__(512, 1) void gemm_draft_stream(GemmArgs a) {
   //   before older loads, so counting it could let the wait pass early, while
   //   leaving it out only ever waits longer.
   int jt = 0, tile = tile_of(0);
-  float ref0 = 0.0f, ref1 = 0.0f, mx_first = 0.0f, sum_first = 0.0f;
+  float mx_first = 0.0f, sum_first = 0.0f;
   auto step = [&](auto S_, f32x16& cur, f32x16& next, int u) {
     constexpr int S = decltype(S_)::value;
     constexpr bool second = S & 1;  // stage u is the second half of its tile
     float x[16];
     read_x(S, x);
-    if (second) seed((S + 1) % kStages, true, next, ref0);   // next tile's first stage sets its ref
-    else seed((S + 1) % kStages, false, next, ref0);         // same tile, same ref
+    seed(next);
     // slot S is rewritten below: its logits must have reached registers
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     dma_w(u + 4, S);
     dma_x(u + 4, S);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) cur[e] = (x[e] - ref1) + cur[e];
+    for (int e = 0; e < 16; ++e) cur[e] = x[e] + cur[e];
     const int c0 = tile * kTile + (second ? kStageCols : 0);
     if (c0 + kStageCols > V) {  // a ragged stage: columns >= V do not exist
 #pragma unroll
@@ -1274,9 +1271,8 @@ __global__ __launch_bounds__(512, 1) void gemm_draft_stream(GemmArgs a) {
       const float m = fmaxf(mx_first, mx);
       float s = sum_first * __builtin_amdgcn_exp2f((mx_first - m) * cT);
       if (sum > 0.0f) s += sum * __builtin_amdgcn_exp2f((mx - m) * cT);
-      if (half == 0) store_rec(st_base + (uint32_t)tile, ref1, m, s);  // both halves hold the same values
+      if (half == 0) store_rec(st_base + (uint32_t)tile, m, s);  // both halves hold the same values
       tile = tile_of(++jt);
-      ref1 = ref0;
     } else {
       mx_first = mx, sum_first = sum;
     }
@@ -1288,8 +1284,7 @@ __global__ __launch_bounds__(512, 1) void gemm_draft_stream(GemmArgs a) {
   // prologue: stage 0 landed (the loads of stages 1 to 3 may be pending)
   wait_vmcnt_c<3 * (W_DMA + X_DMA)>();
   barrier_only();
-  seed(0, true, acc0, ref0);
-  ref1 = ref0;
+  seed(acc0);
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd(0, ks), H[ks], acc0, 0, 0, 0);
   wait_vmcnt_c<2 * (W_DMA + X_DMA)>();  // stage 1 landed
@@ -1333,7 +1328,7 @@ hipError_t launch_draft_stream(const GemmArgs& a, hipStream_t s) {
 //    (gathered through the previous tokens) and each wavefront's backbone rows
 //    of its stages arrive in LDS by direct loads two groups ahead; per stage
 //    16 MFMAs with the U rows as B operand, then the tile statistics exactly as
-//    in the streaming kernel (t = (x - ref) + bias, max, exp2-sum).  Stage
+//    in the streaming kernel (t = x + bias, max, exp2-sum).  Stage
 //    statistics meet in LDS, where the workgroup merges the two stages of each
 //    tile into the tile's record.
 //  * Between phases.  The records of a position (all workgroups) feed the
@@ -1364,11 +1359,11 @@ constexpr int kResRingBytes = 2 * kResXBufBytes;  // two slot groups
 struct ResidentGemmShared {
   uint4 urows[2][32 * 32];                          // U rows of two slot groups, 16-byte chunks swizzled
   float2 st[2][kResWaves * kResStagesPerWave + 1][32];  // (max, exp-sum) per stage and slot; the last row is a sink
-  float ref[2][2 * kResStagesPerWave + 1][32];         // tile reference logit per tile and slot; last row a sink
   int32_t tok[kResMaxB];                             // previous token of every request
 };
 constexpr size_t kResUnionBytes =
     sizeof(ResidentGemmShared) > sizeof(DrawShared) ? sizeof(ResidentGemmShared) : sizeof(DrawShared);
+// ... then the exp2 scale of every request
 constexpr size_t kResLdsBytes = kResRingBytes + ((kResUnionBytes + 15) & ~(size_t)15) + kResMaxB * sizeof(float);
 
 // Eight bf16 -inf values: the backbone chunks past V load this instead, so the
@@ -1390,26 +1385,21 @@ __device__ __forceinline__ void lds_store_f32x2(float2* p, float x, float y) {
   const uint32_t a = (uint32_t)reinterpret_cast<uintptr_t>(p);
   asm volatile("ds_write_b64 %0, %1" ::"v"(a), "v"(make_float2(x, y)) : "memory");
 }
-__device__ __forceinline__ void lds_store_f32(float* p, float x) {
-  const uint32_t a = (uint32_t)reinterpret_cast<uintptr_t>(p);
-  asm volatile("ds_write_b32 %0, %1" ::"v"(a), "v"(x) : "memory");
-}
 
-// The LDS reads of one tile record's merge (two stage statistics, the slot's
-// exp2 scale, the tile reference), issued together and waited for in the same
-// block, likewise without the compiler's wait for direct loads in flight.
+// The LDS reads of one tile record's merge (two stage statistics and the slot's
+// exp2 scale), issued together and waited for in the same block, likewise
+// without the compiler's wait for direct loads in flight.
 __device__ __forceinline__ void lds_load_record_parts(const float2* p0, const float2* p1, const float* pc,
-                                                      const float* pr, float2& s0, float2& s1, float& c, float& r) {
+                                                      float2& s0, float2& s1, float& c) {
   const uint32_t a0 = (uint32_t)reinterpret_cast<uintptr_t>(p0), a1 = (uint32_t)reinterpret_cast<uintptr_t>(p1);
-  const uint32_t ac = (uint32_t)reinterpret_cast<uintptr_t>(pc), ar = (uint32_t)reinterpret_cast<uintptr_t>(pr);
+  const uint32_t ac = (uint32_t)reinterpret_cast<uintptr_t>(pc);
   asm volatile(
-      "ds_read_b64 %0, %4\n\t"
-      "ds_read_b64 %1, %5\n\t"
-      "ds_read_b32 %2, %6\n\t"
-      "ds_read_b32 %3, %7\n\t"
+      "ds_read_b64 %0, %3\n\t"
+      "ds_read_b64 %1, %4\n\t"
+      "ds_read_b32 %2, %5\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=&v"(s0), "=&v"(s1), "=&v"(c), "=&v"(r)
-      : "v"(a0), "v"(a1), "v"(ac), "v"(ar)
+      : "=&v"(s0), "=&v"(s1), "=&v"(c)
+      : "v"(a0), "v"(a1), "v"(ac)
       : "memory");
 }
 
@@ -1530,13 +1520,12 @@ __global__ __launch_bounds__(256, 1) void draft_round_resident(ResidentArgs ra) 
       const int b = g * 32 + sl;
       if (b < B) {
         float2 f, s2;
-        float c, rf;
-        lds_load_record_parts(&gs.st[g & 1][2 * t][sl], &gs.st[g & 1][2 * t + 1][sl], &cTs[b], &gs.ref[g & 1][t][sl],
-                              f, s2, c, rf);
+        float c;
+        lds_load_record_parts(&gs.st[g & 1][2 * t][sl], &gs.st[g & 1][2 * t + 1][sl], &cTs[b], f, s2, c);
         const float m = fmaxf(f.x, s2.x);
         float s = f.y * __builtin_amdgcn_exp2f((f.x - m) * c);
         if (s2.y > 0.0f) s += s2.y * __builtin_amdgcn_exp2f((s2.x - m) * c);
-        store_rec_coherent(const_cast<TileStat*>(a.tstat) + (size_t)b * nt + T0 + t, rf, m, s);
+        store_rec_coherent(static_cast<TileStat*>(const_cast<void*>(a.tstat)) + (size_t)b * nt + T0 + t, m, s);
       }
     }
   };
@@ -1579,7 +1568,7 @@ __global__ __launch_bounds__(256, 1) void draft_round_resident(ResidentArgs ra) 
       // Stage i's statistics run interleaved with the MFMAs of stage i + 1
       // (one wavefront per SIMD: the matrix core works while the vector unit
       // forms t, its maximum and its exp2-sum): per k-step, the first quarter
-      // forms t = (x - ref) + bias for 4 columns, the second takes their
+      // forms t = x + bias for 4 columns, the second takes their
       // maximum, the second half adds 2 exp2 terms.
       const f32x16 zero = {};
       f32x16 acc[2];
@@ -1591,10 +1580,9 @@ __global__ __launch_bounds__(256, 1) void draft_round_resident(ResidentArgs ra) 
         f32x16& cur = acc[i & 1];
         f32x16& nxt = acc[(i + 1) & 1];
         const int cs = S0 + i;  // stage index within the workgroup
-        // columns 16 half .. + 15 of the stage, and the tile's first column
+        // columns 16 half .. + 15 of the stage
         const u32x4 w0 = *reinterpret_cast<const u32x4*>(xrow + (cs * 4 + 2 * half) * 16);
         const u32x4 w1 = *reinterpret_cast<const u32x4*>(xrow + (cs * 4 + 2 * half) * 16 + 16);
-        const float ref = bf16_bits_to_f32(*reinterpret_cast<const uint16_t*>(xrow + (cs & ~1) * 64));
         float tmax = -INFINITY, sum = 0.0f, mc = 0.0f;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
@@ -1606,7 +1594,7 @@ __global__ __launch_bounds__(256, 1) void draft_round_resident(ResidentArgs ra) 
             for (int e = 4 * ks; e < 4 * ks + 4; ++e) {
               const uint32_t w = e < 8 ? w0[(e & 7) >> 1] : w1[(e & 7) >> 1];
               const float x = (e & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
-              cur[e] = (x - ref) + cur[e];  // columns past V: x = -inf
+              cur[e] = x + cur[e];  // columns past V: x = -inf
             }
           } else if (ks < 8) {
 #pragma unroll
@@ -1624,7 +1612,6 @@ __global__ __launch_bounds__(256, 1) void draft_round_resident(ResidentArgs ra) 
           // LDS that no direct load targets: written without the compiler's wait
           // for the direct loads in flight (the waits before the barrier cover it)
           lds_store_f32x2(&gs.st[g & 1][mine ? cs : kResWaves * KW][l32], tmax, sum);
-          if ((cs & 1) == 0) lds_store_f32(&gs.ref[g & 1][mine ? cs >> 1 : 2 * KW][l32], ref);
         }
       }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");

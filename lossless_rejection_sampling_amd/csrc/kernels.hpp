@@ -60,7 +60,8 @@ void launch(void (*k)(Arg), dim3 grid, dim3 block, size_t lds, hipStream_t s, co
 }
 
 // Arguments of the fused Markov-bias GEMM with its softmax-statistics epilogue.
-// Draft mode: one slot per request, base row `pos`; writes TileStat [B][n_tiles].
+// Draft mode: one slot per request, base row `pos`; writes TileRec<logit type>
+// [B + 1][n_tiles] (8 bytes a record for bf16 logits, 16 for fp32).
 // Residual mode: slots are the requests listed in slot_req[0..*slot_count), each
 // at its own row req[b].n; writes the residual mass of every tile [B][n_tiles].
 struct GemmArgs {
@@ -79,7 +80,7 @@ struct GemmArgs {
   int tv;                    // residual mode as the acceptance pass: every (request, row)
   const double2* rowinfo;    // [B, gamma] target row max and ln-sum-exp    (acceptance pass)
   int B, gamma, V, r, n_tiles, pos;
-  TileStat* tstat;           // draft mode output
+  void* tstat;               // draft mode output: TileRec<logit type> records
   float* rsum;               // residual mode output
   uint32_t* status;
 };
@@ -96,7 +97,7 @@ struct DraftSelectArgs {
   const int32_t* prev0;
   const float* temperature;
   const int32_t* pos_offset;
-  const TileStat* tstat;
+  const void* tstat;         // TileRec<logit type> records of position pos
   uint64_t seed;
   int B, gamma, V, r, n_tiles, pos;
   int32_t* draft;
