@@ -590,6 +590,24 @@ __device__ __forceinline__ void block_mass(const double (&d)[4], const float (&s
   m_out = m, e_out = group16_sum(e);
 }
 
+// The row's log-sum-exp (lse, in units of logit / T) with the chosen tile's
+// share of the row's mass taken from the tile's fp64 recompute (sv = d / T of
+// each live lane's column) in place of its share from the tile record:
+//   lse + log(1 - share_rec + share_exact).
+// share_rec is the record's term exactly as the block sums included it
+// (block_mass: the fp32 exponent of (d - m_blk) / T and v_exp_f32), relative to
+// the row's shift gm and sum gs.  The record's top logit carries one fp32
+// rounding at |t|'s scale, which 1/T magnifies; where the chosen tile holds
+// most of the mass, this removes nearly all of it from ln q.
+__device__ __forceinline__ double exact_tile_lse(double lse, double sv, bool live, double rec_d, float rec_sum,
+                                                 double m_blk, double gm, double gs, double invT) {
+  const double ex = wave_sum(live ? exp(sv - lse) : 0.0);
+  float term = 0.0f;
+  if (rec_sum > 0.0f) term = rec_sum * __builtin_amdgcn_exp2f((float)((rec_d - m_blk) * (invT * kLog2eD)));
+  const double rec = (double)term * exp((m_blk - gm) * invT) / gs;
+  return lse + log1p(ex - rec);
+}
+
 // ---------------------------------------------------------------------------
 // One draw per request at block position pos+1 (a workgroup of 4 wavefronts
 // per request): three-level Gumbel-max over blocks of 64 tiles, tiles of 64
@@ -656,11 +674,14 @@ __global__ __launch_bounds__(256) void draft_select_kernel(DraftSelectArgs a) {
 
   int tile;  // chosen tile
   double invT = 0.0, lse = 0.0;
+  double row_m = -INFINITY, row_s = 0.0;            // wavefront 0: the row's shift and sum
+  double c_mblk = 0.0, c_d = 0.0;                   // wavefront 0: the chosen block's shift, the tile's top logit
+  float c_sum = 0.0f;                               // and its exp-sum
   if (Tf > 0.0f) {
     invT = 1.0 / (double)Tf;
     const double mref = rec_top(ts[0]);
     // wavefront 0, lane j: running choice and log-sum-exp over the groups
-    double best = -INFINITY, row_m = -INFINITY, row_s = 0.0;
+    double best = -INFINITY;
     int best_blk = 0x7fffffff;
     for (int g0 = 0; g0 < nblk; g0 += kGroup) {
       // Records of 4 chunks of 16 blocks, all requested at once: thread tid
@@ -716,15 +737,21 @@ __global__ __launch_bounds__(256) void draft_select_kernel(DraftSelectArgs a) {
     if (wave == 0) {
       const int blk = index_or(best_blk, nblk, 0);
       const int t0 = blk * kTilesPerBlock, t1 = min(t0 + kTilesPerBlock, nt);
-      double val = -INFINITY;
+      double val = -INFINITY, d = -INFINITY;
+      float sm = 0.0f;
       int ti = 0x7fffffff;
       if (t0 + lane < t1) {
         const TileRec<TL> st = ts[t0 + lane];
-        val = (rec_top(st) - mref) * invT + log((double)st.sum) + gumbel(a.seed, kDraftMid, b, rpos, lane);
+        d = rec_top(st), sm = st.sum;
+        val = (d - mref) * invT + log((double)st.sum) + gumbel(a.seed, kDraftMid, b, rpos, lane);
         ti = t0 + lane;
       }
+      // the block's shift as block_mass takes it: the fp32 maximum of its tiles' top logits
+      c_mblk = (double)wave_max((float)d);
       wave_argmax(val, ti);
-      if (lane == 0) s_tile = index_or(ti, t1, t0), s_lse = row_m * invT + log(row_s);
+      const int chosen = index_or(ti, t1, t0);
+      c_d = __shfl(d, chosen - t0), c_sum = __shfl(sm, chosen - t0);
+      if (lane == 0) s_tile = chosen, s_lse = row_m * invT + log(row_s);
     }
     __syncthreads();
     tile = s_tile, lse = s_lse;
@@ -768,6 +795,7 @@ __global__ __launch_bounds__(256) void draft_select_kernel(DraftSelectArgs a) {
     wave_argmax(lv, vi);
     const int x = index_or(vi, min(V, (tile + 1) * kTile), tile * kTile);
     const double sx = __shfl(sv, x - tile * kTile);
+    if (Tf > 0.0f) lse = exact_tile_lse(lse, sv, v < V, c_d, c_sum, c_mblk, row_m, row_s, invT);
     if (lane == 0) {
       a.draft[(size_t)b * gamma + pos] = x;
       a.logq[(size_t)b * gamma + pos] = Tf > 0.0f ? (float)(sx - lse) : 0.0f;
@@ -802,7 +830,7 @@ struct DrawShared {
   double g[3][64];           // Gumbel values: block, tile, column level
   double bm[64], part[4][64];
   float be[64];
-  double val[4], lse;
+  double val[4], lse, gm, gs;
   int idx[4], tile;
 };
 
@@ -897,7 +925,7 @@ __device__ __forceinline__ void draft_select_block(const DraftSelectArgs& a, int
       if (lane < nblk) m = s_bm[lane], e = (double)s_be[lane];
       const double gm = wave_max(m);
       const double gs = wave_sum(e > 0.0 ? e * exp((m - gm) * invT) : 0.0);
-      if (lane == 0) s_lse = gm * invT + log(gs);
+      if (lane == 0) s_lse = gm * invT + log(gs), sh.gm = gm, sh.gs = gs;
     } else if (wave == 0) {
       const double mref = s_d[0];
       // block (lane j)
@@ -968,6 +996,10 @@ __device__ __forceinline__ void draft_select_block(const DraftSelectArgs& a, int
     wave_argmax(lv, vi);
     const int x = index_or(vi, min(V, (tile + 1) * kTile), tile * kTile);
     const double sx = __shfl(sv, x - tile * kTile);
+    if (Tf > 0.0f) {
+      const int blk = tile / kTilesPerBlock;
+      lse = exact_tile_lse(lse, sv, v < V, s_d[tile], s_sum[tile], s_bm[blk], sh.gm, sh.gs, 1.0 / (double)Tf);
+    }
     if (lane == 0) {
       if (COHERENT)
         __hip_atomic_store(a.draft + (size_t)b * gamma + pos, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
