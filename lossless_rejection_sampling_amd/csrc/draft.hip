@@ -601,12 +601,37 @@ __device__ __forceinline__ void block_mass(const double (&d)[4], const float (&s
 // most of the mass, this removes nearly all of it from ln q.
 __device__ __forceinline__ double exact_tile_lse(double lse, double sv, bool live, double rec_d, float rec_sum,
                                                  double m_blk, double gm, double gs, double invT) {
-  const double ex = wave_sum(live ? exp(sv - lse) : 0.0);
+  // both shares as v_exp_f32 of exponents formed in fp64 (relative error ~1e-7)
+  const float e = live ? __builtin_amdgcn_exp2f((float)((sv - lse) * kLog2eD)) : 0.0f;
+  const double ex = (double)wave_sum(e);
   float term = 0.0f;
   if (rec_sum > 0.0f) term = rec_sum * __builtin_amdgcn_exp2f((float)((rec_d - m_blk) * (invT * kLog2eD)));
-  const double rec = (double)term * exp((m_blk - gm) * invT) / gs;
-  return lse + log1p(ex - rec);
+  const double rec = (double)(term * __builtin_amdgcn_exp2f((float)((m_blk - gm) * invT * kLog2eD))) / gs;
+  // the shares differ by the record's rounding only: log1p by its series
+  const double d = ex - rec;
+  return lse + (fabs(d) < 1e-3 ? d * (1.0 - d * (0.5 - d * (1.0 / 3.0))) : log1p(d));
 }
+
+// The copy of U[x] into the table the next position's contraction reads (only
+// with bf16 factors at r = 128 or 256, one 16-byte chunk a lane): the load in
+// the constructor, the store in store(), so that work placed between them runs
+// while the load is in flight.
+template <typename TF>
+struct HrowCopy {
+  uint4 u;
+  bool on;
+  __device__ __forceinline__ HrowCopy(const DraftSelectArgs& a, int b, int x, int pos, int lane) : u{}, on(false) {
+    if constexpr (sizeof(TF) == 2) {
+      on = a.hrows && pos + 1 < a.gamma && a.r <= 512 && lane * 8 < a.r;
+      if (on) u = reinterpret_cast<const uint4*>(static_cast<const TF*>(a.U) + (size_t)x * a.r)[lane];
+    }
+  }
+  __device__ __forceinline__ void store(const DraftSelectArgs& a, int b, int x, int lane) const {
+    if constexpr (sizeof(TF) == 2) {
+      if (on) reinterpret_cast<uint4*>(static_cast<TF*>(a.hrows) + (size_t)b * a.r)[lane] = u;
+    }
+  }
+};
 
 // ---------------------------------------------------------------------------
 // One draw per request at block position pos+1 (a workgroup of 4 wavefronts
@@ -795,18 +820,14 @@ __global__ __launch_bounds__(256) void draft_select_kernel(DraftSelectArgs a) {
     wave_argmax(lv, vi);
     const int x = index_or(vi, min(V, (tile + 1) * kTile), tile * kTile);
     const double sx = __shfl(sv, x - tile * kTile);
+    HrowCopy<TF> cp(a, b, x, pos, lane);  // requested before the log-sum-exp's last step
     if (Tf > 0.0f) lse = exact_tile_lse(lse, sv, v < V, c_d, c_sum, c_mblk, row_m, row_s, invT);
     if (lane == 0) {
       a.draft[(size_t)b * gamma + pos] = x;
       a.logq[(size_t)b * gamma + pos] = Tf > 0.0f ? (float)(sx - lse) : 0.0f;
       a.lse[(size_t)b * gamma + pos] = Tf > 0.0f ? lse : sx;
     }
-    // U[x] for the next position's contraction (bf16 factors, 16 bytes a lane)
-    if (a.hrows && pos + 1 < gamma) {
-      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const TF*>(a.U) + (size_t)x * r);
-      uint4* dst = reinterpret_cast<uint4*>(static_cast<TF*>(a.hrows) + (size_t)b * r);
-      for (int i = lane; i * 8 < r; i += 64) dst[i] = src[i];
-    }
+    cp.store(a, b, x, lane);
   }
 }
 
@@ -996,6 +1017,9 @@ __device__ __forceinline__ void draft_select_block(const DraftSelectArgs& a, int
     wave_argmax(lv, vi);
     const int x = index_or(vi, min(V, (tile + 1) * kTile), tile * kTile);
     const double sx = __shfl(sv, x - tile * kTile);
+    // U[x] for the next position's contraction is requested first; the
+    // log-sum-exp's last step runs while it is in flight
+    HrowCopy<TF> cp(a, b, x, pos, lane);
     if (Tf > 0.0f) {
       const int blk = tile / kTilesPerBlock;
       lse = exact_tile_lse(lse, sv, v < V, s_d[tile], s_sum[tile], s_bm[blk], sh.gm, sh.gs, 1.0 / (double)Tf);
@@ -1008,12 +1032,7 @@ __device__ __forceinline__ void draft_select_block(const DraftSelectArgs& a, int
       a.logq[(size_t)b * gamma + pos] = Tf > 0.0f ? (float)(sx - lse) : 0.0f;
       a.lse[(size_t)b * gamma + pos] = Tf > 0.0f ? lse : sx;
     }
-    // U[x] for the next position's contraction (bf16 factors, 16 bytes a lane)
-    if (a.hrows && pos + 1 < gamma) {
-      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const TF*>(a.U) + (size_t)x * r);
-      uint4* dst = reinterpret_cast<uint4*>(static_cast<TF*>(a.hrows) + (size_t)b * r);
-      for (int i = lane; i * 8 < r; i += 64) dst[i] = src[i];
-    }
+    cp.store(a, b, x, lane);
   }
 }
 

@@ -225,13 +225,14 @@ def test_low_temperature_bf16_round(temps):
     # bf16 logits of scale 3 through the streaming draft GEMM (r = 128): t = x + bias
     # carries one fp32 rounding at |t|'s scale, which 1/T magnifies in the tile
     # records; the draw takes the chosen tile's share of the row's mass from its
-    # fp64 recompute, so ln q stays within the log tolerance (and q <= 1).
+    # fp64 recompute, so ln q stays within the log tolerance (and q exceeds 1 by
+    # no more than the probability tolerance, 1e-6).
     rnd = wl.small_random(48, 4, 30000, 128, device=DEV, seed=37, dtype=torch.bfloat16,
                           factor_dtype=torch.bfloat16, temps=temps, std=3.0, noise=0.5)
     say(f"[low_temperature_bf16] temps={temps} B={rnd.B} gamma={rnd.gamma} V={rnd.V} r={rnd.r}")
     buf = run_gpu(rnd)
     assert ds.dspark_status(buf.workspace) == ds.DSPARK_OK
-    assert float(buf.draft_logq.max()) <= 0.0
+    assert float(buf.draft_logq.max()) <= 1e-6
     idx = np.arange(rnd.B)
     rep = compare(rnd, buf, run_oracle(rnd, idx), idx)
     check(rep, "low_temperature_bf16", max_flag_frac=0.05)
