@@ -1043,8 +1043,8 @@ __global__ __launch_bounds__(256) void draft_select_fast(DraftSelectArgs a) {
 }
 
 // The last draw of a round and the scheduler (independent of each other, both
-// bound by memory latency) in one launch: workgroups 0..B-1 draw, the rest are
-// the scheduler's workgroups.
+// bound by memory latency) in one launch: the first workgroups are the
+// scheduler's, the last B draw.
 struct SelectScheduleArgs {
   DraftSelectArgs d;
   ScheduleArgs s;
@@ -1054,8 +1054,11 @@ template <typename TL, typename TF>
 __global__ __launch_bounds__(256) void draft_select_schedule(SelectScheduleArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   __shared__ DrawShared sh;
-  if ((int)blockIdx.x < a.d.B) draft_select_block<TL, TF>(a.d, blockIdx.x, sh);
-  else schedule_block(a.s, (int)blockIdx.x - a.d.B, (int)gridDim.x - a.d.B, smem);
+  // the scheduler's workgroups come first: its chain of phases is the longer
+  // one, and the dispatcher reaches low workgroup indices first
+  const int ns = (int)gridDim.x - a.d.B;
+  if ((int)blockIdx.x < ns) schedule_block(a.s, (int)blockIdx.x, ns, smem);
+  else draft_select_block<TL, TF>(a.d, (int)blockIdx.x - ns, sh);
 }
 
 // ---------------------------------------------------------------------------
