@@ -203,6 +203,24 @@ def test_greedy_target_ties_lowest_index():
     assert np.all(n[0::2] == 0) and np.all(n[1::2] == rnd.gamma)
 
 
+@pytest.mark.parametrize("case", [
+    dict(B=4, gamma=3, V=1, r=1, dtype=torch.float32, fdt=torch.bfloat16, temps=(1.0, 0.0)),
+    dict(B=3, gamma=2, V=3, r=1, dtype=torch.bfloat16, fdt=torch.bfloat16, temps=(1.0, 0.5, 0.0)),
+    dict(B=1, gamma=1, V=64, r=5, dtype=torch.bfloat16, fdt=torch.float32, temps=(1.0,)),
+    dict(B=2, gamma=16, V=7, r=2, dtype=torch.float32, fdt=torch.float32, temps=(0.9, 0.0)),
+], ids=["V1_r1", "V3_r1", "B1_gamma1", "gamma16_V7"])
+def test_degenerate_sizes(case):
+    # the smallest sizes the ABI allows: a one-token vocabulary (p = q = 1: every
+    # position accepted, the bonus token 0), rank 1, one request of one position,
+    # the longest block over a vocabulary smaller than one tile
+    rnd = wl.small_random(case["B"], case["gamma"], case["V"], case["r"], device=DEV, seed=5, dtype=case["dtype"],
+                          factor_dtype=case["fdt"], temps=case["temps"])
+    buf = _full(rnd, f"degenerate_{case['V']}x{case['r']}")
+    if rnd.V == 1:
+        assert torch.all(buf.num_accepted == rnd.gamma)
+        assert torch.all(buf.out_tokens == 0)
+
+
 def test_low_temperature_round():
     # T = 0.05 on fp32 logits of scale 8 (|z| / T up to ~700): block sums and
     # residual masses must carry no error proportional to the row maximum over T.
