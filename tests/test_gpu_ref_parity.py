@@ -11,7 +11,8 @@ here.  The sizes select every kernel path of the round: the streaming draft
 GEMM (bf16 logits and factors, V a multiple of 8, r = 128 or 256), the
 LDS-staged GEMM (r = 64), the generic paths (V not a multiple of 8, fp32
 logits, fp32 factors), scheduler budgets, random budgets with position
-offsets, and the full budget.
+offsets, and the full budget; and a round whose logits exceed 4 GiB (the
+64-bit addressed paths), compared on requests sampled across the batch.
 """
 
 import os
@@ -92,3 +93,31 @@ def test_whole_batch_against_the_c_oracle(k):
     # the round exercises both outcomes of the accept test
     n = buf.num_accepted.cpu().numpy()
     assert (n < want.budget).any() and (n == want.budget).any()
+
+
+def test_logits_beyond_4_gib():
+    # B = 1024, gamma = 16, V = 151936 in bf16: target and backbone logits of
+    # 5.3 and 5.0 GB, beyond the 32-bit byte offsets of the coalesced kernels, so
+    # the round runs on the 64-bit addressed paths.  Requests sampled across the
+    # batch (the last ones past the 4 GiB mark) against the C oracle with their
+    # own request ids.
+    B, gamma, V, r = 1024, 16, 151936, 256
+    rnd = wl.small_random(B, gamma, V, r, device=DEV, seed=77, dtype=BF16, factor_dtype=BF16, temps=(1.0, 0.0, 0.8))
+    rng = np.random.default_rng(77)
+    rnd.budget = torch.tensor(rng.integers(0, gamma + 1, B), dtype=torch.int32, device=DEV)
+    assert B * (gamma + 1) * V * 2 > 1 << 32
+    say(f"[c oracle beyond 4 GiB] B={B} gamma={gamma} V={V} r={r}")
+    buf = run_gpu(rnd)
+    assert ds.dspark_status(buf.workspace) == ds.DSPARK_OK
+    idx = np.array([0, 1, 257, 511, 600, 777, 1000, 1021, 1022, 1023])
+    h = wl.to_host
+    t = torch.as_tensor(idx, dtype=torch.long, device=DEV)
+    pick = lambda x: h(x.index_select(0, t))
+    target, base, prev0, T = pick(rnd.target), pick(rnd.base), pick(rnd.prev0), pick(rnd.temperature)
+    U, W = h(rnd.U), h(rnd.W)
+    budget = h(rnd.budget)[idx].astype(np.int32)
+    ids = idx.astype(np.int32)
+    dr = ref.draft_round(base, U, W, prev0, T, rnd.seed, None, ids)
+    vr = ref.verify(target, base, U, W, prev0, dr.tokens, T, rnd.seed, budget, None, ids)
+    rep = compare(rnd, buf, od.RoundResult(dr, budget, None, vr), idx)
+    check(rep, "beyond_4gib")
