@@ -61,6 +61,8 @@ def test_tiny_round():
     dict(B=40, gamma=3, V=24000, r=128, dtype=torch.bfloat16, fdt=torch.bfloat16, temps=(1.3, 0.0)),
     # more than 4096 tiles (the general draw) over bf16 streams: 4219 tiles, 123 in a partial last round
     dict(B=4, gamma=2, V=270000, r=128, dtype=torch.bfloat16, fdt=torch.bfloat16, temps=(1.0, 0.0)),
+    # the general draw over fp32 logits (16-byte records with the tile-maximum shift): 4110 tiles
+    dict(B=4, gamma=2, V=263000, r=16, dtype=torch.float32, fdt=torch.bfloat16, temps=(1.0, 0.0, 0.5)),
 ])
 def test_small_rounds(case):
     rnd = wl.small_random(case["B"], case["gamma"], case["V"], case["r"], device=DEV, seed=case["B"] + case["V"],
