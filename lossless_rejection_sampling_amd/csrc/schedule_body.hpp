@@ -171,7 +171,8 @@ __device__ __forceinline__ void schedule_block(const ScheduleArgs& a, int bid, i
   // stores to complete before the barrier, and the ticket is taken after it.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  if (tid == 0) s_last = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nblocks - 1;
+  if (tid == 0)
+    s_last = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(nblocks - 1);
   __syncthreads();
   if (!s_last) return;
   // the ranks of this thread's first request, requested with the cut's inputs
