@@ -675,6 +675,57 @@ __device__ __forceinline__ double dot_part(const TF* h, const TF* w, int k0, int
   return acc;
 }
 
+// The chosen tile's 64 dot products U[prev] . W[v] (bf16 factors, r = 64 nj,
+// nj = 2 or 4),
+// in fp64 from exact bf16 x bf16 products.  Lane l of wavefront w takes the
+// rows v0 + 16 w + (l >> 3) + 8 h (h = 0, 1) of W and the 16-byte chunks
+// (l & 7) + 8 j of each, so that every load instruction reads eight whole
+// 128-byte lines; the U[prev] chunks (l & 7) + 8 j are loaded by the caller as
+// soon as prev is known.  Eight lanes then sum a row's partials; lane l & 7 == 0
+// returns rows h = 0 and 1 in dot[0], dot[1].
+struct TileDot {
+  static constexpr int kMaxJ = 4;
+  uint4 hq[kMaxJ];
+  int nj;
+  __device__ __forceinline__ void load_h(const uint16_t* h, int lane) {
+#pragma unroll
+    for (int j = 0; j < kMaxJ; ++j)
+      if (j < nj) hq[j] = reinterpret_cast<const uint4*>(h)[(lane & 7) + 8 * j];
+  }
+  __device__ __forceinline__ void dot(const uint16_t* W, int v0, int V, int wave, int lane, double (&out)[2]) const {
+    uint4 wv[2][kMaxJ];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int v = min(v0 + 16 * wave + (lane >> 3) + 8 * hh, V - 1);
+      const uint4* row = reinterpret_cast<const uint4*>(W + (size_t)v * (64 * nj));
+#pragma unroll
+      for (int j = 0; j < kMaxJ; ++j)
+        if (j < nj) wv[hh][j] = row[(lane & 7) + 8 * j];
+    }
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      // a product of two bf16 values is exact in fp32; the sum runs in fp64
+      double c[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+      for (int j = 0; j < kMaxJ; ++j) {
+        if (j >= nj) break;
+        const uint32_t hv[4] = {hq[j].x, hq[j].y, hq[j].z, hq[j].w};
+        const uint32_t ww[4] = {wv[hh][j].x, wv[hh][j].y, wv[hh][j].z, wv[hh][j].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          c[q] += (double)(__uint_as_float(hv[q] << 16) * __uint_as_float(ww[q] << 16));
+          c[q] += (double)(__uint_as_float(hv[q] & 0xffff0000u) * __uint_as_float(ww[q] & 0xffff0000u));
+        }
+      }
+      double t = (c[0] + c[1]) + (c[2] + c[3]);
+      t += __shfl_xor(t, 1);
+      t += __shfl_xor(t, 2);
+      t += __shfl_xor(t, 4);
+      out[hh] = t;
+    }
+  }
+};
+
 // Draw of block position `pos` for request b = blockIdx.x from the tile
 // records (three-level exact Gumbel-max: block, tile, column), then the fp64
 // recompute of the chosen tile for the token and its log-probability.
@@ -916,6 +967,12 @@ __device__ __forceinline__ void draft_select_block(const DraftSelectArgs& a, int
   if (wave < 3 && (wave != 0 || lane < nblk)) s_g[wave][lane] = gumbel(a.seed, kDraftTop + wave, b, rpos, lane);
   const float Tf = checked_temp(T_raw, a.status);
   const int prev = checked_token(prev_raw, V, a.status, pos == 0 ? kBadPrev : kBadDraft);
+  const TF* h = static_cast<const TF*>(a.U) + (size_t)prev * r;
+  // bf16 factors at r = 128 or 256: the recompute's U[prev] chunks now, while
+  // the records are in flight
+  TileDot td;
+  td.nj = sizeof(TF) == 2 && (r == 128 || r == 256) ? r / 64 : 0;
+  if (td.nj) td.load_h(reinterpret_cast<const uint16_t*>(h), lane);
 
   // 2. records to LDS; block statistics over 16-lane groups
 #pragma unroll
@@ -992,19 +1049,26 @@ __device__ __forceinline__ void draft_select_block(const DraftSelectArgs& a, int
     tile = index_or(bt, nt, 0);
   }
 
-  // 3. fp64 recompute of the chosen tile (rank split over the wavefronts)
+  // 3. fp64 recompute of the chosen tile
   const TL* brow = static_cast<const TL*>(a.base) + ((size_t)b * gamma + pos) * V;
-  const TF* h = static_cast<const TF*>(a.U) + (size_t)prev * r;
   const int v = tile * kTile + lane;
   const float xb = load_logit(brow + min(v, V - 1));  // unconditional: issued with the factor rows
-  const int kq = (r + 3) / 4, k0 = min(wave * kq, r), k1 = min(k0 + kq, r);
-  s_part[wave][lane] = v < V ? dot_part<TF>(h, static_cast<const TF*>(a.Wt) + (size_t)v * r, k0, k1) : 0.0;
+  if (td.nj) {
+    double dt[2];
+    td.dot(static_cast<const uint16_t*>(a.Wt), tile * kTile, V, wave, lane, dt);
+    if ((lane & 7) == 0) s_part[0][16 * wave + (lane >> 3)] = dt[0], s_part[0][16 * wave + (lane >> 3) + 8] = dt[1];
+  } else {
+    // the rank split over the four wavefronts
+    const int kq = (r + 3) / 4, k0 = min(wave * kq, r), k1 = min(k0 + kq, r);
+    s_part[wave][lane] = v < V ? dot_part<TF>(h, static_cast<const TF*>(a.Wt) + (size_t)v * r, k0, k1) : 0.0;
+  }
   __syncthreads();
   if (wave == 0) {
     double lv = -INFINITY, sv = -INFINITY;
     int vi = 0x7fffffff;
     if (v < V) {
-      const double d = (double)xb + ((s_part[0][lane] + s_part[1][lane]) + (s_part[2][lane] + s_part[3][lane]));
+      const double dot = td.nj ? s_part[0][lane] : (s_part[0][lane] + s_part[1][lane]) + (s_part[2][lane] + s_part[3][lane]);
+      const double d = (double)xb + dot;
       if (Tf > 0.0f) {
         sv = d / (double)Tf;
         lv = sv + s_g[2][lane];
