@@ -675,57 +675,6 @@ __device__ __forceinline__ double dot_part(const TF* h, const TF* w, int k0, int
   return acc;
 }
 
-// The chosen tile's 64 dot products U[prev] . W[v] (bf16 factors, r = 64 nj,
-// nj = 2 or 4),
-// in fp64 from exact bf16 x bf16 products.  Lane l of wavefront w takes the
-// rows v0 + 16 w + (l >> 3) + 8 h (h = 0, 1) of W and the 16-byte chunks
-// (l & 7) + 8 j of each, so that every load instruction reads eight whole
-// 128-byte lines; the U[prev] chunks (l & 7) + 8 j are loaded by the caller as
-// soon as prev is known.  Eight lanes then sum a row's partials; lane l & 7 == 0
-// returns rows h = 0 and 1 in dot[0], dot[1].
-struct TileDot {
-  static constexpr int kMaxJ = 4;
-  uint4 hq[kMaxJ];
-  int nj;
-  __device__ __forceinline__ void load_h(const uint16_t* h, int lane) {
-#pragma unroll
-    for (int j = 0; j < kMaxJ; ++j)
-      if (j < nj) hq[j] = reinterpret_cast<const uint4*>(h)[(lane & 7) + 8 * j];
-  }
-  __device__ __forceinline__ void dot(const uint16_t* W, int v0, int V, int wave, int lane, double (&out)[2]) const {
-    uint4 wv[2][kMaxJ];
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const int v = min(v0 + 16 * wave + (lane >> 3) + 8 * hh, V - 1);
-      const uint4* row = reinterpret_cast<const uint4*>(W + (size_t)v * (64 * nj));
-#pragma unroll
-      for (int j = 0; j < kMaxJ; ++j)
-        if (j < nj) wv[hh][j] = row[(lane & 7) + 8 * j];
-    }
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      // a product of two bf16 values is exact in fp32; the sum runs in fp64
-      double c[4] = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-      for (int j = 0; j < kMaxJ; ++j) {
-        if (j >= nj) break;
-        const uint32_t hv[4] = {hq[j].x, hq[j].y, hq[j].z, hq[j].w};
-        const uint32_t ww[4] = {wv[hh][j].x, wv[hh][j].y, wv[hh][j].z, wv[hh][j].w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          c[q] += (double)(__uint_as_float(hv[q] << 16) * __uint_as_float(ww[q] << 16));
-          c[q] += (double)(__uint_as_float(hv[q] & 0xffff0000u) * __uint_as_float(ww[q] & 0xffff0000u));
-        }
-      }
-      double t = (c[0] + c[1]) + (c[2] + c[3]);
-      t += __shfl_xor(t, 1);
-      t += __shfl_xor(t, 2);
-      t += __shfl_xor(t, 4);
-      out[hh] = t;
-    }
-  }
-};
-
 // Draw of block position `pos` for request b = blockIdx.x from the tile
 // records (three-level exact Gumbel-max: block, tile, column), then the fp64
 // recompute of the chosen tile for the token and its log-probability.

@@ -475,7 +475,8 @@ __device__ __forceinline__ double residual_at(const VerifyArgs& a, int b, const 
 //      the state; the Gumbel values of the three levels are computed while the
 //      previous token, the draft log-sum-exp and the masses land;
 //   2. the chosen block's tile masses again (an L2 hit);
-//   3. the tile's factor rows with its backbone and target logits.
+//   3. the tile's factor rows with its backbone and target logits (the U[prev]
+//      chunks of the recompute are requested as soon as prev is known).
 // Block masses sum in the order of the per-block loop (wave by wave, blocks in
 // increasing order), and each wave takes one logarithm per lane for its blocks.
 template <typename TL, typename TF>
@@ -512,6 +513,13 @@ __global__ __launch_bounds__(256) void residual_select_kernel(VerifyArgs a) {
   }
   const int prev_raw = n == 0 ? a.prev0[b] : a.draft[(size_t)b * gamma + n - 1];
   const double lse_q = a.draft_lse[(size_t)b * gamma + n];
+  const int prev = checked_token(prev_raw, V, a.status, n == 0 ? kBadPrev : kBadDraft);
+  const TF* h = static_cast<const TF*>(a.U) + (size_t)prev * r;
+  // bf16 factors at r = 128 or 256: the recompute's U[prev] chunks now, while
+  // the block draw runs
+  TileDot td;
+  td.nj = sizeof(TF) == 2 && (r == 128 || r == 256) ? r / 64 : 0;
+  if (td.nj) td.load_h(reinterpret_cast<const uint16_t*>(h), lane);
   if (wave == 1) s_gmid[lane] = gumbel(a.seed, kFinalMid, b, rpos, lane);
   if (wave == 2) s_gleaf[lane] = gumbel(a.seed, kFinalLeaf, b, rpos, lane);
 
@@ -573,25 +581,31 @@ __global__ __launch_bounds__(256) void residual_select_kernel(VerifyArgs a) {
   wave_argmax(val, ti);
   ti = index_or(ti, t1, t0);
 
-  // Markov bias of the chosen tile in fp64, rank split over the wavefronts; the
-  // column's backbone and target logits come in the same round trip
+  // Markov bias of the chosen tile in fp64; the column's backbone and target
+  // logits come in the same round trip
   const int v = ti * kTile + lane;
-  const int kq = (r + 3) / 4, k0 = min(wave * kq, r), k1 = min(k0 + kq, r);
-  const int prev = checked_token(prev_raw, V, a.status, n == 0 ? kBadPrev : kBadDraft);
-  const TF* h = static_cast<const TF*>(a.U) + (size_t)prev * r;
   double xb = 0.0, zt = 0.0;
   if (wave == 0 && v < V) {
     const TL* brow = static_cast<const TL*>(a.base) + ((size_t)b * gamma + n) * V;
     xb = (double)load_logit(brow + v), zt = (double)load_logit(trow + v);
   }
-  s_part[wave][lane] = v < V ? dot_range<TF>(h, static_cast<const TF*>(a.Wt) + (size_t)v * r, k0, k1) : 0.0;
+  if (td.nj) {
+    double dt[2];
+    td.dot(static_cast<const uint16_t*>(a.Wt), ti * kTile, V, wave, lane, dt);
+    if ((lane & 7) == 0) s_part[0][16 * wave + (lane >> 3)] = dt[0], s_part[0][16 * wave + (lane >> 3) + 8] = dt[1];
+  } else {
+    // the rank split over the four wavefronts
+    const int kq = (r + 3) / 4, k0 = min(wave * kq, r), k1 = min(k0 + kq, r);
+    s_part[wave][lane] = v < V ? dot_range<TF>(h, static_cast<const TF*>(a.Wt) + (size_t)v * r, k0, k1) : 0.0;
+  }
   __syncthreads();
   if (wave != 0) return;
   double lv = -INFINITY, lp = -INFINITY;
   int vi = 0x7fffffff;
   if (v < V) {
     double p;
-    const double bias = (s_part[0][lane] + s_part[1][lane]) + (s_part[2][lane] + s_part[3][lane]);
+    const double bias =
+        td.nj ? s_part[0][lane] : (s_part[0][lane] + s_part[1][lane]) + (s_part[2][lane] + s_part[3][lane]);
     const double rv = residual_from(xb, zt, st, invT, lse_q, bias, &p);
     const double g = s_gleaf[lane];
     if (rv > 0.0) lv = log(rv) + g, vi = v;
