@@ -840,10 +840,12 @@ __global__ __launch_bounds__(256) void draft_select_kernel(DraftSelectArgs a) {
 //   2. Records go to LDS; 16-lane groups reduce each block; wave 0 draws the
 //      block, then the tile from the LDS copy, while wave 1 forms the row's
 //      log-sum-exp.
-//   3. The chosen tile is recomputed in fp64 (rank split over the four
+//   3. The chosen tile is recomputed in fp64 (bf16 factors at r = 128 or 256:
+//      eight lanes a factor row, whole lines per load, the U[prev] chunks
+//      requested in step 1; otherwise the rank split over the four
 //      wavefronts), the column drawn, and U[x] copied for the next position.
 // The arithmetic of every value that decides a draw is that of
-// draft_select_kernel.
+// draft_select_kernel, up to the order of the fp64 sums of exact products.
 constexpr int kDrawMaxTiles = kTilesPerBlock * 64;
 struct DrawShared {
   double d[kDrawMaxTiles];   // largest draft logit of every tile
@@ -1156,7 +1158,7 @@ __global__ __launch_bounds__(512, 1) void gemm_draft_stream(GemmArgs a) {
   // Tiles of this workgroup.  Workgroups are dealt to the 8 XCDs round robin
   // (blockIdx.x % 8), each XCD with its own L2.  In the nt / G full rounds the
   // G tiles of a round are split into 8 runs of G / 8 adjacent tiles, one per
-  // XCD, so the 16-byte records of neighbouring tiles of a row meet in one L2
+  // XCD, so the 8-byte records of neighbouring tiles of a row meet in one L2
   // and leave it as whole lines.  The nt % G leftover tiles go to the workgroups
   // of even XCDs first (odd XCDs stream measurably slower in this kernel).
   // Without a multiple of 8 workgroups the order is plain: tile bx + j G.

@@ -469,7 +469,8 @@ __device__ __forceinline__ double residual_at(const VerifyArgs& a, int b, const 
 
 // One workgroup of 4 wavefronts per request that rejected: block and tile from
 // the residual tile masses, column from an fp64 recompute of the chosen tile
-// (rank split over the wavefronts).  Memory round trips on the critical path:
+// (TileDot for bf16 factors at r = 128 or 256, else the rank split over the
+// wavefronts).  Memory round trips on the critical path:
 //   1. the request's state with the tile masses of the first 64 blocks (wave w,
 //      lane l: tile l of blocks w, w + 4, ...), the masses being independent of
 //      the state; the Gumbel values of the three levels are computed while the
