@@ -264,14 +264,13 @@ __device__ __forceinline__ int index_or(int i, int limit, int fallback) {
   return (i >= 0 && i < limit) ? i : fallback;
 }
 
-// The chosen tile's 64 dot products U[prev] . W[v] (bf16 factors, r = 64 nj,
-// nj = 2 or 4),
-// in fp64 from exact bf16 x bf16 products.  Lane l of wavefront w takes the
-// rows v0 + 16 w + (l >> 3) + 8 h (h = 0, 1) of W and the 16-byte chunks
-// (l & 7) + 8 j of each, so that every load instruction reads eight whole
-// 128-byte lines; the U[prev] chunks (l & 7) + 8 j are loaded by the caller as
-// soon as prev is known.  Eight lanes then sum a row's partials; lane l & 7 == 0
-// returns rows h = 0 and 1 in dot[0], dot[1].
+// The chosen tile's 64 dot products U[prev] . W[v] (bf16 factors, r = 64 nj
+// with nj = 2 or 4) in fp64 from exact bf16 x bf16 products, by a workgroup of
+// four wavefronts.  Lane l of wavefront w takes the rows v0 + 16 w + (l >> 3)
+// + 8 h (h = 0, 1) of W and the 16-byte chunks (l & 7) + 8 j of each, so that
+// every load instruction reads eight whole 128-byte lines; load_h() fetches the
+// matching U[prev] chunks.  Eight lanes then sum a row's partials, and every
+// lane of the eight returns rows h = 0 and 1 in out[0], out[1].
 struct TileDot {
   static constexpr int kMaxJ = 4;
   uint4 hq[kMaxJ];

@@ -919,11 +919,6 @@ __device__ __forceinline__ void draft_select_block(const DraftSelectArgs& a, int
   const float Tf = checked_temp(T_raw, a.status);
   const int prev = checked_token(prev_raw, V, a.status, pos == 0 ? kBadPrev : kBadDraft);
   const TF* h = static_cast<const TF*>(a.U) + (size_t)prev * r;
-  // bf16 factors at r = 128 or 256: the recompute's U[prev] chunks now, while
-  // the records are in flight
-  TileDot td;
-  td.nj = sizeof(TF) == 2 && (r == 128 || r == 256) ? r / 64 : 0;
-  if (td.nj) td.load_h(reinterpret_cast<const uint16_t*>(h), lane);
 
   // 2. records to LDS; block statistics over 16-lane groups
 #pragma unroll
@@ -1000,7 +995,13 @@ __device__ __forceinline__ void draft_select_block(const DraftSelectArgs& a, int
     tile = index_or(bt, nt, 0);
   }
 
-  // 3. fp64 recompute of the chosen tile
+  // 3. fp64 recompute of the chosen tile (bf16 factors at r = 128 or 256: its
+  // U[prev] chunks and W rows in one round trip; requested any earlier, these
+  // conditional loads make the compiler's waits for the tile records wait for
+  // them too)
+  TileDot td;
+  td.nj = sizeof(TF) == 2 && (r == 128 || r == 256) ? r / 64 : 0;
+  if (td.nj) td.load_h(reinterpret_cast<const uint16_t*>(h), lane);
   const TL* brow = static_cast<const TL*>(a.base) + ((size_t)b * gamma + pos) * V;
   const int v = tile * kTile + lane;
   const float xb = load_logit(brow + min(v, V - 1));  // unconditional: issued with the factor rows

@@ -476,8 +476,7 @@ __device__ __forceinline__ double residual_at(const VerifyArgs& a, int b, const 
 //      the state; the Gumbel values of the three levels are computed while the
 //      previous token, the draft log-sum-exp and the masses land;
 //   2. the chosen block's tile masses again (an L2 hit);
-//   3. the tile's factor rows with its backbone and target logits (the U[prev]
-//      chunks of the recompute are requested as soon as prev is known).
+//   3. the tile's factor rows and U[prev] with its backbone and target logits.
 // Block masses sum in the order of the per-block loop (wave by wave, blocks in
 // increasing order), and each wave takes one logarithm per lane for its blocks.
 template <typename TL, typename TF>
@@ -514,13 +513,6 @@ __global__ __launch_bounds__(256) void residual_select_kernel(VerifyArgs a) {
   }
   const int prev_raw = n == 0 ? a.prev0[b] : a.draft[(size_t)b * gamma + n - 1];
   const double lse_q = a.draft_lse[(size_t)b * gamma + n];
-  const int prev = checked_token(prev_raw, V, a.status, n == 0 ? kBadPrev : kBadDraft);
-  const TF* h = static_cast<const TF*>(a.U) + (size_t)prev * r;
-  // bf16 factors at r = 128 or 256: the recompute's U[prev] chunks now, while
-  // the block draw runs
-  TileDot td;
-  td.nj = sizeof(TF) == 2 && (r == 128 || r == 256) ? r / 64 : 0;
-  if (td.nj) td.load_h(reinterpret_cast<const uint16_t*>(h), lane);
   if (wave == 1) s_gmid[lane] = gumbel(a.seed, kFinalMid, b, rpos, lane);
   if (wave == 2) s_gleaf[lane] = gumbel(a.seed, kFinalLeaf, b, rpos, lane);
 
@@ -583,7 +575,13 @@ __global__ __launch_bounds__(256) void residual_select_kernel(VerifyArgs a) {
   ti = index_or(ti, t1, t0);
 
   // Markov bias of the chosen tile in fp64; the column's backbone and target
-  // logits come in the same round trip
+  // logits come in the same round trip (with bf16 factors at r = 128 or 256,
+  // so do the U[prev] chunks)
+  const int prev = checked_token(prev_raw, V, a.status, n == 0 ? kBadPrev : kBadDraft);
+  const TF* h = static_cast<const TF*>(a.U) + (size_t)prev * r;
+  TileDot td;
+  td.nj = sizeof(TF) == 2 && (r == 128 || r == 256) ? r / 64 : 0;
+  if (td.nj) td.load_h(reinterpret_cast<const uint16_t*>(h), lane);
   const int v = ti * kTile + lane;
   double xb = 0.0, zt = 0.0;
   if (wave == 0 && v < V) {
