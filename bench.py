@@ -13,7 +13,7 @@ grants) per round / seconds per round.  Three copies of the inputs are used in
 rotation so that no round finds the previous round's data in the 256 MB
 Infinity Cache.
 
-Prints one JSON line.  With --gpus N > 1 it exits: this build runs on one GPU.
+Prints one JSON line.  With --gpus N > 1 it exits: the library runs on one GPU.
 """
 
 from __future__ import annotations
@@ -119,8 +119,8 @@ def main():
         calibrate_copy()
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU layout is "
-              "a design note, not part of this build", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has no "
+              "multi-GPU path", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

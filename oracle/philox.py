@@ -11,7 +11,7 @@ and 2 by two fixed odd constants, keeps both halves of the 64-bit products, and
 mixes the high halves with words 1 and 3 and the round key; the key is advanced
 by two Weyl constants between rounds.
 
-Counter layout of one draw (the reading written down for this build):
+Counter layout of one draw (the reading of the pages taken here):
     key     = (seed mod 2^32, seed div 2^32)
     counter = (n div 4, position, request, stream)
     word    = n mod 4 of the four output words

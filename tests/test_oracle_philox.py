@@ -2,7 +2,7 @@
 
 The exact output bits are pinned against an independent implementation of the
 same published generator: PyTorch ships a header-only Philox4x32-10 engine
-(ATen/core/PhiloxRNGEngine.h); a small driver compiled here from that header
+(ATen/core/PhiloxRNGEngine.h); a small program compiled here from that header
 (a library routine, not code of this repository) is run on the same counters.
 The statistical properties the method needs (uniform, independent draws) are
 pinned by chi-square and correlation tests.
@@ -19,7 +19,7 @@ from scipy import stats
 
 from oracle import philox as px
 
-_DRIVER = r"""
+_PROGRAM = r"""
 #include <ATen/core/PhiloxRNGEngine.h>
 #include <cstdio>
 int main() {
@@ -51,7 +51,7 @@ def torch_philox():
     d = tempfile.mkdtemp()
     src, exe = os.path.join(d, "drv.cpp"), os.path.join(d, "drv")
     with open(src, "w") as f:
-        f.write(_DRIVER)
+        f.write(_PROGRAM)
     subprocess.run(["g++", "-std=c++17", "-O1", "-I", inc, src, "-o", exe], check=True)
 
     def run(triples):
