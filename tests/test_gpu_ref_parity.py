@@ -8,7 +8,8 @@ The C oracle (plain fp64 loops, OpenMP over requests) is pinned against the
 numpy oracle by tests/test_oracle_ref.py and is fast enough that whole batches
 with tens of thousands of vocabulary entries are compared request by request
 here.  The sizes select every kernel path of the round: the streaming draft
-GEMM (bf16 logits and factors, V a multiple of 8, r = 128 or 256), the
+GEMM (bf16 logits and factors, V a multiple of 8, r = 128 or 256; one slot
+group, and two with the second partly filled at B = 300), the
 LDS-staged GEMM (r = 64), the generic paths (V not a multiple of 8, fp32
 logits, fp32 factors), scheduler budgets, random budgets with position
 offsets, and the full budget; and a round whose logits exceed 4 GiB (the
@@ -45,6 +46,7 @@ CASES = [
     ("fp32 logits", 64, 5, 50000, 256, F32, BF16, (1.0, 0.5, 0.0), "scheduled"),
     ("fp32 factors r64", 48, 4, 40000, 64, BF16, F32, (1.2, 0.0), "random"),
     ("LDS-staged r64", 128, 4, 60000, 64, BF16, BF16, (1.0,), "full"),
+    ("streaming two slot groups the second partial", 300, 3, 50000, 256, BF16, BF16, (1.0, 0.0, 0.6), "random"),
 ]
 
 
