@@ -98,3 +98,29 @@ def test_source_hash_gates_the_bench_figure(runs, tmp_path, monkeypatch):
 def test_committed_summary_is_readable():
     rec = counters.read_summary(os.path.join(os.path.dirname(bench.__file__), "profiles", "draft_gemm_B256_traffic.md"))
     assert rec is not None and rec["kernel"] == "draft_gemm" and rec["bytes"] > 0
+
+
+def test_algorithmic_bytes_of_the_headline_round():
+    # the per-launch algorithmic work of the bench line, hand-computed for the
+    # DSpark-5 round at B = 256, gamma = 5, V = 151936, r = 256 in bf16
+    import torch
+    from types import SimpleNamespace
+
+    bf = torch.empty(0, dtype=torch.bfloat16)
+    rnd = SimpleNamespace(B=256, gamma=5, V=151936, r=256, base=bf, U=bf)
+    a = bench.algorithmic(rnd, budgets=None, emitted=[583], rejected=196)
+    # draft step: backbone rows 256 x 151936 x 2 B = 77 791 232, W2 once per
+    # round 151936 x 256 x 2 B / 5 = 15 558 246.4, U rows 256 x 256 x 2 B = 131 072
+    assert a["draft_gemm"]["bytes"] == pytest.approx(93_480_550.4, abs=1e-3)
+    assert a["draft_gemm"]["flops"] == 19_914_555_392.0          # 2 B r V
+    assert a["draft_gemm"]["overhead_bytes"] == 256 * 2374 * 8   # 8-byte tile records
+    # verification: the 583 target rows up to the first rejection
+    assert a["row_stats"]["bytes"] == 583 * 151936 * 2 == 177_157_376
+    # residual: one target and one backbone row for each of 196 rejected requests, W2 once
+    assert a["residual_gemm"]["bytes"] == 196 * 2 * 151936 * 2 + 151936 * 256 * 2 == 196_909_056
+    # resident round: five steps' rows and W2 once
+    assert a["draft_round"]["bytes"] == 5 * (77_791_232 + 131_072) + 77_791_232
+    # fp32 logits keep a 16-byte record (shift, max, exp-sum)
+    f32 = torch.empty(0, dtype=torch.float32)
+    a32 = bench.algorithmic(SimpleNamespace(B=256, gamma=5, V=151936, r=256, base=f32, U=bf), None, [583], 196)
+    assert a32["draft_gemm"]["overhead_bytes"] == 256 * 2374 * 16
