@@ -8,7 +8,10 @@
 * Expected tokens per pass (same page, section "Rendement attendu ..."): the
   closed form and its worked value at gamma = 4, alpha = 0.7.
 * Analytic acceptance ("DSpark, la bozza ...", section "Verificare meglio, non di
-  più", eq. c*): P(accept) = 1 - TV(p, q) = sum_v min(p_v, q_v).
+  più", eq. c*): P(accept) = 1 - TV(p, q) = sum_v min(p_v, q_v), at the first
+  position and, given the drafted token, at the second.
+* The draft's Markov conditioning ("DSpark, la bozza ...", eq. p_k): the drafted
+  pairs (x_1, x_2) follow q_1(x_1 | prev0) q_2(x_2 | x_1).
 * Special cases: greedy = longest matching prefix, q = p always accepts,
   disjoint supports always reject; structural invariants.
 """
@@ -211,6 +214,60 @@ def test_yield_approaches_block_plus_one_at_high_alpha():
     # the page notes the yield nears gamma + 1 at alpha = 0.9
     g = 4
     assert (1 - 0.9 ** (g + 1)) / (1 - 0.9) > 0.8 * (g + 1)
+
+
+def draft_conditional_pvalue(m=od, T=1.0, B=4000, seed=31):
+    """p-value of the drafted pairs (x_1, x_2) of B rounds against the joint
+    q_1(x_1 | prev0) q_2(x_2 | x_1) of the draft definition ("DSpark, la bozza
+    ...", eq. p_k: the Markov bias of position k is that of the token drawn at
+    k - 1)."""
+    pb = Problem(2, T, seed=17)
+    base, prev0, temps = pb.batch(B)
+    dr = m.draft_round(base, pb.U, pb.W, prev0, temps, seed)
+    x1, x2 = dr.tokens[:, 0].astype(int), dr.tokens[:, 1].astype(int)
+    q1 = pb.q(1, pb.prev0)
+    exp = np.array([q1[a] * pb.q(2, a)[c] for a in range(V8) for c in range(V8)]) * B
+    obs = np.bincount(x1 * V8 + x2, minlength=V8 * V8).astype(float)
+    big = exp >= 5
+    return stats.chisquare(np.append(obs[big], obs[~big].sum()), np.append(exp[big], exp[~big].sum())).pvalue
+
+
+def accept_rate_pvalue(m=od, T=1.0, B=6000, seed=37):
+    """p-value of the accept counts of B rounds at position 1 and, grouped by
+    the drafted x_1, at position 2, against sum_v min(p_k, q_k) of the
+    problem's own distributions (the probability that u < min(1, p/q) when
+    x ~ q; "Les mathématiques ...", section "La garantie de l'échantillonnage
+    par rejet")."""
+    pb = Problem(2, T, seed=19)
+    base, prev0, temps = pb.batch(B)
+    dr = m.draft_round(base, pb.U, pb.W, prev0, temps, seed)
+    tgt = pb.target_for(dr.tokens)
+    vr = m.verify(tgt, base, pb.U, pb.W, prev0, dr.tokens, temps, seed, np.full(B, 2))
+    n = np.asarray(vr.num_accepted)
+    c1 = np.minimum(pb.p(()), pb.q(1, pb.prev0)).sum()
+    k1 = int((n >= 1).sum())
+    chi2, df = (k1 - B * c1) ** 2 / (B * c1 * (1 - c1)), 1
+    x1 = dr.tokens[:, 0]
+    for a in range(V8):
+        sel = (n >= 1) & (x1 == a)
+        N = int(sel.sum())
+        c2 = np.minimum(pb.p((a,)), pb.q(2, a)).sum()
+        if N < 30 or not 0 < c2 < 1:
+            continue
+        k = int((n[sel] >= 2).sum())
+        chi2 += (k - N * c2) ** 2 / (N * c2 * (1 - c2))
+        df += 1
+    return stats.chi2.sf(chi2, df)
+
+
+@pytest.mark.parametrize("T", [1.0, 0.7])
+def test_draft_tokens_follow_the_markov_conditionals(T):
+    assert draft_conditional_pvalue(T=T) > 1e-4
+
+
+@pytest.mark.parametrize("T", [1.0, 0.7])
+def test_accept_rates_given_the_prefix(T):
+    assert accept_rate_pvalue(T=T) > 1e-4
 
 
 def test_single_position_acceptance_equals_one_minus_tv():
