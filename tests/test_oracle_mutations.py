@@ -15,6 +15,8 @@ copy:
     a table clamped at its last point, the first segment's slope everywhere;
   * the sequential fp32 prefix product (test_oracle_schedule.py): the product
     taken in fp64;
+  * the scheduler pins (test_oracle_schedule.py): candidates in ascending
+    order, tau started without the final tokens, the batch started empty;
   * the sampler's draws against softmax (test_oracle_sampler.py): tile masses
     taken as the tile's maximum, the leaf's Gumbel noise with the wrong sign;
     and the same sampler mistake seen through the round's pin.
@@ -184,3 +186,40 @@ def test_a_sampler_mistake_reaches_the_round():
     s_mod = _mutant("sampler.py", SAMPLER_MUTANTS[1][1], SAMPLER_MUTANTS[1][2], "leaf_gumbel_sign_round")
     m = _mutant("dspark.py", None, None, "round_on_mutant_sampler", sampler=s_mod)
     assert _round_pin_fails(m, 1.0)
+
+
+# (Skipping a failed candidate instead of stopping is no mistake in this rule:
+# a failure leaves tau and N unchanged and the test is monotone in Q, so every
+# later candidate, whose Q is no larger, fails too.)
+SCHEDULE_MUTANTS = [
+    ("ascending_order", "cand = sorted((-int(Q[b, j]), b, j) for b in range(B) for j in range(gamma))",
+     "cand = sorted((int(Q[b, j]), b, j) for b in range(B) for j in range(gamma))"),
+    ("no_final_tokens_in_tau", "    tau = B << 32\n", "    tau = 0\n"),
+    ("empty_initial_batch", "    N = B\n    budget = np.zeros(B, dtype=np.int32)\n",
+     "    N = 0\n    budget = np.zeros(B, dtype=np.int32)\n"),
+]
+
+
+def _schedule_pins_fail(m, monkeypatch):
+    """True when one of the scheduler pins of test_oracle_schedule.py fails
+    (raises) with module m in place of the oracle."""
+    import test_oracle_schedule as ts
+    monkeypatch.setattr(ts, "od", m)
+    pins = [lambda: ts.test_admission_follows_the_greedy_early_stop_rule(s) for s in range(3)]
+    pins += [ts.test_scheduler_admission_crossing_the_last_table_point, ts.test_constant_rate_admits_every_nonzero_candidate,
+             ts.test_budgets_shrink_as_concurrency_grows]
+    for pin in pins:
+        try:
+            pin()
+        except Exception:
+            return True
+    return False
+
+
+def test_schedule_pins_pass_on_the_oracle(monkeypatch):
+    assert not _schedule_pins_fail(od, monkeypatch)
+
+
+@pytest.mark.parametrize("tag,old,new", SCHEDULE_MUTANTS, ids=[c[0] for c in SCHEDULE_MUTANTS])
+def test_schedule_pins_catch(tag, old, new, monkeypatch):
+    assert _schedule_pins_fail(_mutant("dspark.py", old, new, tag), monkeypatch)
