@@ -266,11 +266,11 @@ __device__ __forceinline__ int index_or(int i, int limit, int fallback) {
 
 // The chosen tile's 64 dot products U[prev] . W[v] (bf16 factors, r = 64 nj
 // with nj = 2 or 4) in fp64 from exact bf16 x bf16 products, by a workgroup of
-// four wavefronts.  Lane l of wavefront w takes the rows v0 + 16 w + (l >> 3)
-// + 8 h (h = 0, 1) of W and the 16-byte chunks (l & 7) + 8 j of each, so that
-// every load instruction reads eight whole 128-byte lines; load_h() fetches the
-// matching U[prev] chunks.  Eight lanes then sum a row's partials, and every
-// lane of the eight returns rows h = 0 and 1 in out[0], out[1].
+// 8 / NH wavefronts.  Lane l of wavefront w takes the rows v0 + 8 NH w +
+// (l >> 3) + 8 h (h < NH) of W and the 16-byte chunks (l & 7) + 8 j of each, so
+// that every load instruction reads eight whole 128-byte lines; load_h()
+// fetches the matching U[prev] chunks.  Eight lanes then sum a row's partials,
+// and every lane of the eight returns row h in out[h].
 struct TileDot {
   static constexpr int kMaxJ = 4;
   uint4 hq[kMaxJ];
@@ -280,18 +280,19 @@ struct TileDot {
     for (int j = 0; j < kMaxJ; ++j)
       if (j < nj) hq[j] = reinterpret_cast<const uint4*>(h)[(lane & 7) + 8 * j];
   }
+  template <int NH = 2>
   __device__ __forceinline__ void dot(const uint16_t* W, int v0, int V, int wave, int lane, double (&out)[2]) const {
-    uint4 wv[2][kMaxJ];
+    uint4 wv[NH][kMaxJ];
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const int v = min(v0 + 16 * wave + (lane >> 3) + 8 * hh, V - 1);
+    for (int hh = 0; hh < NH; ++hh) {
+      const int v = min(v0 + 8 * NH * wave + (lane >> 3) + 8 * hh, V - 1);
       const uint4* row = reinterpret_cast<const uint4*>(W + (size_t)v * (64 * nj));
 #pragma unroll
       for (int j = 0; j < kMaxJ; ++j)
         if (j < nj) wv[hh][j] = row[(lane & 7) + 8 * j];
     }
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
+    for (int hh = 0; hh < NH; ++hh) {
       // a product of two bf16 values is exact in fp32; the sum runs in fp64
       double c[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll

@@ -853,8 +853,8 @@ struct DrawShared {
   double g[3][64];           // Gumbel values: block, tile, column level
   double bm[64], part[4][64];
   float be[64];
-  double val[4], lse, gm, gs;
-  int idx[4], tile;
+  double val[8], lse, gm, gs;
+  int idx[8], tile;
 };
 
 // Accesses to data that other workgroups of the same launch write or read
@@ -874,8 +874,14 @@ __device__ __forceinline__ int load_coherent(const int32_t* p) {
 
 // COHERENT: the tile records and the previous position's token were written by
 // other workgroups of the same launch, and the token drawn here is read by them.
-template <typename TL, typename TF, bool COHERENT = false>
+// NW: wavefronts of the workgroup (4 or 8).  Each 16-lane group covers the same
+// 64 tiles of a block and each factor row of the recompute is summed by the
+// same 8 lanes either way, so the results do not depend on NW.
+template <typename TL, typename TF, bool COHERENT = false, int NW = 4>
 __device__ __forceinline__ void draft_select_block(const DraftSelectArgs& a, int b, DrawShared& sh) {
+  static_assert(NW == 4 || NW == 8, "four or eight wavefronts");
+  constexpr int NQ = 16 / NW;     // groups of four tiles per lane
+  constexpr int QS = 256 * NW;    // tiles per group: tile QS q + 4 tid + k
 
   auto& s_d = sh.d;
   auto& s_sum = sh.sum;
@@ -900,20 +906,20 @@ __device__ __forceinline__ void draft_select_block(const DraftSelectArgs& a, int
                        : COHERENT               ? load_coherent(a.draft + (size_t)b * gamma + pos - 1)
                                                 : a.draft[(size_t)b * gamma + pos - 1];
   const uint32_t off = a.pos_offset ? (uint32_t)a.pos_offset[b] : 0u;
-  Rec rec[4][4];  // tiles 1024 q + 4 tid + k (unconditional loads, so that they all go out at once)
+  Rec rec[NQ][4];  // tiles QS q + 4 tid + k (unconditional loads, so that they all go out at once)
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
+  for (int q = 0; q < NQ; ++q)
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const Rec* p = ts + min(1024 * q + 4 * tid + k, nt - 1);
+      const Rec* p = ts + min(QS * q + 4 * tid + k, nt - 1);
       if constexpr (COHERENT) rec[q][k] = load_rec_coherent(p);
       else rec[q][k] = *p;
     }
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
+  for (int q = 0; q < NQ; ++q)
 #pragma unroll
     for (int k = 0; k < 4; ++k)
-      if (1024 * q + 4 * tid + k >= nt) rec[q][k].mx = -INFINITY, rec[q][k].sum = 0.0f;
+      if (QS * q + 4 * tid + k >= nt) rec[q][k].mx = -INFINITY, rec[q][k].sum = 0.0f;
   const uint32_t rpos = (uint32_t)(pos + 1) + off;
   if (wave < 3 && (wave != 0 || lane < nblk)) s_g[wave][lane] = gumbel(a.seed, kDraftTop + wave, b, rpos, lane);
   const float Tf = checked_temp(T_raw, a.status);
@@ -922,10 +928,10 @@ __device__ __forceinline__ void draft_select_block(const DraftSelectArgs& a, int
 
   // 2. records to LDS; block statistics over 16-lane groups
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
+  for (int q = 0; q < NQ; ++q)
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const int t = 1024 * q + 4 * tid + k;
+      const int t = QS * q + 4 * tid + k;
       if (t < nt) s_d[t] = rec_top(rec[q][k]), s_sum[t] = rec[q][k].sum;
     }
   int tile;
@@ -933,13 +939,13 @@ __device__ __forceinline__ void draft_select_block(const DraftSelectArgs& a, int
   if (Tf > 0.0f) {
     const double invT = 1.0 / (double)Tf;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < NQ; ++q) {
       double d[4], m;
       float sm[4], e;
 #pragma unroll
       for (int k = 0; k < 4; ++k) d[k] = rec_top(rec[q][k]), sm[k] = rec[q][k].sum;
       block_mass(d, sm, invT * kLog2eD, m, e);
-      const int j = 16 * q + 4 * wave + (lane >> 4);
+      const int j = (QS / kTilesPerBlock) * q + 4 * wave + (lane >> 4);
       if ((lane & 15) == 0 && j < nblk) s_bm[j] = m, s_be[j] = e;
     }
     __syncthreads();
@@ -979,10 +985,10 @@ __device__ __forceinline__ void draft_select_block(const DraftSelectArgs& a, int
     double best = -INFINITY;
     int bt = 0x7fffffff;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < NQ; ++q)
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const int t = 1024 * q + 4 * tid + k;
+        const int t = QS * q + 4 * tid + k;
         const double d = rec_top(rec[q][k]);
         if (t < nt && d > best) best = d, bt = t;
       }
@@ -990,7 +996,7 @@ __device__ __forceinline__ void draft_select_block(const DraftSelectArgs& a, int
     if (lane == 0) s_val[wave] = best, s_idx[wave] = bt;
     __syncthreads();
     best = -INFINITY, bt = 0x7fffffff;
-    for (int w = 0; w < 4; ++w)
+    for (int w = 0; w < NW; ++w)
       if (s_val[w] > best || (s_val[w] == best && s_idx[w] < bt)) best = s_val[w], bt = s_idx[w];
     tile = index_or(bt, nt, 0);
   }
@@ -1007,10 +1013,13 @@ __device__ __forceinline__ void draft_select_block(const DraftSelectArgs& a, int
   const float xb = load_logit(brow + min(v, V - 1));  // unconditional: issued with the factor rows
   if (td.nj) {
     double dt[2];
-    td.dot(static_cast<const uint16_t*>(a.Wt), tile * kTile, V, wave, lane, dt);
-    if ((lane & 7) == 0) s_part[0][16 * wave + (lane >> 3)] = dt[0], s_part[0][16 * wave + (lane >> 3) + 8] = dt[1];
-  } else {
-    // the rank split over the four wavefronts
+    td.dot<8 / NW>(static_cast<const uint16_t*>(a.Wt), tile * kTile, V, wave, lane, dt);
+    if ((lane & 7) == 0) {
+      s_part[0][(64 / NW) * wave + (lane >> 3)] = dt[0];
+      if (NW == 4) s_part[0][(64 / NW) * wave + (lane >> 3) + 8] = dt[1];
+    }
+  } else if (wave < 4) {
+    // the rank split over four wavefronts
     const int kq = (r + 3) / 4, k0 = min(wave * kq, r), k1 = min(k0 + kq, r);
     s_part[wave][lane] = v < V ? dot_part<TF>(h, static_cast<const TF*>(a.Wt) + (size_t)v * r, k0, k1) : 0.0;
   }
@@ -1052,10 +1061,12 @@ __device__ __forceinline__ void draft_select_block(const DraftSelectArgs& a, int
   }
 }
 
+// Eight wavefronts: the block sums and the records' LDS copies, on one
+// wavefront per SIMD with every latency exposed, are split twice as finely.
 template <typename TL, typename TF>
-__global__ __launch_bounds__(256) void draft_select_fast(DraftSelectArgs a) {
+__global__ __launch_bounds__(512) void draft_select_fast(DraftSelectArgs a) {
   __shared__ DrawShared sh;
-  draft_select_block<TL, TF>(a, blockIdx.x, sh);
+  draft_select_block<TL, TF, false, 8>(a, blockIdx.x, sh);
 }
 
 // The last draw of a round and the scheduler (independent of each other, both
@@ -2322,11 +2333,11 @@ hipError_t launch_draft_select(const DraftSelectArgs& a, int logits_dtype, int f
   const dim3 grid(a.B);
   if (a.n_tiles <= kTilesPerBlock * 64) {
     if (logits_dtype == DSPARK_BF16) {
-      if (factor_dtype == DSPARK_BF16) launch(&draft_select_fast<uint16_t, uint16_t>, grid, 256, 0, s, a);
-      else launch(&draft_select_fast<uint16_t, float>, grid, 256, 0, s, a);
+      if (factor_dtype == DSPARK_BF16) launch(&draft_select_fast<uint16_t, uint16_t>, grid, 512, 0, s, a);
+      else launch(&draft_select_fast<uint16_t, float>, grid, 512, 0, s, a);
     } else {
-      if (factor_dtype == DSPARK_BF16) launch(&draft_select_fast<float, uint16_t>, grid, 256, 0, s, a);
-      else launch(&draft_select_fast<float, float>, grid, 256, 0, s, a);
+      if (factor_dtype == DSPARK_BF16) launch(&draft_select_fast<float, uint16_t>, grid, 512, 0, s, a);
+      else launch(&draft_select_fast<float, float>, grid, 512, 0, s, a);
     }
     return hipGetLastError();
   }
