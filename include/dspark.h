@@ -112,6 +112,12 @@ int dspark_abi_version(void);
 /* Static text for a return code. */
 const char* dspark_error_string(int code);
 
+/* The HIP error behind the calling thread's most recent DSPARK_EHIP return
+ * (a hipError_t value; 0 if this thread has had none), and, when `name` is not
+ * NULL, its name from the HIP runtime (a static string) in *name.  Each
+ * DSPARK_EHIP return overwrites it; other returns leave it as it was. */
+int dspark_last_hip_error(const char** name);
+
 /* Bytes of device workspace the three calls need for these sizes (0 if a size
  * is out of range).  One workspace serves draft, schedule and verify. */
 size_t dspark_workspace_bytes(int B, int gamma, int V, int r);
@@ -142,8 +148,23 @@ int dspark_pack_w2(const void* W, int factor_dtype, int V, int r, void* W_packed
  * the same draft round ([P1] eq. p_k) with the same arithmetic.  On MI355X the
  * per-position launches are the faster ones at the sizes measured (the
  * resident round's two device-wide waits per position cost more than the
- * kernel boundaries they replace), so they are the default. */
+ * kernel boundaries they replace), so they are the default.  The resident
+ * round is a cooperative launch; where it does not fit (see dspark_draft_round)
+ * or the HIP runtime refuses it (as it does while another process on the GPU
+ * holds the device's cooperative-launch resources), the call takes the
+ * per-position launches instead, with the same results. */
 int dspark_set_draft_path(int path);
+
+/* Bound, in seconds (0 to 60; default 0.2), of each device-wide wait of the
+ * resident draft round, for launches enqueued after the call, process-wide.  A
+ * wait that passes its bound stops waiting and sets a bit of the workspace
+ * status word (dspark_status then returns DSPARK_EDATA): the round's outputs
+ * are then unspecified, every memory access stays in bounds and the launch
+ * completes, leaving the workspace fit for the next call.  Only a GPU shared
+ * with other work that holds CUs for that long stalls the round; a bound of 0
+ * forces the stall path.  The previous bound goes to *previous when it is not
+ * NULL.  DSPARK_EINVAL for a bound outside [0, 60] or NaN. */
+int dspark_set_resident_wait_bound(double seconds, double* previous);
 
 /*
  * dspark_draft_round -- [P1] eq. p_k with the Markov head.

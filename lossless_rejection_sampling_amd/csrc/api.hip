@@ -148,6 +148,12 @@ hipError_t kernel_setup(const void* fn, int threads, size_t lds, int* groups) {
 
 KernelEvents* kernel_events() { return t_events; }
 
+thread_local int t_hip_error = 0;
+int hip_failed(hipError_t e) {
+  t_hip_error = (int)e;
+  return DSPARK_EHIP;
+}
+
 ProfileScope::ProfileScope(int c, hipStream_t) : cls(c), ev{nullptr, nullptr, 0}, outer(t_events), on(false) {
   {
     ProfState& p = prof();
@@ -185,9 +191,10 @@ ProfileScope::~ProfileScope() {
 
 using namespace dspark;
 
-#define DSPARK_TRY(expr)                  \
-  do {                                    \
-    if ((expr) != hipSuccess) return DSPARK_EHIP; \
+#define DSPARK_TRY(expr)                         \
+  do {                                           \
+    const hipError_t e_ = (expr);                \
+    if (e_ != hipSuccess) return hip_failed(e_); \
   } while (0)
 
 namespace {
@@ -279,7 +286,7 @@ int draft_round(const void* base_logits, int logits_dtype, const void* U, const 
       }
       return DSPARK_OK;
     }
-    if (e != hipErrorNotSupported) return DSPARK_EHIP;
+    if (e != hipErrorNotSupported) return hip_failed(e);
   }
 
   const bool table = factor_dtype == DSPARK_BF16 && (r == 128 || r == 256);
@@ -298,7 +305,7 @@ int draft_round(const void* base_logits, int logits_dtype, const void* U, const 
       ProfileScope ps(kClsDraftSelect, s);
       const hipError_t e = launch_draft_select_schedule(d, *sched, logits_dtype, factor_dtype, s);
       if (e == hipSuccess) return DSPARK_OK;
-      if (e != hipErrorNotSupported) return DSPARK_EHIP;
+      if (e != hipErrorNotSupported) return hip_failed(e);
     }
     {
       ProfileScope ps(kClsDraftSelect, s);
@@ -328,6 +335,11 @@ const char* dspark_error_string(int code) {
   }
 }
 
+int dspark_last_hip_error(const char** name) {
+  if (name) *name = hipGetErrorName(static_cast<hipError_t>(t_hip_error));
+  return t_hip_error;
+}
+
 size_t dspark_workspace_bytes(int B, int gamma, int V, int r) {
   if (!sizes_ok(B, gamma, V, r)) return 0;
   return layout(B, gamma, V, r).total;
@@ -349,6 +361,13 @@ int dspark_pack_w2(const void* W, int factor_dtype, int V, int r, void* W_packed
 int dspark_set_draft_path(int path) {
   if (path != DSPARK_DRAFT_PER_POSITION && path != DSPARK_DRAFT_RESIDENT) return DSPARK_EINVAL;
   return draft_path().exchange(path);
+}
+
+int dspark_set_resident_wait_bound(double seconds, double* previous) {
+  if (!(seconds >= 0.0 && seconds <= 60.0)) return DSPARK_EINVAL;
+  const uint64_t prev = set_resident_wait_ticks((uint64_t)(seconds * 1e8));
+  if (previous) *previous = (double)prev * 1e-8;
+  return DSPARK_OK;
 }
 
 int dspark_draft_round(const void* base_logits, int logits_dtype, const void* U, const void* W,
@@ -554,8 +573,9 @@ int dspark_profile_read(int kernel_class, int* launches, double* total_ms) {
   int rc = DSPARK_OK;
   for (auto& e : evs) {
     float ms = 0.0f;
-    if (hipEventSynchronize(e.second) != hipSuccess || hipEventElapsedTime(&ms, e.first, e.second) != hipSuccess)
-      rc = DSPARK_EHIP;
+    hipError_t he = hipEventSynchronize(e.second);
+    if (he == hipSuccess) he = hipEventElapsedTime(&ms, e.first, e.second);
+    if (he != hipSuccess) rc = hip_failed(he);
     tot += ms;
   }
   {

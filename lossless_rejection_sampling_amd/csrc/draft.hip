@@ -10,6 +10,7 @@
 // contraction are contiguous along r.
 #include <math.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "dspark.h"
@@ -2293,6 +2294,12 @@ hipError_t launch_draft_select_schedule(const DraftSelectArgs& d, const Schedule
                                      : launch_select_schedule_t<float, float>(d, sa, stream);
 }
 
+// Bound of the resident round's device-wide waits, in s_memrealtime ticks
+// (100 MHz); 0.2 s unless set.
+static std::atomic<uint64_t> g_resident_wait_ticks{20000000ull};
+
+uint64_t set_resident_wait_ticks(uint64_t ticks) { return g_resident_wait_ticks.exchange(ticks); }
+
 hipError_t launch_draft_resident(const DraftSelectArgs& d, int logits_dtype, int factor_dtype,
                                  uint32_t* grid_words, hipStream_t s) {
   static_assert(kResMaxGrid + 1 <= kResidentGridWords, "phase flags and exit counter");
@@ -2317,13 +2324,20 @@ hipError_t launch_draft_resident(const DraftSelectArgs& d, int logits_dtype, int
   ra.d = d;
   ra.flags = grid_words;
   ra.exits = grid_words + kResMaxGrid;
-  ra.spin_limit = 20000000ull;  // 0.2 s
+  ra.spin_limit = g_resident_wait_ticks.load(std::memory_order_relaxed);
   void* args[] = {&ra};
   KernelEvents* ev = kernel_events();
   if (ev && ev->launches == 0) (void)hipEventRecord(ev->start, s);
   e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&draft_round_resident), dim3(cus), dim3(256), args,
                                  (unsigned)kResLdsBytes, s);
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess) {
+    // Nothing was enqueued.  The runtime refuses a cooperative launch with
+    // hipErrorIllegalState while another process on the device holds its
+    // cooperative-launch resources: the caller then takes the per-position
+    // launches, with the error cleared so that their checks do not report it.
+    (void)hipGetLastError();
+    return e == hipErrorIllegalState || e == hipErrorCooperativeLaunchTooLarge ? hipErrorNotSupported : e;
+  }
   if (ev && hipEventRecord(ev->stop, s) == hipSuccess) ++ev->launches;
   return hipSuccess;
 }

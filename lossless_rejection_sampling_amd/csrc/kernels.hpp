@@ -25,6 +25,9 @@ struct KernelEvents {
   int launches;
 };
 KernelEvents* kernel_events();  // the innermost open scope's events, or NULL
+// Records `e` as this thread's last HIP failure (dspark_last_hip_error) and
+// returns DSPARK_EHIP.
+int hip_failed(hipError_t e);
 
 struct ProfileScope {
   ProfileScope(int cls, hipStream_t s);
@@ -118,6 +121,9 @@ hipError_t launch_draft_select(const DraftSelectArgs& a, int logits_dtype, int f
 constexpr int kResidentGridWords = 1024 + 64;
 hipError_t launch_draft_resident(const DraftSelectArgs& d, int logits_dtype, int factor_dtype,
                                  uint32_t* grid_words, hipStream_t s);
+// Sets the bound of the resident round's device-wide waits (s_memrealtime
+// ticks, 100 MHz) for later launches; returns the previous bound.
+uint64_t set_resident_wait_ticks(uint64_t ticks);
 
 struct VerifyArgs {
   const void* target;

@@ -86,14 +86,16 @@ int dspark_peak_stream_read(const void* buf, size_t bytes, uint32_t* sink, void*
   const size_t chunks = (a.n16 + kChunkWords - 1) / kChunkWords;
   if ((chunks + 3) / 4 > 0x7fffffffu) return DSPARK_EINVAL;
   launch(&stream_read_chunks_kernel, (unsigned)((chunks + 3) / 4), 256, 0, static_cast<hipStream_t>(stream), a);
-  return hipGetLastError() == hipSuccess ? DSPARK_OK : DSPARK_EHIP;
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? DSPARK_OK : hip_failed(e);
 }
 
 int dspark_peak_mfma_bf16(int blocks, int iters, uint32_t* sink, void* stream) {
   if (blocks < 1 || blocks > (1 << 20) || iters < 1 || !sink) return DSPARK_EINVAL;
   MfmaArgs a{iters, sink};
   launch(&mfma_loop_kernel, blocks, 256, 0, static_cast<hipStream_t>(stream), a);
-  return hipGetLastError() == hipSuccess ? DSPARK_OK : DSPARK_EHIP;
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? DSPARK_OK : hip_failed(e);
 }
 
 }  // extern "C"

@@ -32,7 +32,12 @@ DSPARK_DRAFT_PER_POSITION, DSPARK_DRAFT_RESIDENT = 0, 1
 
 class DsparkError(RuntimeError):
     def __init__(self, fn: str, code: int):
-        super().__init__(f"{fn} failed: {code} ({error_string(code)})")
+        detail = error_string(code)
+        self.hip_error = 0
+        if code == DSPARK_EHIP:
+            self.hip_error, name = last_hip_error()
+            detail += f": {name} ({self.hip_error})"
+        super().__init__(f"{fn} failed: {code} ({detail})")
         self.code = code
 
 
@@ -42,10 +47,12 @@ _I = ctypes.c_int
 _SIG = {
     "dspark_abi_version": (_I, []),
     "dspark_error_string": (ctypes.c_char_p, [_I]),
+    "dspark_last_hip_error": (_I, [ctypes.POINTER(ctypes.c_char_p)]),
     "dspark_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
     "dspark_schedule_workspace_bytes": (ctypes.c_size_t, [_I, _I]),
     "dspark_pack_w2": (_I, [_P, _I, _I, _I, _P, _P]),
     "dspark_set_draft_path": (_I, [_I]),
+    "dspark_set_resident_wait_bound": (_I, [ctypes.c_double, ctypes.POINTER(ctypes.c_double)]),
     "dspark_draft_round": (_I, [_P, _I, _P, _P, _I, _I, _P, _P, ctypes.c_uint64, _P,
                                 _I, _I, _I, _I, _P, _P, _P, _P, _P]),
     "dspark_draft_schedule": (_I, [_P, _I, _P, _P, _I, _I, _P, _P, ctypes.c_uint64, _P, _I, _I, _I, _I, _P, _P,
@@ -83,6 +90,16 @@ def declared_functions(header: str = HEADER):
     text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(dspark_[a-z_]+)\s*\(", text)))
+
+
+def last_hip_error():
+    """(code, name) of the HIP error behind this thread's last DSPARK_EHIP."""
+    try:
+        name = ctypes.c_char_p()
+        code = lib().dspark_last_hip_error(ctypes.byref(name))
+        return code, (name.value or b"").decode()
+    except Exception:
+        return -1, "unknown"
 
 
 def error_string(code: int) -> str:
@@ -167,6 +184,14 @@ def dspark_set_draft_path(path):
     if res < 0:
         _check("dspark_set_draft_path", res)
     return res
+
+
+def dspark_set_resident_wait_bound(seconds: float) -> float:
+    """Bound (seconds) of the resident draft round's device-wide waits for later
+    launches, process-wide; returns the previous bound."""
+    prev = ctypes.c_double()
+    _check("dspark_set_resident_wait_bound", lib().dspark_set_resident_wait_bound(float(seconds), ctypes.byref(prev)))
+    return prev.value
 
 
 def dspark_draft_round(base_logits, U, W, prev0, temperature, seed, pos_offset,

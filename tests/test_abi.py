@@ -31,6 +31,18 @@ def test_version_and_error_strings(lib):
     assert "device" in ds.error_string(-3)
 
 
+def test_last_hip_error_is_per_thread_and_starts_clear(lib):
+    # a thread that has had no DSPARK_EHIP return reads 0 (no HIP call is made
+    # when the name is not asked for)
+    import threading
+
+    seen = []
+    t = threading.Thread(target=lambda: seen.append(lib.dspark_last_hip_error(None)))
+    t.start()
+    t.join()
+    assert seen == [0]
+
+
 def test_workspace_size_rules(lib):
     assert ds.dspark_workspace_bytes(256, 5, 151936, 256) > 0
     assert ds.dspark_workspace_bytes(0, 5, 100, 8) == 0
@@ -119,6 +131,17 @@ def test_draft_path_switch(lib):
     assert lib.dspark_set_draft_path(0) == 1
     assert lib.dspark_set_draft_path(2) == -1 and lib.dspark_set_draft_path(-1) == -1
     assert lib.dspark_set_draft_path(0) == 0
+
+
+def test_resident_wait_bound_setter():
+    # process state too: a bound in [0, 60] s, default 0.2 s
+    prev = ds.dspark_set_resident_wait_bound(0.05)
+    assert prev == pytest.approx(0.2)
+    assert ds.dspark_set_resident_wait_bound(prev) == pytest.approx(0.05)
+    for bad in (-1e-9, 60.5, float("nan"), float("inf")):
+        with pytest.raises(ds.DsparkError):
+            ds.dspark_set_resident_wait_bound(bad)
+    assert ds.dspark_set_resident_wait_bound(0.2) == pytest.approx(0.2)
 
 
 def test_binding_reads_the_layout_from_the_shape():

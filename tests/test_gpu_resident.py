@@ -123,3 +123,82 @@ def test_draft_schedule_resident_budgets():
 
 def test_set_draft_path_rejects_unknown_values():
     assert ds.lib().dspark_set_draft_path(7) == ds.DSPARK_EINVAL
+
+
+
+def test_forced_stall_is_reported_and_the_workspace_recovers():
+    # the waits' bound forced to zero from the host: workgroups pass their
+    # device-wide waits early, the kernel completes (every index it reads across
+    # workgroups is clamped), the status word carries the stall bit, and the
+    # workspace then serves both paths with the results of a fresh one
+    say("[resident stall] wait bound 0, B=64 gamma=4 V=30000")
+    rnd = wl.small_random(64, 4, 30000, 256, DEV, seed=9, dtype=torch.bfloat16, factor_dtype=torch.bfloat16,
+                          temps=(1.0, 0.0, 0.7))
+    fresh = rd.allocate(rnd)
+    ref = _draft(rnd, fresh, ds.DSPARK_DRAFT_PER_POSITION)
+    buf = rd.allocate(rnd)
+    prev_bound = ds.dspark_set_resident_wait_bound(0.0)
+    prev_path = ds.dspark_set_draft_path(ds.DSPARK_DRAFT_RESIDENT)
+    ds.dspark_profile_enable(CLS_ROUND, 1)
+    try:
+        rd.draft(rnd, buf)
+        torch.cuda.synchronize()
+        launches, _ = ds.dspark_profile_read(CLS_ROUND)
+    finally:
+        ds.dspark_profile_enable(CLS_ROUND, 0)
+        ds.dspark_set_draft_path(prev_path)
+        ds.dspark_set_resident_wait_bound(prev_bound)
+    assert prev_bound == pytest.approx(0.2)
+    assert launches == 1, "the resident kernel did not run"
+    word = int(buf.workspace[:4].view(torch.int32).item())
+    assert word & 64, f"status word {word:#x}: no stall reported"
+    assert ds.dspark_status(buf.workspace) == ds.DSPARK_EDATA
+    assert ds.dspark_status(buf.workspace) == ds.DSPARK_OK  # read and cleared
+    _same(ref, _draft(rnd, buf, ds.DSPARK_DRAFT_PER_POSITION), "per-position after the stall")
+    _same(ref, _draft(rnd, buf, ds.DSPARK_DRAFT_RESIDENT), "resident after the stall")
+
+
+COOP_CHILD = r"""
+import sys
+sys.path.insert(0, ROOT)
+import torch
+from lossless_rejection_sampling_amd import dspark as ds, round as rd, workloads as wl
+cls = ds.KERNEL_CLASSES["draft_round"]
+rnd = wl.small_random(64, 4, 30000, 256, "cuda", seed=9, dtype=torch.bfloat16, factor_dtype=torch.bfloat16,
+                      temps=(1.0, 0.0, 0.7))
+ref_buf, buf = rd.allocate(rnd), rd.allocate(rnd)
+rd.draft(rnd, ref_buf)
+ds.dspark_set_draft_path(ds.DSPARK_DRAFT_RESIDENT)
+ds.dspark_profile_enable(cls, 1)
+rd.draft(rnd, buf)
+torch.cuda.synchronize()
+n = ds.dspark_profile_read(cls)[0]
+ds.dspark_profile_enable(cls, 0)
+ds.dspark_set_draft_path(ds.DSPARK_DRAFT_PER_POSITION)
+rd.draft(rnd, buf)  # and the next call on this thread sees no stale error
+torch.cuda.synchronize()
+assert ds.dspark_status(buf.workspace) == ds.DSPARK_OK
+for k in ("draft_tokens", "draft_logq", "draft_lse"):
+    assert torch.equal(getattr(buf, k), getattr(ref_buf, k)), k
+print("coop ok: resident launches", n, flush=True)
+"""
+
+
+def test_second_process_falls_back_when_cooperative_launch_is_refused():
+    # this process has made cooperative launches (the tests above), which the
+    # HIP runtime lets only one process on the device hold: a second process
+    # asking for the resident round gets the per-position launches, with the
+    # same results and no error left behind
+    import os
+    import subprocess
+    import sys
+
+    rnd = wl.small_random(8, 2, 4096, 256, DEV, seed=3, dtype=torch.bfloat16, factor_dtype=torch.bfloat16)
+    assert _resident_launches(rnd, rd.allocate(rnd)) == 1
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    say("[resident coop] second process, B=64 gamma=4 V=30000")
+    res = subprocess.run([sys.executable, "-c", COOP_CHILD.replace("ROOT", repr(root), 1)], capture_output=True,
+                         text=True, timeout=300, cwd=root)
+    assert res.returncode == 0, res.stdout[-2000:] + res.stderr[-4000:]
+    assert "coop ok" in res.stdout, res.stdout
+    say(res.stdout.strip())
