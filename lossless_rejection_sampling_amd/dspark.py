@@ -85,11 +85,15 @@ def lib():
     return _lib
 
 
-def declared_functions(header: str = HEADER):
-    """Names of the functions include/dspark.h declares."""
+def declared_functions(header: str = HEADER, with_arity: bool = False):
+    """Names of the functions include/dspark.h declares (with their parameter
+    counts when `with_arity`)."""
     text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(dspark_[a-z_]+)\s*\(", text)))
+    decls = re.findall(r"\b(dspark_[a-z0-9_]+)\s*\(([^()]*)\)\s*;", text)
+    if with_arity:
+        return {n: 0 if p.strip() in ("", "void") else p.count(",") + 1 for n, p in decls}
+    return sorted(set(n for n, _ in decls))
 
 
 def last_hip_error():

@@ -19,9 +19,21 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = ds.declared_functions()
-    assert {"dspark_draft_round", "dspark_verify", "dspark_schedule"} <= set(names)
+    assert {"dspark_draft_round", "dspark_verify", "dspark_schedule", "dspark_pack_w2",
+            "dspark_peak_mfma_bf16"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
+
+
+def test_binding_signatures_match_the_header():
+    # every declared function has a ctypes signature with the header's number of
+    # parameters, and the binding declares nothing the header does not
+    arity = ds.declared_functions(with_arity=True)
+    assert len(arity) >= 20
+    for n, k in arity.items():
+        assert n in ds._SIG, n
+        assert len(ds._SIG[n][1]) == k, (n, len(ds._SIG[n][1]), k)
+    assert set(ds._SIG) <= set(arity), set(ds._SIG) - set(arity)
 
 
 def test_version_and_error_strings(lib):
