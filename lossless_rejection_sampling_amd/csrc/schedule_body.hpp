@@ -171,6 +171,7 @@ __device__ __forceinline__ void schedule_block(const ScheduleArgs& a, int bid, i
   // stores to complete before the barrier, and the ticket is taken after it.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+  asm volatile(";; dspark publish: scheduler ticket" ::: "memory");  // a comment: no instruction
   if (tid == 0)
     s_last = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(nblocks - 1);
   __syncthreads();

@@ -353,6 +353,8 @@ __global__ __launch_bounds__(256) void verify_lazy_kernel(VerifyArgs a) {
   __syncthreads();
   if (wave != 0) return;
   uint32_t before = 0u;
+  // names the publication point in the assembly (a comment: no instruction)
+  asm volatile(";; dspark publish: row counter" ::: "memory");
   if (lane == 0) before = __hip_atomic_fetch_add(a.rowcnt + row0 + j, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (__shfl(before, 0) != (uint32_t)(nch - 1)) return;
   // row j is complete: announce it, and test position j + 1 if its turn has come
