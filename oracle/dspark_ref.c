@@ -278,12 +278,14 @@ int ref_draft_round(const void* base, int logits_dtype, const void* U, const voi
  * max(0, p - q) of the rejected row (p if that has no mass) or, after a fully
  * accepted block, from target row L (streams 4/5/6 at position n + 1 +
  * pos_offset); greedy requests emit the target argmax.  logp/logq_out hold
- * ln p_k(x_k) and ln q_k(x_k) at tested positions (NaN elsewhere). */
+ * ln p_k(x_k) and ln q_k(x_k) at tested positions (NaN elsewhere); the
+ * optional residual_out [B, V] (NULL to skip) the row the final token of a
+ * sampled request is drawn from after a rejection (NaN rows elsewhere). */
 int ref_verify(const void* target, const void* base, int logits_dtype, const void* U, const void* W,
                int factor_dtype, const int32_t* prev0, const int32_t* draft_tokens, const float* temperature,
                uint64_t seed, const int32_t* budget, const int32_t* pos_offset, const int32_t* req_ids, int B,
                int gamma, int V, int r, int32_t* out_tokens, int32_t* num_accepted, int32_t* num_emitted,
-               double* logp_out, double* logq_out, double* margin, int32_t* rows_flagged) {
+               double* logp_out, double* logq_out, double* margin, int32_t* rows_flagged, double* residual_out) {
   if (!target || !base || !U || !W || !prev0 || !draft_tokens || !temperature || !out_tokens || !num_accepted ||
       !num_emitted || !logp_out || !logq_out || !margin || !rows_flagged)
     return -1;
@@ -312,6 +314,12 @@ int ref_verify(const void* target, const void* base, int logits_dtype, const voi
     margin[b] = INFINITY;
     rows_flagged[b] = 0;
     for (int k = 0; k < gamma; ++k) logp_out[(size_t)b * gamma + k] = NAN, logq_out[(size_t)b * gamma + k] = NAN;
+    /* optional [B, V] output: the distribution the final token is drawn from
+     * after a rejection (the normalised residual, or p where the residual has
+     * no mass); NaN on rows that hold no such draw */
+    double* const res_row = residual_out ? residual_out + (size_t)b * V : NULL;
+    if (res_row)
+      for (int v = 0; v < V; ++v) res_row[v] = NAN;
     int n = 0;
     for (int k = 1; k <= L; ++k) {
       for (int v = 0; v < V; ++v) z[v] = elem(target, logits_dtype, ((size_t)b * (gamma + 1) + (k - 1)) * V + v);
@@ -361,8 +369,12 @@ int ref_verify(const void* target, const void* base, int logits_dtype, const voi
           q[v] = p[v] + q[v];  /* cancellation scale of each residual entry */
         }
         y = tree_sample(w, V, seed, streams, rq, (uint32_t)(n + 1) + pos0, q, &m);
+        if (res_row)
+          for (int v = 0; v < V; ++v) res_row[v] = d[v] / mass;
       } else {
         y = tree_sample(w, V, seed, streams, rq, (uint32_t)(n + 1) + pos0, NULL, &m);
+        if (res_row)
+          for (int v = 0; v < V; ++v) res_row[v] = p[v];
       }
       if (m < margin[b]) margin[b] = m;
       rows_flagged[b] += m < MARGIN_FLAG;

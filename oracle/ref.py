@@ -32,7 +32,7 @@ def lib():
                                          _P, _P, _P, _P]
         _lib.ref_draft_round.restype = _I
         _lib.ref_verify.argtypes = [_P, _P, _I, _P, _P, _I, _P, _P, _P, ctypes.c_uint64, _P, _P, _P, _I, _I, _I,
-                                    _I, _P, _P, _P, _P, _P, _P, _P]
+                                    _I, _P, _P, _P, _P, _P, _P, _P, _P]
         _lib.ref_verify.restype = _I
         _lib.ref_schedule.argtypes = [_P, _P, _P, _I, _I, _I, _P, _P]
         _lib.ref_schedule.restype = _I
@@ -77,7 +77,7 @@ def draft_round(base, U, W, prev0, temperature, seed: int, pos_offset=None, req_
 
 
 def verify(target, base, U, W, prev0, draft_tokens, temperature, seed: int, budget=None, pos_offset=None,
-           req_ids=None) -> VerifyResult:
+           req_ids=None, keep_residual=False) -> VerifyResult:
     target, base, U, W = _f32(target), _f32(base), _f32(U), _f32(W)
     B, gamma, V = base.shape
     r = U.shape[1]
@@ -89,12 +89,15 @@ def verify(target, base, U, W, prev0, draft_tokens, temperature, seed: int, budg
     n_acc, n_emit, rows_flagged = (np.zeros(B, dtype=np.int32) for _ in range(3))
     logp, logq = np.zeros((B, gamma)), np.zeros((B, gamma))
     margin = np.zeros(B)
+    res = np.empty((B, V)) if keep_residual else None
     rc = lib().ref_verify(_ptr(target), _ptr(base), 1, _ptr(U), _ptr(W), 1, _ptr(prev0), _ptr(drafts), _ptr(T),
                           int(seed) & (2**64 - 1), _ptr(L), _ptr(off), _ptr(ids), B, gamma, V, r, _ptr(out),
-                          _ptr(n_acc), _ptr(n_emit), _ptr(logp), _ptr(logq), _ptr(margin), _ptr(rows_flagged))
+                          _ptr(n_acc), _ptr(n_emit), _ptr(logp), _ptr(logq), _ptr(margin), _ptr(rows_flagged),
+                          _ptr(res))
     if rc != 0:
         raise ValueError("ref_verify rejected its inputs")
-    return VerifyResult(out, n_acc, n_emit, logp, logq, {}, margin, rows_flagged)
+    residual = {} if res is None else {b: res[b] for b in range(B) if not np.isnan(res[b, 0])}
+    return VerifyResult(out, n_acc, n_emit, logp, logq, residual, margin, rows_flagged)
 
 
 def schedule(conf, sps_B, sps_val) -> ScheduleResult:

@@ -41,6 +41,29 @@ def run_gpu(rnd: wl.Round, debug=True) -> rd.Buffers:
     return buf
 
 
+def run_c_oracle(rnd: wl.Round, keep_residual=False) -> od.RoundResult:
+    """The C oracle (oracle/dspark_ref.c) on the whole batch: the scheduler (or
+    the round's own budgets), the draft round and the verification, with the
+    residual rows of every rejected sampled request when ``keep_residual``."""
+    from oracle import ref
+
+    h = wl.to_host
+    target, base, U, W = h(rnd.target), h(rnd.base), h(rnd.U), h(rnd.W)
+    prev0, T = h(rnd.prev0), h(rnd.temperature)
+    off = None if rnd.pos_offset is None else h(rnd.pos_offset)
+    sched = None
+    if rnd.scheduled:
+        sched = ref.schedule(h(rnd.conf), rnd.sps_B, rnd.sps_val)
+        budget = sched.budget
+    elif rnd.budget is not None:
+        budget = h(rnd.budget).astype(np.int32)
+    else:
+        budget = np.full(rnd.B, rnd.gamma, dtype=np.int32)
+    dr = ref.draft_round(base, U, W, prev0, T, rnd.seed, off)
+    vr = ref.verify(target, base, U, W, prev0, dr.tokens, T, rnd.seed, budget, off, keep_residual=keep_residual)
+    return od.RoundResult(dr, budget, sched, vr)
+
+
 def run_oracle(rnd: wl.Round, idx, budget_full=None) -> od.RoundResult:
     """Oracle on requests ``idx`` of the round; budgets come from the oracle's
     scheduler over the whole batch (the scheduler is global)."""

@@ -6,9 +6,13 @@ scheduled and at its full budget, block lengths 4/8/16 at B=256, the scheduled
 round at B=512 and the stress round at B=1024, V=262144) run the whole batch on
 the GPU in the configuration the benchmark times; every request is compared
 with the oracle's whole-batch expectations in tests/golden/rounds (written by
-tests/golden/make_round_goldens.py from the same host-drawn inputs), and the
-residual rows of a few requests with the oracle run here.
+tests/golden/make_round_goldens.py from the same host-drawn inputs), the
+residual rows of a few requests with the numpy oracle run here, and, up to the
+B=512 round, every request again with the C oracle run here (oracle/dspark_ref.c,
+pinned to the numpy oracle on the CPU), residual rows included.
 """
+
+import os
 
 import numpy as np
 import pytest
@@ -18,8 +22,9 @@ from lossless_rejection_sampling_amd import dspark as ds
 from lossless_rejection_sampling_amd import round as rd
 from lossless_rejection_sampling_amd import workloads as wl
 from oracle import dspark as od
+from oracle import ref
 
-from parity import check, compare, compare_golden, load_golden, run_gpu, run_oracle, say
+from parity import check, compare, compare_golden, load_golden, run_c_oracle, run_gpu, run_oracle, say
 
 pytestmark = [
     pytest.mark.gpu,
@@ -367,10 +372,12 @@ def test_scheduler_bit_exact():
 # Full-size workloads: the whole batch on the GPU, a sample through the oracle.
 # ---------------------------------------------------------------------------
 
-def _sampled(rnd, name, n_sample, seed=0):
+def _sampled(rnd, name, n_sample, seed=0, whole=True):
     """The whole batch on the GPU in the benchmark's launch configuration; every
-    request against the oracle's whole-batch expectations, and the residual rows
-    of a few sampled requests against the oracle run here."""
+    request against the oracle's whole-batch expectations, the residual rows of
+    a few sampled requests against the numpy oracle run here, and (``whole``)
+    every request again, residual rows included, against the C oracle run
+    here."""
     say(f"[{name}] B={rnd.B} gamma={rnd.gamma} V={rnd.V} r={rnd.r} dtype={rnd.base.dtype}")
     buf = run_gpu(rnd, debug=True)
     assert ds.dspark_status(buf.workspace) == ds.DSPARK_OK
@@ -383,6 +390,11 @@ def _sampled(rnd, name, n_sample, seed=0):
     rng = np.random.default_rng(seed)
     idx = np.sort(rng.choice(rnd.B, size=min(n_sample, rnd.B), replace=False))
     check(compare(rnd, buf, run_oracle(rnd, idx), idx), name + "_residual_sample")
+    if whole and os.path.exists(ref.LIB):
+        want = run_c_oracle(rnd, keep_residual=True)
+        n_res = sum(1 for b in range(rnd.B) if b in want.verify.residual)
+        say(f"[{name}] C oracle, whole batch: {n_res} residual rows")
+        check(compare(rnd, buf, want, np.arange(rnd.B)), name + "_c_oracle_whole")
     return buf
 
 
@@ -409,6 +421,6 @@ def test_scheduled_b512():
 
 def test_stress_b1024():
     rnd = wl.stress(device=DEV)
-    _sampled(rnd, "stress_B1024", 3)
+    _sampled(rnd, "stress_B1024", 3, whole=False)  # the C oracle's whole batch here would take minutes
     del rnd
     torch.cuda.empty_cache()

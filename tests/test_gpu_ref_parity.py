@@ -27,7 +27,7 @@ from lossless_rejection_sampling_amd import workloads as wl
 from oracle import dspark as od
 from oracle import ref
 
-from parity import check, compare, run_gpu, say
+from parity import check, compare, run_c_oracle, run_gpu, say
 
 pytestmark = [
     pytest.mark.gpu,
@@ -64,21 +64,7 @@ def _round(case, seed):
 
 
 def _c_oracle(rnd) -> od.RoundResult:
-    h = wl.to_host
-    target, base, U, W = h(rnd.target), h(rnd.base), h(rnd.U), h(rnd.W)
-    prev0, T = h(rnd.prev0), h(rnd.temperature)
-    off = None if rnd.pos_offset is None else h(rnd.pos_offset)
-    sched = None
-    if rnd.scheduled:
-        sched = ref.schedule(h(rnd.conf), rnd.sps_B, rnd.sps_val)
-        budget = sched.budget
-    elif rnd.budget is not None:
-        budget = h(rnd.budget).astype(np.int32)
-    else:
-        budget = np.full(rnd.B, rnd.gamma, dtype=np.int32)
-    dr = ref.draft_round(base, U, W, prev0, T, rnd.seed, off)
-    vr = ref.verify(target, base, U, W, prev0, dr.tokens, T, rnd.seed, budget, off)
-    return od.RoundResult(dr, budget, sched, vr)
+    return run_c_oracle(rnd)
 
 
 @pytest.mark.parametrize("k", range(len(CASES)), ids=[c[0].replace(" ", "_") for c in CASES])

@@ -80,8 +80,8 @@ def test_round_matches_the_numpy_oracle(case):
     m = np.isfinite(dn.margin) & sure
     np.testing.assert_allclose(dc.margin[m], dn.margin[m], rtol=1e-6, atol=1e-12)
 
-    vn = od.verify(target, base, U, W, prev0, dn.tokens, T, seed, budget, off, ids)
-    vc = ref.verify(target, base, U, W, prev0, dn.tokens, T, seed, budget, off, ids)
+    vn = od.verify(target, base, U, W, prev0, dn.tokens, T, seed, budget, off, ids, keep_residual=True)
+    vc = ref.verify(target, base, U, W, prev0, dn.tokens, T, seed, budget, off, ids, keep_residual=True)
     ok = vn.margin >= TIE
     assert np.array_equal(vc.num_accepted[ok], vn.num_accepted[ok])
     assert np.array_equal(vc.out_tokens[ok], vn.out_tokens[ok])
@@ -89,6 +89,14 @@ def test_round_matches_the_numpy_oracle(case):
     _close(vc.logp[ok], vn.logp[ok])
     _close(vc.logq[ok], vn.logq[ok])
     assert np.array_equal(vc.rows_flagged[ok], vn.rows_flagged[ok])
+    # the rows the final token is drawn from after a rejection: the same rows
+    # kept, each the same distribution
+    kept = [b for b in range(B) if ok[b]]
+    assert [b for b in kept if b in vc.residual] == [b for b in kept if b in vn.residual]
+    for b in kept:
+        if b in vn.residual:
+            np.testing.assert_allclose(vc.residual[b], vn.residual[b], rtol=1e-9, atol=1e-15)
+            assert abs(vc.residual[b].sum() - 1.0) < 1e-9
     # the round exercises rejections (residual draws or greedy corrections)
     assert (vn.num_accepted < budget).any()
 
